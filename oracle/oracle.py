@@ -1,0 +1,206 @@
+"""ctypes wrapper around the plain-C CPU oracle (mep_oracle.c).
+
+TEST INFRASTRUCTURE: only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module.  It shares no code with the GPU
+library and never loads it.
+
+Every function takes and returns numpy arrays in the layouts the C file
+documents; the arithmetic lives in the C file.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mep_oracle.c")
+_LIB = os.path.join(_HERE, "libmep_oracle.so")
+
+ST_BAD_INDEX = 1
+ST_DUP_EXPERT = 2
+ST_EM_OVERFLOW = 4
+
+GCC_FLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+             "-Wall", "-Wextra"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no FMA contraction, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        L = C.CDLL(_LIB)
+        p = C.c_void_p
+        i32, i64, f32 = C.c_int32, C.c_int64, C.c_float
+        L.oracle_bf16_to_f32.argtypes, L.oracle_bf16_to_f32.restype = [C.c_uint16], f32
+        L.oracle_bf16_rne.argtypes, L.oracle_bf16_rne.restype = [f32], C.c_uint16
+        L.oracle_e4m3_decode.argtypes, L.oracle_e4m3_decode.restype = [C.c_uint8], C.c_double
+        L.oracle_e4m3_encode.argtypes, L.oracle_e4m3_encode.restype = [f32], C.c_uint8
+        L.oracle_e4m3_encode_array.argtypes = [p, i64, p]
+        L.oracle_bf16_rne_array.argtypes = [p, i64, p]
+        L.oracle_plan.argtypes = [p, i32, i32, i32, i32, i32, i32, p, p, p]
+        L.oracle_plan.restype = i32
+        L.oracle_quant_row.argtypes = [p, i32, p, p]
+        L.oracle_dispatch.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, i32,
+                                      p, p, p, p, p, p]
+        L.oracle_combine.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, p]
+        L.oracle_to_expert_major.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, i32,
+                                             i32, i32, i32, i64, p, p, p, p, p, p]
+        L.oracle_to_expert_major.restype = i32
+        L.oracle_combine_em.argtypes = [p, p, p, i32, i32, i32, p]
+        L.oracle_expert_dequant.argtypes = [p, p, i64, i32, f32, p]
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(C.c_void_p)
+
+
+# --- codecs -------------------------------------------------------------------
+
+def bf16_rne(v: np.ndarray) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.uint16)
+    lib().oracle_bf16_rne_array(_p(v), v.size, _p(out))
+    return out
+
+
+def bf16_to_f32(h: np.ndarray) -> np.ndarray:
+    return (np.asarray(h, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.uint8)
+    lib().oracle_e4m3_encode_array(_p(v), v.size, _p(out))
+    return out
+
+
+def e4m3_decode_table() -> np.ndarray:
+    return np.array([lib().oracle_e4m3_decode(c) for c in range(256)], dtype=np.float64)
+
+
+def quant_row(x_row: np.ndarray):
+    x_row = np.ascontiguousarray(x_row, dtype=np.uint16)
+    H = x_row.shape[0]
+    q = np.empty(H, dtype=np.uint8)
+    s = np.empty(H // 128, dtype=np.float32)
+    lib().oracle_quant_row(_p(x_row), H, _p(q), _p(s))
+    return q, s
+
+
+# --- the path -----------------------------------------------------------------
+
+def plan(indices: np.ndarray, R: int, epr: int, cap: int, src_rank: int = 0) -> dict:
+    idx = np.ascontiguousarray(indices, dtype=np.int32)
+    T, k = idx.shape
+    counts = np.zeros(R, dtype=np.int32)
+    spos = np.full((R, cap), -1, dtype=np.int32)
+    slot = np.empty((T, k), dtype=np.int32)
+    st = lib().oracle_plan(_p(idx), T, k, R, epr, cap, src_rank, _p(counts), _p(spos), _p(slot))
+    return {"recv_counts": counts, "src_token_pos": spos, "slot": slot, "status": int(st)}
+
+
+def dispatch(x: np.ndarray, weights: np.ndarray, indices: np.ndarray, pl: dict, R: int,
+             epr: int, cap: int, quant: bool, fill: int = 0) -> dict:
+    """Returns recv_x ([R,cap,H] uint16 bf16 bits, or uint8 E4M3 codes), recv_scales
+    ([R,cap,H/128] or None), recv_weights, recv_indices.  Unwritten rows keep
+    ``fill`` (bytes) so callers can see which rows were written."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    w = np.ascontiguousarray(weights, dtype=np.float32)
+    idx = np.ascontiguousarray(indices, dtype=np.int32)
+    T, H = x.shape
+    k = idx.shape[1]
+    nb = H // 128 if quant else 0
+    if quant:
+        rx = np.full((R, cap, H), fill, dtype=np.uint8)
+        rs = np.zeros((R, cap, nb), dtype=np.float32)
+    else:
+        rx = np.full((R, cap, H), fill * 0x0101, dtype=np.uint16)
+        rs = np.zeros(1, dtype=np.float32)
+    rw = np.zeros((R, cap, k), dtype=np.float32)
+    ri = np.full((R, cap, k), -1, dtype=np.int32)
+    qt = np.empty(H, dtype=np.uint8)
+    st = np.empty(max(nb, 1), dtype=np.float32)
+    lib().oracle_dispatch(_p(x), _p(w), _p(idx), _p(pl["slot"]), T, H, k, R, epr, cap,
+                          1 if quant else 0, _p(rx), _p(rs), _p(rw), _p(ri), _p(qt), _p(st))
+    return {"recv_x": rx, "recv_scales": rs if quant else None, "recv_weights": rw,
+            "recv_indices": ri}
+
+
+def combine(y: np.ndarray, weights: np.ndarray, indices: np.ndarray, pl: dict, epr: int,
+            cap: int) -> np.ndarray:
+    y = np.ascontiguousarray(y, dtype=np.uint16)
+    w = np.ascontiguousarray(weights, dtype=np.float32)
+    idx = np.ascontiguousarray(indices, dtype=np.int32)
+    T, k = idx.shape
+    H = y.shape[-1]
+    out = np.empty((T, H), dtype=np.uint16)
+    lib().oracle_combine(_p(y), _p(w), _p(idx), _p(pl["slot"]), T, H, k, epr, cap, _p(out))
+    return out
+
+
+def to_expert_major(disp: dict, pl: dict, R: int, epr: int, cap: int, T: int, cap_em: int,
+                    src_rank: int = 0, fill: int = 0) -> dict:
+    rx = np.ascontiguousarray(disp["recv_x"])
+    elem = rx.dtype.itemsize
+    H = rx.shape[-1]
+    rs = disp["recv_scales"]
+    nb = 0 if rs is None else rs.shape[-1]
+    ri = np.ascontiguousarray(disp["recv_indices"], dtype=np.int32)
+    k = ri.shape[-1]
+    E = R * epr
+    em_x = np.full((cap_em, H), fill * (0x0101 if elem == 2 else 1), dtype=rx.dtype)
+    em_s = np.zeros((cap_em, max(nb, 1)), dtype=np.float32)
+    em_counts = np.zeros(E, dtype=np.int32)
+    em_offsets = np.zeros(E + 1, dtype=np.int32)
+    em_src = np.full(cap_em, -1, dtype=np.int32)
+    tok = np.empty((T, k), dtype=np.int32)
+    rs_arr = np.ascontiguousarray(rs if rs is not None else np.zeros(1, np.float32))
+    st = lib().oracle_to_expert_major(_p(rx), _p(rs_arr), _p(ri), _p(pl["recv_counts"]),
+                                      _p(pl["src_token_pos"]), R, epr, cap, H, nb, k, elem,
+                                      src_rank, T, cap_em, _p(em_x), _p(em_s), _p(em_counts),
+                                      _p(em_offsets), _p(em_src), _p(tok))
+    return {"em_x": em_x, "em_scales": em_s if nb else None, "em_counts": em_counts,
+            "em_offsets": em_offsets, "em_src_pos": em_src, "tok_em_row": tok,
+            "status": int(st)}
+
+
+def combine_em(y_em: np.ndarray, weights: np.ndarray, tok_em_row: np.ndarray) -> np.ndarray:
+    y_em = np.ascontiguousarray(y_em, dtype=np.uint16)
+    w = np.ascontiguousarray(weights, dtype=np.float32)
+    tok = np.ascontiguousarray(tok_em_row, dtype=np.int32)
+    T, k = tok.shape
+    H = y_em.shape[-1]
+    out = np.empty((T, H), dtype=np.uint16)
+    lib().oracle_combine_em(_p(y_em), _p(w), _p(tok), T, H, k, _p(out))
+    return out
+
+
+def expert_dequant(q: np.ndarray, scales: np.ndarray, mult: float) -> np.ndarray:
+    """Expert stand-in for FP8 payloads: bf16((decode(q) * scale) * mult)."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    H = q.shape[-1]
+    rows = q.size // H
+    s = np.ascontiguousarray(scales, dtype=np.float32)
+    y = np.empty(q.shape, dtype=np.uint16)
+    lib().oracle_expert_dequant(_p(q), _p(s), rows, H, mult, _p(y))
+    return y
