@@ -1,0 +1,210 @@
+"""ctypes marshalling for libmep.so: one Python function per C entry point,
+same names, same argument order.  Tensors are passed as their device
+pointers; ``stream=None`` means torch's current stream on the tensors'
+device.  Non-zero return codes raise MepError (except mep_get_status, which
+returns the device status word)."""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmep.so")
+
+MEP_OK = 0
+MEP_ERR_NULL = -1
+MEP_ERR_CONFIG = -2
+MEP_ERR_SHAPE = -3
+MEP_ERR_ALIGN = -4
+MEP_ERR_STATE = -5
+MEP_ERR_HIP = -6
+MEP_ERR_DEVICE = -7
+
+MEP_DEV_BAD_INDEX = 1
+MEP_DEV_DUP_EXPERT = 2
+MEP_DEV_EM_OVERFLOW = 4
+
+MEP_QUANT_NONE = 0
+MEP_QUANT_FP8_E4M3_BLOCK128 = 1
+MEP_RANK_MAJOR = 0
+MEP_EXPERT_MAJOR = 1
+
+
+class MepConfig(C.Structure):
+    _fields_ = [
+        ("hidden_dim", C.c_int32),
+        ("scale_dim", C.c_int32),
+        ("num_experts_per_rank", C.c_int32),
+        ("num_experts_per_token", C.c_int32),
+        ("max_num_inp_token_per_rank", C.c_int32),
+        ("world_size", C.c_int32),
+        ("rank", C.c_int32),
+        ("quant", C.c_int32),
+    ]
+
+
+class MepError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        super().__init__(f"{fn}: {mep_error_string(code)} ({code})")
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m combine_mep_plan_amd.build` (there is no fallback)")
+        L = C.CDLL(LIB_PATH)
+        p, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+        cfgp = C.POINTER(MepConfig)
+        sig = {
+            "mep_error_string": ([C.c_int], C.c_char_p),
+            "mep_workspace_bytes": ([cfgp], sz),
+            "mep_create": ([cfgp, p, sz, C.POINTER(p)], C.c_int),
+            "mep_destroy": ([p], C.c_int),
+            "mep_plan": ([p, p, i32, p, p, p], C.c_int),
+            "mep_dispatch": ([p, p, p, p, p, p, p, p, p], C.c_int),
+            "mep_to_expert_major": ([p, p, p, p, p, p, p, p, p, p, p, i64, p], C.c_int),
+            "mep_combine": ([p, i32, p, p, p, p], C.c_int),
+            "mep_reset": ([p, p], C.c_int),
+            "mep_get_status": ([p, p, C.POINTER(i32)], C.c_int),
+            "mep_get_route": ([p, p, p, p], C.c_int),
+            "mep_probe_e4m3": ([p, p, i64, p], C.c_int),
+            "mep_probe_bf16": ([p, p, i64, p], C.c_int),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes, f.restype = args, res
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    """Device pointer of a tensor (must be contiguous), an int, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmep must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream, *tensors):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    dev = next((t.device for t in tensors if hasattr(t, "device") and t.device.type == "cuda"),
+               None)
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != MEP_OK:
+        raise MepError(fn, rc)
+
+
+def mep_error_string(code: int) -> str:
+    return lib().mep_error_string(code).decode()
+
+
+def mep_workspace_bytes(cfg: MepConfig) -> int:
+    return lib().mep_workspace_bytes(C.byref(cfg))
+
+
+def mep_create(cfg: MepConfig, workspace, workspace_bytes: int) -> int:
+    h = C.c_void_p()
+    _check("mep_create", lib().mep_create(C.byref(cfg), _ptr(workspace), workspace_bytes,
+                                          C.byref(h)))
+    return h.value
+
+
+def mep_destroy(h: int) -> None:
+    _check("mep_destroy", lib().mep_destroy(h))
+
+
+def mep_plan(h, indices, T, recv_counts, src_token_pos, stream=None) -> None:
+    s = _stream(stream, recv_counts)
+    _check("mep_plan", lib().mep_plan(h, _ptr(indices), T, _ptr(recv_counts),
+                                      _ptr(src_token_pos), s))
+
+
+def mep_dispatch(h, x, weights, indices, recv_x, recv_scales, recv_weights, recv_indices,
+                 stream=None) -> None:
+    s = _stream(stream, recv_x)
+    _check("mep_dispatch", lib().mep_dispatch(h, _ptr(x), _ptr(weights), _ptr(indices),
+                                              _ptr(recv_x), _ptr(recv_scales),
+                                              _ptr(recv_weights), _ptr(recv_indices), s))
+
+
+def mep_to_expert_major(h, recv_x, recv_scales, recv_indices, recv_counts, src_token_pos, em_x,
+                        em_scales, em_counts, em_offsets, em_src_pos, cap_em,
+                        stream=None) -> None:
+    s = _stream(stream, em_x)
+    _check("mep_to_expert_major", lib().mep_to_expert_major(
+        h, _ptr(recv_x), _ptr(recv_scales), _ptr(recv_indices), _ptr(recv_counts),
+        _ptr(src_token_pos), _ptr(em_x), _ptr(em_scales), _ptr(em_counts), _ptr(em_offsets),
+        _ptr(em_src_pos), cap_em, s))
+
+
+def mep_combine(h, layout, y, weights, out, stream=None) -> None:
+    s = _stream(stream, out)
+    _check("mep_combine", lib().mep_combine(h, layout, _ptr(y), _ptr(weights), _ptr(out), s))
+
+
+def mep_reset(h, stream=None) -> None:
+    _check("mep_reset", lib().mep_reset(h, _stream(stream)))
+
+
+def mep_get_status(h, stream=None) -> int:
+    v = C.c_int32(0)
+    rc = lib().mep_get_status(h, _stream(stream), C.byref(v))
+    if rc not in (MEP_OK, MEP_ERR_DEVICE):
+        raise MepError("mep_get_status", rc)
+    return v.value
+
+
+def mep_get_route(h, recv_row, em_row=None, stream=None) -> None:
+    s = _stream(stream, recv_row)
+    _check("mep_get_route", lib().mep_get_route(h, _ptr(recv_row), _ptr(em_row), s))
+
+
+def mep_probe_e4m3(inp, out, n, stream=None) -> None:
+    _check("mep_probe_e4m3", lib().mep_probe_e4m3(_ptr(inp), _ptr(out), n, _stream(stream, out)))
+
+
+def mep_probe_bf16(inp, out, n, stream=None) -> None:
+    _check("mep_probe_bf16", lib().mep_probe_bf16(_ptr(inp), _ptr(out), n, _stream(stream, out)))
+
+
+class Mep:
+    """A handle together with the device workspace it is bound to (allocated
+    here with torch, the only allocation on the Python side)."""
+
+    def __init__(self, hidden_dim, num_experts_per_rank, num_experts_per_token,
+                 max_num_inp_token_per_rank, world_size, rank=0, fp8=False, device="cuda"):
+        import torch
+        self.cfg = MepConfig(hidden_dim, hidden_dim // 128 if fp8 else 0, num_experts_per_rank,
+                             num_experts_per_token, max_num_inp_token_per_rank, world_size, rank,
+                             MEP_QUANT_FP8_E4M3_BLOCK128 if fp8 else MEP_QUANT_NONE)
+        nbytes = mep_workspace_bytes(self.cfg)
+        if nbytes == 0:
+            raise MepError("mep_workspace_bytes", MEP_ERR_CONFIG)
+        self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        self.h = mep_create(self.cfg, self.workspace, nbytes)
+
+    def close(self):
+        if self.h:
+            mep_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,324 @@
+// Host side of the C ABI declared in include/mep.h: argument checks, call-order
+// state and launch of the gfx950 kernels.  Every check here runs before any
+// HIP call, so a rejected call launches nothing.
+#include <stdlib.h>
+#include <string.h>
+
+#include "mep_internal.h"
+
+struct mep_handle {
+  mep_config cfg;
+  unsigned char* ws;
+  size_t ws_bytes;
+  mep::WsLayout lay;
+  mep::RankDiv rdiv;
+  bool plan_valid;
+  bool em_valid;
+  int32_t plan_T;
+};
+
+namespace mep {
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(const mep_config& c) {
+  WsLayout L{};
+  const size_t cap = (size_t)c.max_num_inp_token_per_rank, k = (size_t)c.num_experts_per_token;
+  const size_t R = (size_t)c.world_size, epr = (size_t)c.num_experts_per_rank;
+  const size_t C = (cap + kChunk - 1) / kChunk;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+  L.status = take(sizeof(uint32_t));
+  L.chunk_cnt = take(C * R * sizeof(int32_t));
+  L.mask = take(cap * sizeof(uint64_t));
+  L.rrow = take(cap * k * sizeof(int32_t));
+  L.ufirst = take(cap * sizeof(uint32_t));
+  L.em_row = take(cap * k * sizeof(int32_t));
+  L.em_lmask = take(R * cap * sizeof(uint64_t));
+  L.em_ccnt = take(R * C * epr * sizeof(int32_t));
+  L.em_cbase = take(R * C * epr * sizeof(int32_t));
+  L.total = off;
+  return L;
+}
+
+}  // namespace mep
+
+using mep::WsLayout;
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static int check_config(const mep_config* c) {
+  if (!c) return MEP_ERR_NULL;
+  const int64_t H = c->hidden_dim, R = c->world_size, epr = c->num_experts_per_rank;
+  const int64_t k = c->num_experts_per_token, cap = c->max_num_inp_token_per_rank;
+  if (H <= 0 || H % 8 != 0 || H > (1 << 20)) return MEP_ERR_CONFIG;
+  if (R < 1 || R > mep::kMaxRanks) return MEP_ERR_CONFIG;
+  if (epr < 1 || epr > mep::kMaxEpr) return MEP_ERR_CONFIG;
+  if (k < 1 || k > mep::kMaxTopk || k > R * epr) return MEP_ERR_CONFIG;
+  if (cap < 1) return MEP_ERR_CONFIG;
+  if (c->rank < 0 || c->rank >= R) return MEP_ERR_CONFIG;
+  // flat receive rows and src_token_pos must fit int32
+  if (R * cap + (int64_t)c->rank * R * cap > INT32_MAX) return MEP_ERR_CONFIG;
+  if (c->quant == MEP_QUANT_NONE) {
+    if (c->scale_dim != 0) return MEP_ERR_CONFIG;
+  } else if (c->quant == MEP_QUANT_FP8_E4M3_BLOCK128) {
+    if (H % 128 != 0 || c->scale_dim != H / 128) return MEP_ERR_CONFIG;
+  } else {
+    return MEP_ERR_CONFIG;
+  }
+  return MEP_OK;
+}
+
+static mep::RankDiv make_rdiv(int32_t epr) {
+  mep::RankDiv d;
+  d.m = (uint32_t)(((1u << 20) + (uint32_t)epr - 1) / (uint32_t)epr);
+  return d;
+}
+
+template <class T>
+static T* ws_ptr(mep_handle* h, size_t off) {
+  return reinterpret_cast<T*>(h->ws + off);
+}
+
+static int hip_rc(hipError_t e) { return e == hipSuccess ? MEP_OK : MEP_ERR_HIP; }
+
+extern "C" {
+
+const char* mep_error_string(int code) {
+  switch (code) {
+    case MEP_OK: return "ok";
+    case MEP_ERR_NULL: return "null pointer";
+    case MEP_ERR_CONFIG: return "invalid config";
+    case MEP_ERR_SHAPE: return "size out of range";
+    case MEP_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case MEP_ERR_STATE: return "call order violated";
+    case MEP_ERR_HIP: return "HIP runtime error";
+    case MEP_ERR_DEVICE: return "device status set";
+    default: return "unknown";
+  }
+}
+
+size_t mep_workspace_bytes(const mep_config* cfg) {
+  if (check_config(cfg) != MEP_OK) return 0;
+  return mep::ws_layout(*cfg).total;
+}
+
+int mep_create(const mep_config* cfg, void* workspace, size_t workspace_bytes, mep_handle** out) {
+  if (!out) return MEP_ERR_NULL;
+  *out = nullptr;
+  int rc = check_config(cfg);
+  if (rc != MEP_OK) return rc;
+  if (!workspace) return MEP_ERR_NULL;
+  if (!aligned16(workspace)) return MEP_ERR_ALIGN;
+  const WsLayout lay = mep::ws_layout(*cfg);
+  if (workspace_bytes < lay.total) return MEP_ERR_SHAPE;
+  const mep::RankDiv rd = make_rdiv(cfg->num_experts_per_rank);
+  const uint32_t E = (uint32_t)cfg->world_size * (uint32_t)cfg->num_experts_per_rank;
+  for (uint32_t e = 0; e < E; ++e)
+    if (rd(e) != e / (uint32_t)cfg->num_experts_per_rank) return MEP_ERR_CONFIG;
+  mep_handle* h = (mep_handle*)calloc(1, sizeof(mep_handle));
+  if (!h) return MEP_ERR_CONFIG;
+  h->cfg = *cfg;
+  h->ws = (unsigned char*)workspace;
+  h->ws_bytes = workspace_bytes;
+  h->lay = lay;
+  h->rdiv = rd;
+  *out = h;
+  return MEP_OK;
+}
+
+int mep_destroy(mep_handle* h) {
+  if (!h) return MEP_ERR_NULL;
+  free(h);
+  return MEP_OK;
+}
+
+int mep_plan(mep_handle* h, const int32_t* indices, int32_t T, int32_t* recv_counts,
+             int32_t* src_token_pos, void* stream) {
+  if (!h || !recv_counts || !src_token_pos) return MEP_ERR_NULL;
+  if (T < 0 || T > h->cfg.max_num_inp_token_per_rank) return MEP_ERR_SHAPE;
+  if (T > 0 && !indices) return MEP_ERR_NULL;
+  if ((indices && !aligned16(indices)) || !aligned16(recv_counts) || !aligned16(src_token_pos))
+    return MEP_ERR_ALIGN;
+  const mep_config& c = h->cfg;
+  mep::PlanArgs a{};
+  a.indices = indices;
+  a.recv_counts = recv_counts;
+  a.spos = src_token_pos;
+  a.status = ws_ptr<uint32_t>(h, h->lay.status);
+  a.chunk_cnt = ws_ptr<int32_t>(h, h->lay.chunk_cnt);
+  a.mask = ws_ptr<uint64_t>(h, h->lay.mask);
+  a.rrow = ws_ptr<int32_t>(h, h->lay.rrow);
+  a.ufirst = ws_ptr<uint32_t>(h, h->lay.ufirst);
+  a.T = T;
+  a.k = c.num_experts_per_token;
+  a.R = c.world_size;
+  a.E = c.world_size * c.num_experts_per_rank;
+  a.cap = c.max_num_inp_token_per_rank;
+  a.spos_base = c.rank * c.world_size * c.max_num_inp_token_per_rank;
+  a.rdiv = h->rdiv;
+  h->plan_valid = false;
+  h->em_valid = false;
+  int rc = hip_rc(mep::launch_plan(a, (hipStream_t)stream));
+  if (rc != MEP_OK) return rc;
+  h->plan_valid = true;
+  h->plan_T = T;
+  return MEP_OK;
+}
+
+int mep_dispatch(mep_handle* h, const void* x, const float* weights, const int32_t* indices,
+                 void* recv_x, float* recv_scales, float* recv_weights, int32_t* recv_indices,
+                 void* stream) {
+  if (!h) return MEP_ERR_NULL;
+  if (!h->plan_valid) return MEP_ERR_STATE;
+  const mep_config& c = h->cfg;
+  const bool fp8 = c.quant == MEP_QUANT_FP8_E4M3_BLOCK128;
+  const int32_t T = h->plan_T;
+  if (!recv_x || !recv_weights || !recv_indices) return MEP_ERR_NULL;
+  if (fp8 && !recv_scales) return MEP_ERR_NULL;
+  if (T > 0 && (!x || !weights || !indices)) return MEP_ERR_NULL;
+  if ((x && !aligned16(x)) || (weights && !aligned16(weights)) ||
+      (indices && !aligned16(indices)) || !aligned16(recv_x) ||
+      (recv_scales && !aligned16(recv_scales)) || !aligned16(recv_weights) ||
+      !aligned16(recv_indices))
+    return MEP_ERR_ALIGN;
+  mep::DispatchArgs a{};
+  a.x = x;
+  a.w = weights;
+  a.idx = indices;
+  a.rrow = ws_ptr<int32_t>(h, h->lay.rrow);
+  a.ufirst = ws_ptr<uint32_t>(h, h->lay.ufirst);
+  a.recv_x = recv_x;
+  a.recv_scales = recv_scales;
+  a.recv_w = recv_weights;
+  a.recv_idx = recv_indices;
+  a.T = T;
+  a.H = c.hidden_dim;
+  a.k = c.num_experts_per_token;
+  return hip_rc(mep::launch_dispatch(a, fp8, (hipStream_t)stream));
+}
+
+int mep_to_expert_major(mep_handle* h, const void* recv_x, const float* recv_scales,
+                        const int32_t* recv_indices, const int32_t* recv_counts,
+                        const int32_t* src_token_pos, void* em_x, float* em_scales,
+                        int32_t* em_counts, int32_t* em_offsets, int32_t* em_src_pos,
+                        int64_t cap_em, void* stream) {
+  if (!h) return MEP_ERR_NULL;
+  if (!h->plan_valid) return MEP_ERR_STATE;
+  const mep_config& c = h->cfg;
+  const bool fp8 = c.quant == MEP_QUANT_FP8_E4M3_BLOCK128;
+  if (!recv_x || !recv_indices || !recv_counts || !src_token_pos || !em_x || !em_counts ||
+      !em_offsets || !em_src_pos)
+    return MEP_ERR_NULL;
+  if (fp8 && (!recv_scales || !em_scales)) return MEP_ERR_NULL;
+  if (cap_em < 0 || cap_em > INT32_MAX) return MEP_ERR_SHAPE;
+  if (!aligned16(recv_x) || !aligned16(recv_indices) || !aligned16(recv_counts) ||
+      !aligned16(src_token_pos) || !aligned16(em_x) || !aligned16(em_counts) ||
+      !aligned16(em_offsets) || !aligned16(em_src_pos) ||
+      (recv_scales && !aligned16(recv_scales)) || (em_scales && !aligned16(em_scales)))
+    return MEP_ERR_ALIGN;
+  mep::EmArgs a{};
+  a.recv_x = recv_x;
+  a.recv_scales = fp8 ? recv_scales : nullptr;
+  a.recv_idx = recv_indices;
+  a.recv_counts = recv_counts;
+  a.spos = src_token_pos;
+  a.rrow = ws_ptr<int32_t>(h, h->lay.rrow);
+  a.em_x = em_x;
+  a.em_scales = fp8 ? em_scales : nullptr;
+  a.em_counts = em_counts;
+  a.em_offsets = em_offsets;
+  a.em_src_pos = em_src_pos;
+  a.em_row = ws_ptr<int32_t>(h, h->lay.em_row);
+  a.lmask = ws_ptr<uint64_t>(h, h->lay.em_lmask);
+  a.ccnt = ws_ptr<int32_t>(h, h->lay.em_ccnt);
+  a.cbase = ws_ptr<int32_t>(h, h->lay.em_cbase);
+  a.status = ws_ptr<uint32_t>(h, h->lay.status);
+  a.cap_em = cap_em;
+  a.T = h->plan_T;
+  a.H = c.hidden_dim;
+  a.k = c.num_experts_per_token;
+  a.R = c.world_size;
+  a.epr = c.num_experts_per_rank;
+  a.cap = c.max_num_inp_token_per_rank;
+  a.CR = (c.max_num_inp_token_per_rank + mep::kChunk - 1) / mep::kChunk;
+  a.nb = fp8 ? c.hidden_dim / 128 : 0;
+  a.elem_bytes = fp8 ? 1 : 2;
+  a.spos_base = c.rank * c.world_size * c.max_num_inp_token_per_rank;
+  h->em_valid = false;
+  int rc = hip_rc(mep::launch_to_expert_major(a, (hipStream_t)stream));
+  if (rc != MEP_OK) return rc;
+  h->em_valid = true;
+  return MEP_OK;
+}
+
+int mep_combine(mep_handle* h, int32_t layout, const void* y, const float* weights, void* out,
+                void* stream) {
+  if (!h) return MEP_ERR_NULL;
+  if (layout != MEP_RANK_MAJOR && layout != MEP_EXPERT_MAJOR) return MEP_ERR_SHAPE;
+  if (!h->plan_valid) return MEP_ERR_STATE;
+  if (layout == MEP_EXPERT_MAJOR && !h->em_valid) return MEP_ERR_STATE;
+  const int32_t T = h->plan_T;
+  if (!out) return MEP_ERR_NULL;
+  if (T > 0 && (!y || !weights)) return MEP_ERR_NULL;
+  if ((y && !aligned16(y)) || (weights && !aligned16(weights)) || !aligned16(out))
+    return MEP_ERR_ALIGN;
+  mep::CombineArgs a{};
+  a.y = y;
+  a.w = weights;
+  a.rows = ws_ptr<int32_t>(h, layout == MEP_RANK_MAJOR ? h->lay.rrow : h->lay.em_row);
+  a.out = out;
+  a.T = T;
+  a.H = h->cfg.hidden_dim;
+  a.k = h->cfg.num_experts_per_token;
+  return hip_rc(mep::launch_combine(a, (hipStream_t)stream));
+}
+
+int mep_reset(mep_handle* h, void* stream) {
+  if (!h) return MEP_ERR_NULL;
+  int rc = hip_rc(mep::launch_reset(ws_ptr<uint32_t>(h, h->lay.status), (hipStream_t)stream));
+  h->plan_valid = false;
+  h->em_valid = false;
+  return rc;
+}
+
+int mep_get_status(mep_handle* h, void* stream, int32_t* device_status) {
+  if (!h || !device_status) return MEP_ERR_NULL;
+  uint32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, ws_ptr<uint32_t>(h, h->lay.status), sizeof(v),
+                                hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return MEP_ERR_HIP;
+  *device_status = (int32_t)v;
+  return v ? MEP_ERR_DEVICE : MEP_OK;
+}
+
+int mep_get_route(mep_handle* h, int32_t* recv_row, int32_t* em_row, void* stream) {
+  if (!h || !recv_row) return MEP_ERR_NULL;
+  if (!h->plan_valid) return MEP_ERR_STATE;
+  if (em_row && !h->em_valid) return MEP_ERR_STATE;
+  if (!aligned16(recv_row) || (em_row && !aligned16(em_row))) return MEP_ERR_ALIGN;
+  const int64_t n = (int64_t)h->plan_T * h->cfg.num_experts_per_token;
+  int rc = hip_rc(mep::launch_copy_i32(ws_ptr<int32_t>(h, h->lay.rrow), recv_row, n,
+                                       (hipStream_t)stream));
+  if (rc == MEP_OK && em_row)
+    rc = hip_rc(mep::launch_copy_i32(ws_ptr<int32_t>(h, h->lay.em_row), em_row, n,
+                                     (hipStream_t)stream));
+  return rc;
+}
+
+int mep_probe_e4m3(const float* in, uint8_t* out, int64_t n, void* stream) {
+  if (n < 0) return MEP_ERR_SHAPE;
+  if (n > 0 && (!in || !out)) return MEP_ERR_NULL;
+  if (n > 0 && (!aligned16(in) || !aligned16(out))) return MEP_ERR_ALIGN;
+  return hip_rc(mep::launch_probe_e4m3(in, out, n, (hipStream_t)stream));
+}
+
+int mep_probe_bf16(const float* in, uint16_t* out, int64_t n, void* stream) {
+  if (n < 0) return MEP_ERR_SHAPE;
+  if (n > 0 && (!in || !out)) return MEP_ERR_NULL;
+  if (n > 0 && (!aligned16(in) || !aligned16(out))) return MEP_ERR_ALIGN;
+  return hip_rc(mep::launch_probe_bf16(in, out, n, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// Internal declarations shared by the host ABI (mep_abi.cpp) and the kernels.
+// Not installed; the public interface is include/mep.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "mep.h"
+
+namespace mep {
+
+constexpr int kWave = 64;        // CDNA wavefront width
+constexpr int kMaxRanks = 64;    // a token's destination ranks fit one 64-bit mask
+constexpr int kMaxTopk = 32;     // first-occurrence bits of a token fit 32 bits
+constexpr int kMaxEpr = 64;      // a row's local experts fit one 64-bit mask
+constexpr int kChunk = 64;       // tokens (or receive rows) per scan chunk = one wave
+
+// Expert id -> rank without a hardware divide: for e < 4096 and epr <= 64,
+// (e * m) >> 20 with m = ceil(2^20 / epr) equals e / epr (checked on the host
+// for every expert id when a handle is created).
+struct RankDiv {
+  uint32_t m;
+  __host__ __device__ inline uint32_t operator()(uint32_t e) const { return (e * m) >> 20; }
+};
+
+// Byte offsets of the workspace sections (each 256-byte aligned).
+struct WsLayout {
+  size_t status;     // uint32: sticky MEP_DEV_* bits
+  size_t chunk_cnt;  // int32 [C][R]: rows each 64-token chunk sends to each rank
+  size_t mask;       // uint64 [cap]: destination-rank mask of each token (0 = dropped)
+  size_t rrow;       // int32 [cap][k]: flat receive row r*cap+slot of (t, j), -1 if dropped
+  size_t ufirst;     // uint32 [cap]: bit j set when top-k position j owns its rank's row
+  size_t em_row;     // int32 [cap][k]: expert-major row of (t, j), -1 if none
+  size_t em_lmask;   // uint64 [R*cap]: local experts named by each receive row
+  size_t em_ccnt;    // int32 [R][CR][epr]: per 64-row chunk, rows per local expert
+  size_t em_cbase;   // int32 [R][CR][epr]: first expert-major row of each chunk's run
+  size_t total;
+};
+
+WsLayout ws_layout(const mep_config& c);
+
+struct PlanArgs {
+  const int32_t* indices;  // [T,k]
+  int32_t* recv_counts;    // [R]
+  int32_t* spos;           // [R,cap]
+  uint32_t* status;
+  int32_t* chunk_cnt;
+  uint64_t* mask;
+  int32_t* rrow;
+  uint32_t* ufirst;
+  int32_t T, k, R, E, cap, spos_base;  // spos_base = rank * R * cap
+  RankDiv rdiv;
+};
+
+struct DispatchArgs {
+  const void* x;           // [T,H] bf16
+  const float* w;          // [T,k]
+  const int32_t* idx;      // [T,k]
+  const int32_t* rrow;
+  const uint32_t* ufirst;
+  void* recv_x;            // [R*cap, H] bf16 or e4m3
+  float* recv_scales;      // [R*cap, H/128]
+  float* recv_w;           // [R*cap, k]
+  int32_t* recv_idx;       // [R*cap, k]
+  int32_t T, H, k;
+};
+
+struct CombineArgs {
+  const void* y;           // bf16 rows
+  const float* w;          // [T,k]
+  const int32_t* rows;     // [T,k] row of (t, j) in y, -1 = skip
+  void* out;               // [T,H] bf16
+  int32_t T, H, k;
+};
+
+struct EmArgs {
+  const void* recv_x;
+  const float* recv_scales;
+  const int32_t* recv_idx;      // [R*cap, k]
+  const int32_t* recv_counts;   // [R]
+  const int32_t* spos;          // [R*cap]
+  const int32_t* rrow;          // plan rows, to find dropped tokens
+  void* em_x;
+  float* em_scales;
+  int32_t* em_counts;           // [E]
+  int32_t* em_offsets;          // [E+1]
+  int32_t* em_src_pos;          // [cap_em]
+  int32_t* em_row;              // [T,k]
+  uint64_t* lmask;              // [R*cap]
+  int32_t* ccnt;                // [R][CR][epr]
+  int32_t* cbase;               // [R][CR][epr]
+  uint32_t* status;
+  int64_t cap_em;
+  int32_t T, H, k, R, epr, cap, CR, nb, elem_bytes, spos_base;
+};
+
+// Launchers (return hipError_t of the launch).
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_dispatch(const DispatchArgs& a, bool fp8, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_to_expert_major(const EmArgs& a, hipStream_t s);
+hipError_t launch_reset(uint32_t* status, hipStream_t s);
+hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int64_t n, hipStream_t s);
+hipError_t launch_probe_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t s);
+hipError_t launch_probe_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);
+
+}  // namespace mep

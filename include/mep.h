@@ -1,0 +1,211 @@
+/*
+ * mep.h -- C ABI of libmep: MoE token dispatch and combine on one gfx950 GPU.
+ *
+ * The operation is the MORI-EP intra-node dispatch/combine ("MORI-EP User
+ * Guide", sections 2 Configuration and 3 Operator API; standard-MoE layout in
+ * section 4), restated for one device: the receive buffers of R "virtual
+ * ranks" are ordinary device buffers in local HBM, and this device's T tokens
+ * are routed into them.  Ranks own contiguous expert blocks: expert e lives on
+ * rank e / num_experts_per_rank.
+ *
+ * Conventions (every entry point):
+ *   - Pointers named x, recv_*, y, out, em_*, indices, weights, recv_counts,
+ *     src_token_pos and workspace are DEVICE pointers, caller-owned, borrowed
+ *     only for the duration of the asynchronous call on `stream`
+ *     (a hipStream_t passed as void*; NULL = the null stream).  The library
+ *     never allocates or frees device memory and never synchronises, except
+ *     in mep_get_status.
+ *   - All device pointers must be 16-byte aligned (MEP_ERR_ALIGN otherwise).
+ *   - Errors a host can see (null pointers, bad shapes, alignment, call order)
+ *     return a negative MEP_ERR_* code synchronously and launch nothing.
+ *     Data errors only the device can see (an expert id out of range, a
+ *     repeated expert in one token, expert-major overflow) set bits of a
+ *     sticky device status word (MEP_DEV_*), read by mep_get_status.
+ *   - A handle is not thread-safe; use one handle per stream.  Calls on one
+ *     handle must be issued on one stream (or externally ordered).
+ *   - Layouts are row-major and dense: [T,H] means row t at offset t*H.
+ */
+#ifndef MEP_H
+#define MEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ------------------------------------------------------- */
+#define MEP_OK 0
+#define MEP_ERR_NULL (-1)    /* a required pointer is NULL                     */
+#define MEP_ERR_CONFIG (-2)  /* config fields out of range or inconsistent      */
+#define MEP_ERR_SHAPE (-3)   /* a size argument out of range                    */
+#define MEP_ERR_ALIGN (-4)   /* a device pointer is not 16-byte aligned         */
+#define MEP_ERR_STATE (-5)   /* call order violated (e.g. dispatch before plan) */
+#define MEP_ERR_HIP (-6)     /* the HIP runtime reported an error               */
+#define MEP_ERR_DEVICE (-7)  /* mep_get_status: device status word is non-zero  */
+
+/* ---- device status bits (sticky until mep_reset) ------------------------- */
+#define MEP_DEV_BAD_INDEX 1   /* an expert id outside [0, E): that token is not
+                                 dispatched and combines to +0                  */
+#define MEP_DEV_DUP_EXPERT 2  /* a token names one expert twice (still routed)  */
+#define MEP_DEV_EM_OVERFLOW 4 /* expert-major rows exceed cap_em; rows past it
+                                 are dropped                                    */
+
+/* ---- payload and layout selectors --------------------------------------- */
+#define MEP_QUANT_NONE 0              /* dispatch payload: bf16 bit copy        */
+#define MEP_QUANT_FP8_E4M3_BLOCK128 1 /* dispatch payload: OCP E4M3 codes with
+                                         one fp32 scale per 128 columns          */
+#define MEP_RANK_MAJOR 0              /* combine input: [R, cap, H] bf16         */
+#define MEP_EXPERT_MAJOR 1            /* combine input: [cap_em, H] bf16         */
+
+/*
+ * Configuration.  Fields follow EpDispatchCombineConfig ("MORI-EP User Guide",
+ * section 2 Configuration); the multi-node fields (gpu_per_node,
+ * rdma_block_num, num_qp_per_pe, kernel_type) and launch geometry have no
+ * meaning on one device and are absent.
+ */
+typedef struct mep_config {
+  int32_t hidden_dim;                 /* H: > 0, multiple of 8; multiple of 128 with FP8  */
+  int32_t scale_dim;                  /* 0, or H/128 with MEP_QUANT_FP8_E4M3_BLOCK128      */
+  int32_t num_experts_per_rank;       /* epr: 1..64                                       */
+  int32_t num_experts_per_token;      /* k: 1..32, k <= R*epr                              */
+  int32_t max_num_inp_token_per_rank; /* cap: receive rows per rank and the largest T, >= 1 */
+  int32_t world_size;                 /* R virtual ranks: 1..64                           */
+  int32_t rank;                       /* source rank used in src_token_pos: 0..R-1        */
+  int32_t quant;                      /* MEP_QUANT_*  (the pages' data_type choice)        */
+} mep_config;
+
+typedef struct mep_handle mep_handle;
+
+/* Human-readable name of a MEP_OK / MEP_ERR_* code (static string). */
+const char *mep_error_string(int code);
+
+/* Bytes of device workspace a handle needs for this config, or 0 if the config
+ * is invalid.  The workspace holds the routing plan (receive row of every
+ * (token, top-k slot)), the expert-major maps and the status word. */
+size_t mep_workspace_bytes(const mep_config *cfg);
+
+/* Check the config and bind it to a caller-owned device workspace of at least
+ * mep_workspace_bytes(cfg) bytes.  Host-only: launches nothing, makes no HIP
+ * call.  *out receives a host-heap handle freed by mep_destroy. */
+int mep_create(const mep_config *cfg, void *workspace, size_t workspace_bytes,
+               mep_handle **out);
+int mep_destroy(mep_handle *h);
+
+/*
+ * Routing plan ("MORI-EP User Guide" section 3: dispatch() returns
+ * recv_num_token; get_dispatch_src_token_pos() gives each received row's
+ * origin).  For T tokens with top-k expert ids indices[T,k] (int32):
+ *   - each token is sent once to each distinct rank among its experts (the
+ *     first top-k position naming that rank owns the row; later positions on
+ *     the same rank share it);
+ *   - recv_counts[r] (int32, R entries) = rows rank r receives;
+ *   - inside a rank, rows are in ascending token order, and
+ *     src_token_pos[r*cap + s] (int32, [R,cap]) = rank*(R*cap) + t for the
+ *     token t in slot s < recv_counts[r]; entries past the count are not
+ *     written.
+ * The plan is kept in the workspace and stays valid (for any number of
+ * dispatch/combine calls: routing replay) until mep_reset or the next plan.
+ * 0 <= T <= cap.
+ */
+int mep_plan(mep_handle *h, const int32_t *indices, int32_t T, int32_t *recv_counts,
+             int32_t *src_token_pos, void *stream);
+
+/*
+ * Dispatch ("MORI-EP User Guide" section 3 dispatch()): every planned
+ * (token, rank) row receives
+ *   recv_x[r, s, :]       the token row: x[T,H] bf16 copied bit for bit
+ *                         (MEP_QUANT_NONE, recv_x is [R,cap,H] bf16), or its
+ *                         OCP E4M3 codes (FP8, recv_x is [R,cap,H] bytes):
+ *                         per 128 columns b, scale = amax_b / 448 (fp32) and
+ *                         code = E4M3_rne_satfinite(x / scale), signed zero
+ *                         when amax_b == 0;
+ *   recv_scales[r, s, b]  those scales (FP8 only; [R,cap,H/128] fp32, else NULL);
+ *   recv_weights[r, s, :] the token's k weights (fp32 [R,cap,k]);
+ *   recv_indices[r, s, :] the token's k expert ids (int32 [R,cap,k]).
+ * Rows past recv_counts[r] are not written.  Needs a valid plan; x, weights
+ * and indices hold the planned T tokens.
+ */
+int mep_dispatch(mep_handle *h, const void *x, const float *weights, const int32_t *indices,
+                 void *recv_x, float *recv_scales, float *recv_weights,
+                 int32_t *recv_indices, void *stream);
+
+/*
+ * Standard-MoE layout ("MORI-EP User Guide" section 4,
+ * convert_dispatch_output(): packed rows, per-expert counts, source info).
+ * From the dispatch outputs (recv_x, recv_scales or NULL, recv_indices,
+ * recv_counts, and the plan's src_token_pos), for every expert e in global
+ * order:
+ *   em_counts[e]        rows naming expert e (int32, E = R*epr entries);
+ *   em_offsets[e]       first row of e's segment; segments are padded to
+ *                       multiples of 128 rows (int32, E+1 entries,
+ *                       em_offsets[E] = rows used);
+ *   em_x[em_offsets[e] + i, :]      the i-th such receive row (ascending
+ *                       receive slot), same element type as recv_x;
+ *   em_scales[...]      its scales (FP8 only, else NULL);
+ *   em_src_pos[...]     its src_token_pos.
+ * Padding rows are not written.  cap_em is the row capacity of em_x /
+ * em_scales / em_src_pos; T*k + 127*E always suffices.  Rows past cap_em are
+ * dropped and set MEP_DEV_EM_OVERFLOW.  Needs a valid plan.
+ */
+int mep_to_expert_major(mep_handle *h, const void *recv_x, const float *recv_scales,
+                        const int32_t *recv_indices, const int32_t *recv_counts,
+                        const int32_t *src_token_pos, void *em_x, float *em_scales,
+                        int32_t *em_counts, int32_t *em_offsets, int32_t *em_src_pos,
+                        int64_t cap_em, void *stream);
+
+/*
+ * Combine ("MORI-EP User Guide" section 3 combine(): expert outputs gathered
+ * back to token order as a weighted combination; section 4
+ * combine_standard_moe() for the expert-major input; "Choosing an EP API and
+ * backend": gather combine in BF16/FP32).  For every planned token t:
+ *   out[t, h] = bf16_rne(acc),  acc = +0.0f, then for j = 0..k-1 in order
+ *               acc = fmaf(weights[t, j], y_j[h], acc)
+ * where y_j is the bf16 expert-output row holding (t, expert j):
+ *   MEP_RANK_MAJOR:   y is [R,cap,H]; y_j = y[rank of expert j, slot of t];
+ *                     a row shared by two experts is used once per expert;
+ *   MEP_EXPERT_MAJOR: y is [cap_em,H] in the layout mep_to_expert_major
+ *                     produced (needs that call after the current plan).
+ * weights are token-major fp32 [T,k]; out is [T,H] bf16.  Tokens that were
+ * not dispatched (bad expert id) produce +0.
+ */
+int mep_combine(mep_handle *h, int32_t layout, const void *y, const float *weights, void *out,
+                void *stream);
+
+/*
+ * Reset between iterations ("MORI-EP User Guide" section 3 reset()): clears
+ * the device status word on `stream` and invalidates the plan (and the
+ * expert-major maps) on the host.  Caller buffers are not touched: the
+ * library writes a caller buffer only during the call that names it.
+ */
+int mep_reset(mep_handle *h, void *stream);
+
+/* Synchronise `stream`, then copy the device status word (MEP_DEV_* bits) to
+ * *device_status.  Returns MEP_ERR_DEVICE if any bit is set, else MEP_OK. */
+int mep_get_status(mep_handle *h, void *stream, int32_t *device_status);
+
+/*
+ * Inspection of the current plan (for verification, "MORI-EP User Guide"
+ * section 3 get_dispatch_src_token_pos()): copies, on `stream`, the flat
+ * receive row r*cap + slot of every (token, top-k position) into
+ * recv_row[T,k] (int32, -1 for tokens not dispatched), and, if em_row is not
+ * NULL and mep_to_expert_major ran on this plan, the expert-major row of each
+ * (token, top-k position) into em_row[T,k].
+ */
+int mep_get_route(mep_handle *h, int32_t *recv_row, int32_t *em_row, void *stream);
+
+/*
+ * Codec probes: run, over n values, exactly the device conversions the
+ * kernels use.  in is fp32 [n]; mep_probe_e4m3 writes OCP E4M3 codes (uint8
+ * [n]) of in[i] (no scaling; values must satisfy |v| <= 464), mep_probe_bf16
+ * writes bf16 round-to-nearest-even bits (uint16 [n]).
+ */
+int mep_probe_e4m3(const float *in, uint8_t *out, int64_t n, void *stream);
+int mep_probe_bf16(const float *in, uint16_t *out, int64_t n, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MEP_H */

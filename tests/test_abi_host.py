@@ -1,0 +1,119 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched): the
+library loads, exports every entry point include/mep.h declares, and rejects
+bad configs, shapes, alignment and call order before touching the device.
+The device pointers used here are fake aligned addresses; every call below
+returns before any HIP call would dereference them."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import combine_mep_plan_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000000000  # 256-byte aligned, never dereferenced on the host
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "mep.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mep_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 13
+    L = C.CDLL(M.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def cfg(**kw):
+    base = dict(hidden_dim=7168, scale_dim=0, num_experts_per_rank=32, num_experts_per_token=8,
+                max_num_inp_token_per_rank=4096, world_size=8, rank=0, quant=M.MEP_QUANT_NONE)
+    base.update(kw)
+    return M.MepConfig(**base)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(hidden_dim=0), dict(hidden_dim=7170), dict(world_size=0), dict(world_size=65),
+    dict(num_experts_per_rank=0), dict(num_experts_per_rank=65),
+    dict(num_experts_per_token=0), dict(num_experts_per_token=33),
+    dict(num_experts_per_token=5, world_size=2, num_experts_per_rank=2),
+    dict(max_num_inp_token_per_rank=0), dict(rank=8), dict(rank=-1),
+    dict(scale_dim=56),                                    # scales without quant
+    dict(quant=M.MEP_QUANT_FP8_E4M3_BLOCK128, scale_dim=0),  # quant without scales
+    dict(quant=M.MEP_QUANT_FP8_E4M3_BLOCK128, hidden_dim=7176, scale_dim=56),
+    dict(quant=7),
+    dict(world_size=64, max_num_inp_token_per_rank=1 << 25),  # rows overflow int32
+])
+def test_bad_configs_rejected(bad):
+    c = cfg(**bad)
+    assert M.mep_workspace_bytes(c) == 0
+    h = C.c_void_p()
+    assert M.lib().mep_create(C.byref(c), FAKE, 1 << 40, C.byref(h)) == M.MEP_ERR_CONFIG
+    assert h.value is None
+
+
+def test_workspace_size_and_create_checks():
+    c = cfg(quant=M.MEP_QUANT_FP8_E4M3_BLOCK128, scale_dim=56)
+    n = M.mep_workspace_bytes(c)
+    assert n > 4096 * 8 * 4  # at least the receive-row map
+    L = M.lib()
+    h = C.c_void_p()
+    assert L.mep_create(C.byref(c), None, n, C.byref(h)) == M.MEP_ERR_NULL
+    assert L.mep_create(C.byref(c), FAKE + 8, n, C.byref(h)) == M.MEP_ERR_ALIGN
+    assert L.mep_create(C.byref(c), FAKE, n - 1, C.byref(h)) == M.MEP_ERR_SHAPE
+    assert L.mep_create(C.byref(c), FAKE, n, None) == M.MEP_ERR_NULL
+    assert L.mep_create(None, FAKE, n, C.byref(h)) == M.MEP_ERR_NULL
+    assert L.mep_create(C.byref(c), FAKE, n, C.byref(h)) == M.MEP_OK
+    assert L.mep_destroy(h) == M.MEP_OK
+
+
+@pytest.mark.parametrize("R,epr", [(1, 1), (4, 2), (8, 32), (16, 16), (32, 8), (64, 64), (7, 13)])
+def test_create_accepts_the_expert_rank_maps(R, epr):
+    # mep_create checks its divide-free expert -> rank map for every expert id
+    c = cfg(world_size=R, num_experts_per_rank=epr, num_experts_per_token=min(8, R * epr),
+            max_num_inp_token_per_rank=64)
+    h = C.c_void_p()
+    assert M.lib().mep_create(C.byref(c), FAKE, M.mep_workspace_bytes(c), C.byref(h)) == M.MEP_OK
+    M.lib().mep_destroy(h)
+
+
+def test_call_order_and_argument_checks_before_any_launch():
+    L = M.lib()
+    c = cfg()
+    n = M.mep_workspace_bytes(c)
+    h = C.c_void_p()
+    assert L.mep_create(C.byref(c), FAKE, n, C.byref(h)) == M.MEP_OK
+    h = h.value
+    f = FAKE
+    # no plan yet: dispatch, expert-major conversion, combine and route inspection refuse
+    assert L.mep_dispatch(h, f, f, f, f, None, f, f, None) == M.MEP_ERR_STATE
+    assert L.mep_to_expert_major(h, f, None, f, f, f, f, None, f, f, f, 1000, None) \
+        == M.MEP_ERR_STATE
+    assert L.mep_combine(h, M.MEP_RANK_MAJOR, f, f, f, None) == M.MEP_ERR_STATE
+    assert L.mep_combine(h, 5, f, f, f, None) == M.MEP_ERR_SHAPE
+    assert L.mep_get_route(h, f, None, None) == M.MEP_ERR_STATE
+    # plan argument checks
+    assert L.mep_plan(h, f, 4097, f, f, None) == M.MEP_ERR_SHAPE
+    assert L.mep_plan(h, f, -1, f, f, None) == M.MEP_ERR_SHAPE
+    assert L.mep_plan(h, None, 16, f, f, None) == M.MEP_ERR_NULL
+    assert L.mep_plan(h, f, 16, None, f, None) == M.MEP_ERR_NULL
+    assert L.mep_plan(h, f + 4, 16, f, f, None) == M.MEP_ERR_ALIGN
+    assert L.mep_plan(h, f, 16, f, f + 4, None) == M.MEP_ERR_ALIGN
+    # probes and status
+    assert L.mep_probe_e4m3(f, f, -1, None) == M.MEP_ERR_SHAPE
+    assert L.mep_probe_bf16(None, f, 8, None) == M.MEP_ERR_NULL
+    assert L.mep_probe_bf16(f + 2, f, 8, None) == M.MEP_ERR_ALIGN
+    assert L.mep_get_status(None, None, None) == M.MEP_ERR_NULL
+    assert L.mep_destroy(h) == M.MEP_OK
+    assert L.mep_destroy(None) == M.MEP_ERR_NULL
+
+
+def test_error_strings():
+    for code in range(-7, 1):
+        assert M.mep_error_string(code) not in ("", "unknown")
+    assert M.mep_error_string(-99) == "unknown"

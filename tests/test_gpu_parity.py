@@ -1,0 +1,258 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bar: bit-exact for counts, src_token_pos, receive rows, route, E4M3 codes,
+scales, weights, ids and the expert-major layout; combine within 1 bf16 ulp
+(the kernels mirror the oracle's fused multiply-add order, so 0 is expected
+and the exact fraction is printed).
+
+Sources: "MORI-EP User Guide" section 3 (dispatch, combine, reset,
+get_dispatch_src_token_pos), section 4 (standard-MoE layout), section 7
+(identity expert); "Choosing an EP API and backend" (OCP E4M3 on gfx950).
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import combine_mep_plan_amd as M
+from oracle import oracle as O
+from synthetic import WORKLOADS, Workload, make_inputs
+
+from _gpu_harness import (SENT32, bf16_ulp_diff, check_combine, check_plan_dispatch, dev,
+                          gpu_plan_dispatch, host, oracle_plan_dispatch, run_full)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# device conversions
+# ---------------------------------------------------------------------------
+
+def test_probe_e4m3_matches_oracle():
+    tab = O.e4m3_decode_table()[:0x7F]
+    vals = [tab[c] for c in range(0x7F)] + [0.5 * (tab[c - 1] + tab[c]) for c in range(1, 0x7F)]
+    b = np.array(vals, np.float32).view(np.uint32)
+    near = np.concatenate([b, b + 1, b + 2, np.maximum(b, 1) - 1]).view(np.float32)
+    top = int(np.float32(448.0).view(np.uint32)) + 2  # quotients reach 448 * (1 + 2^-23)
+    sweep = np.arange(0, top + 1, 61, dtype=np.uint32).view(np.float32)
+    extra = np.float32([448.0, np.nextafter(np.float32(448), np.float32(1e9)), 0.0, 2.0 ** -10,
+                        2.0 ** -11, 1e-30, 1e-45])
+    v = np.concatenate([near, sweep, extra])
+    v = np.concatenate([v, -v]).astype(np.float32)
+    v = np.ascontiguousarray(v[np.abs(v) <= np.float32(448.0) * np.float32(1 + 2 ** -23)])
+    out = torch.empty(v.size, dtype=torch.uint8, device="cuda")
+    M.mep_probe_e4m3(dev(v), out, v.size)
+    got = host(out)
+    ref = O.e4m3_encode(v)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(float(v[i]), hex(got[i]), hex(ref[i])) for i in bad[:10]]
+
+
+def test_probe_bf16_matches_oracle():
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 2**32, size=2_000_000, dtype=np.uint64).astype(np.uint32)
+    v = bits.view(np.float32)
+    v = v[np.isfinite(v)]
+    ties = ((rng.integers(0, 2**16, size=200_000).astype(np.uint32) << 16) | 0x8000) \
+        .view(np.float32)
+    ties = ties[np.isfinite(ties)]
+    den = rng.integers(1, 2**23, size=200_000).astype(np.uint32).view(np.float32)
+    v = np.ascontiguousarray(np.concatenate([v, ties, den, -den]).astype(np.float32))
+    out = torch.empty(v.size, dtype=torch.int16, device="cuda")
+    M.mep_probe_bf16(dev(v), out, v.size)
+    got = host(out, np.uint16)
+    ref = O.bf16_rne(v)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(float(v[i]), hex(got[i]), hex(ref[i])) for i in bad[:10]]
+
+
+# ---------------------------------------------------------------------------
+# whole path, reduced and full sizes
+# ---------------------------------------------------------------------------
+
+def _variant(name, **kw):
+    return dataclasses.replace(WORKLOADS[name], **kw)
+
+
+SMALL = [
+    ("tiny", WORKLOADS["tiny"], (0, 1, 2)),
+    ("tiny_T5", _variant("tiny", tokens=5), (3,)),
+    ("decode_T77", _variant("decode", tokens=77), (0,)),
+    ("decode", WORKLOADS["decode"], (1,)),
+    ("prefill_T300", _variant("prefill", tokens=300, cap=512), (0, 1)),
+    ("skew_T300", _variant("skew", tokens=300, cap=300), (0,)),
+    ("stdmoe_T300", _variant("stdmoe", tokens=300, cap=320), (0,)),
+    # ragged rows: 1152 = 9 x 128 columns leaves a partial lane sweep per row
+    ("odd_bf16", Workload("odd_bf16", 131, 1152, 5, 3, 3, 140, "none", "uniform", "identity",
+                          "rank_major"), (0,)),
+    ("odd_fp8", Workload("odd_fp8", 131, 1152, 5, 3, 3, 140, "fp8", "uniform", "dequant_half",
+                         "rank_major"), (0,)),
+    ("odd_em", Workload("odd_em", 97, 1152, 3, 5, 4, 100, "fp8", "uniform", "dequant",
+                        "expert_major"), (0,)),
+    ("em_bf16", Workload("em_bf16", 150, 256, 4, 4, 3, 150, "none", "uniform", "identity",
+                         "expert_major"), (0,)),
+    # top-k above 8 takes the wide combine variant
+    ("top12", Workload("top12", 70, 512, 6, 4, 12, 70, "none", "uniform", "identity",
+                       "rank_major"), (0,)),
+    ("one_rank", Workload("one_rank", 64, 256, 1, 16, 4, 64, "none", "uniform", "identity",
+                          "rank_major"), (0,)),
+    ("wide64", Workload("wide64", 100, 256, 64, 2, 8, 100, "fp8", "uniform", "dequant_half",
+                        "rank_major"), (0,)),
+]
+
+
+@pytest.mark.parametrize("label,wl,seeds", SMALL, ids=[s[0] for s in SMALL])
+def test_parity_small(label, wl, seeds):
+    for seed in seeds:
+        _say(f"[parity-small] {label} seed={seed} T={wl.tokens} H={wl.hidden} R={wl.ranks}")
+        st = run_full(wl, seed, src_rank=seed % wl.ranks)
+        _say(f"    U={st['U']} max_ulp={st['max_ulp']} exact={st['exact_frac']:.6f}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "skew", "stdmoe"])
+def test_parity_full_size(name):
+    wl = WORKLOADS[name]
+    _say(f"[parity-full] {name} T={wl.tokens} H={wl.hidden} R={wl.ranks} k={wl.topk}")
+    st = run_full(wl, 0)
+    _say(f"    U={st['U']} max_ulp={st['max_ulp']} exact={st['exact_frac']:.6f}")
+
+
+# ---------------------------------------------------------------------------
+# edge cases and lifecycle
+# ---------------------------------------------------------------------------
+
+def test_empty_batch():
+    wl = _variant("tiny", tokens=0)
+    inp = {"x": np.zeros((0, wl.hidden), np.uint16), "indices": np.zeros((0, wl.topk), np.int32),
+           "weights": np.zeros((0, wl.topk), np.float32)}
+    m = M.Mep(wl.hidden, wl.experts_per_rank, wl.topk, wl.cap, wl.ranks)
+    counts = torch.full((wl.ranks,), 7, dtype=torch.int32, device="cuda")
+    spos = torch.full((wl.ranks, wl.cap), SENT32, dtype=torch.int32, device="cuda")
+    M.mep_plan(m.h, None, 0, counts, spos)
+    out = torch.empty((1, wl.hidden), dtype=torch.int16, device="cuda")
+    rx = torch.zeros((wl.ranks, wl.cap, wl.hidden), dtype=torch.int16, device="cuda")
+    rw = torch.zeros((wl.ranks, wl.cap, wl.topk), dtype=torch.float32, device="cuda")
+    ri = torch.zeros((wl.ranks, wl.cap, wl.topk), dtype=torch.int32, device="cuda")
+    M.mep_dispatch(m.h, None, None, None, rx, None, rw, ri)
+    M.mep_combine(m.h, M.MEP_RANK_MAJOR, None, None, out)
+    torch.cuda.synchronize()
+    assert np.all(host(counts) == 0)
+    assert np.all(host(spos) == SENT32)
+    assert M.mep_get_status(m.h) == 0
+    del inp
+
+
+def test_full_capacity_and_single_rank_hotspot():
+    # T == cap and every token on rank 0: rank 0 receives cap rows
+    wl = Workload("hot", 256, 512, 4, 4, 4, 256, "fp8", "uniform", "dequant_half", "rank_major")
+    inp = make_inputs(wl, 0)
+    rng = np.random.default_rng(9)
+    inp["indices"] = np.stack([rng.permutation(4)[:4] for _ in range(256)]).astype(np.int32)
+    g = gpu_plan_dispatch(wl, inp)
+    pl, d = oracle_plan_dispatch(wl, inp)
+    check_plan_dispatch(wl, inp, g, pl, d)
+    assert host(g.counts)[0] == 256
+
+
+def test_bad_and_duplicate_expert_ids():
+    wl = _variant("tiny", tokens=16)
+    inp = make_inputs(wl, 5)
+    idx = inp["indices"].copy()
+    idx[3] = [1, 99]      # out of range -> token 3 not dispatched
+    idx[7] = [-4, 2]      # negative -> token 7 not dispatched
+    idx[9] = [5, 5]       # repeated expert -> still routed, status bit
+    inp["indices"] = idx
+    g = gpu_plan_dispatch(wl, inp)
+    pl, d = oracle_plan_dispatch(wl, inp)
+    assert pl["status"] == M.MEP_DEV_BAD_INDEX | M.MEP_DEV_DUP_EXPERT
+    check_plan_dispatch(wl, inp, g, pl, d)
+    out = torch.empty((wl.tokens, wl.hidden), dtype=torch.int16, device="cuda")
+    M.mep_combine(g.m.h, M.MEP_RANK_MAJOR, g.recv_x, g.w, out)
+    ref = O.combine(d["recv_x"], inp["weights"], idx, pl, wl.experts_per_rank, wl.cap)
+    check_combine(host(out, np.uint16), ref)
+    assert np.all(host(out, np.uint16)[[3, 7]] == 0)
+    assert M.mep_get_status(g.m.h) == M.MEP_DEV_BAD_INDEX | M.MEP_DEV_DUP_EXPERT
+    M.mep_reset(g.m.h)
+    assert M.mep_get_status(g.m.h) == 0
+
+
+def test_reset_invalidates_plan():
+    wl = WORKLOADS["tiny"]
+    inp = make_inputs(wl, 1)
+    g = gpu_plan_dispatch(wl, inp)
+    counts = host(g.counts).copy()
+    M.mep_reset(g.m.h)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(g.counts), counts)  # caller buffers untouched
+    with pytest.raises(M.MepError) as ei:
+        M.mep_dispatch(g.m.h, g.x, g.w, g.idx, g.recv_x, None, g.recv_w, g.recv_i)
+    assert ei.value.code == M.MEP_ERR_STATE
+    with pytest.raises(M.MepError):
+        M.mep_combine(g.m.h, M.MEP_RANK_MAJOR, g.recv_x, g.w, g.recv_x)
+
+
+def test_routing_replay_and_determinism():
+    # one plan serves several dispatch/combine rounds with new token rows; repeated
+    # runs give identical bits
+    wl = _variant("prefill", tokens=200, cap=256)
+    inp = make_inputs(wl, 2)
+    g = gpu_plan_dispatch(wl, inp)
+    pl = O.plan(inp["indices"], wl.ranks, wl.experts_per_rank, wl.cap)
+    rng = np.random.default_rng(4)
+    for round_ in range(3):
+        x2 = torch.from_numpy(rng.standard_normal((wl.tokens, wl.hidden), dtype=np.float32)) \
+            .to(torch.bfloat16).view(torch.int16)
+        x2_np = x2.numpy().view(np.uint16)
+        M.mep_dispatch(g.m.h, x2.cuda(), g.w, g.idx, g.recv_x, g.recv_s, g.recv_w, g.recv_i)
+        d = O.dispatch(x2_np, inp["weights"], inp["indices"], pl, wl.ranks, wl.experts_per_rank,
+                       wl.cap, True)
+        inp2 = dict(inp, x=x2_np)
+        check_plan_dispatch(wl, inp2, g, pl, d)
+    first = host(g.recv_x).copy()
+    M.mep_dispatch(g.m.h, x2.cuda(), g.w, g.idx, g.recv_x, g.recv_s, g.recv_w, g.recv_i)
+    assert np.array_equal(first, host(g.recv_x))
+
+
+def test_combine_random_expert_rows():
+    # non-identity expert rows (random per receive row) pin the gather indices
+    for wl in (_variant("decode", tokens=100, cap=128), _variant("skew", tokens=150, cap=160)):
+        inp = make_inputs(wl, 8)
+        g = gpu_plan_dispatch(wl, inp)
+        pl = O.plan(inp["indices"], wl.ranks, wl.experts_per_rank, wl.cap)
+        rng = np.random.default_rng(10)
+        y = torch.from_numpy(rng.standard_normal((wl.ranks, wl.cap, wl.hidden), dtype=np.float32))
+        y = y.to(torch.bfloat16).view(torch.int16)
+        w = rng.uniform(-1, 1, size=inp["weights"].shape).astype(np.float32)
+        out = torch.empty((wl.tokens, wl.hidden), dtype=torch.int16, device="cuda")
+        M.mep_combine(g.m.h, M.MEP_RANK_MAJOR, y.cuda(), dev(w), out)
+        ref = O.combine(y.numpy().view(np.uint16), w, inp["indices"], pl, wl.experts_per_rank,
+                        wl.cap)
+        st = check_combine(host(out, np.uint16), ref)
+        _say(f"    random rows {wl.name}: max_ulp={st['max_ulp']} exact={st['exact_frac']:.6f}")
+
+
+def test_expert_major_overflow_sets_status():
+    wl = _variant("stdmoe", tokens=64, cap=64)
+    inp = make_inputs(wl, 0)
+    g = gpu_plan_dispatch(wl, inp)
+    cap_em = 700  # 64*8 rows need far more than 700 once each expert is padded to 128
+    em_x = torch.zeros((cap_em, wl.hidden), dtype=torch.uint8, device="cuda")
+    em_s = torch.zeros((cap_em, wl.hidden // 128), dtype=torch.float32, device="cuda")
+    em_c = torch.zeros(wl.experts, dtype=torch.int32, device="cuda")
+    em_o = torch.zeros(wl.experts + 1, dtype=torch.int32, device="cuda")
+    em_p = torch.full((cap_em,), SENT32, dtype=torch.int32, device="cuda")
+    M.mep_to_expert_major(g.m.h, g.recv_x, g.recv_s, g.recv_i, g.counts, g.spos, em_x, em_s, em_c,
+                          em_o, em_p, cap_em)
+    assert M.mep_get_status(g.m.h) == M.MEP_DEV_EM_OVERFLOW
+    pl, d = oracle_plan_dispatch(wl, inp)
+    em = O.to_expert_major(d, pl, wl.ranks, wl.experts_per_rank, wl.cap, wl.tokens, cap_em)
+    assert em["status"] == O.ST_EM_OVERFLOW
+    assert np.array_equal(host(em_c), em["em_counts"])
+    assert np.array_equal(host(em_p), np.where(em["em_src_pos"] >= 0, em["em_src_pos"], SENT32))
