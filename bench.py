@@ -1,7 +1,8 @@
 """Benchmark of the MoE dispatch/combine hot path on one MI355X.
 
-One step = the whole path on one batch: routing plan, FP8 dispatch
-(OCP E4M3, one fp32 scale per 128 columns) and bf16 combine, then reset, for
+One step = the whole path on one batch: routing plan and FP8 dispatch
+(OCP E4M3, one fp32 scale per 128 columns) through the fused
+mep_plan_dispatch, bf16 combine, then reset, for
 4096 tokens x 7168 hidden, top-8 of 256 experts on 8 virtual ranks -- the
 shape of the MORI README bandwidth table ("4096 tokens, 7168 hidden, top-8,
 FP8 dispatch + BF16 combine").  Inputs are synthetic and already resident in
@@ -117,46 +118,67 @@ def setup_prefill(M, torch, wl, inp, nsets):
     return m, sets, U
 
 
+def _loop_ms(torch, stream, fn, n):
+    """Average ms per call of fn(i) over n back-to-back calls on `stream`,
+    timed by two HIP events (none inside the loop)."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(n):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
 def time_prefill(M, torch, m, sets, wl, steps, warmup):
+    """Headline loop: whole steps back to back.  Then one loop per kernel
+    (same rotation of buffer sets) for its average launch duration.  Every set
+    has the same routing, so the plan in the handle serves any set."""
     T = wl.tokens
     stream = torch.cuda.current_stream()
-    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    n = len(sets)
 
-    def step(s, marks=None):
-        if marks is not None:
-            marks[0].record(stream)
+    def plan(i):
+        s = sets[i % n]
         M.mep_plan(m.h, s["idx"], T, s["counts"], s["spos"], stream)
-        if marks is not None:
-            marks[1].record(stream)
+
+    def dispatch(i):
+        s = sets[i % n]
         M.mep_dispatch(m.h, s["x"], s["w"], s["idx"], s["rx"], s["rs"], s["rw"], s["ri"], stream)
-        if marks is not None:
-            marks[2].record(stream)
+
+    def combine(i):
+        s = sets[i % n]
         M.mep_combine(m.h, M.MEP_RANK_MAJOR, s["y"], s["w"], s["out"], stream)
-        if marks is not None:
-            marks[3].record(stream)
+
+    def plan_dispatch(i):
+        s = sets[i % n]
+        M.mep_plan_dispatch(m.h, s["idx"], T, s["counts"], s["spos"], s["x"], s["w"], s["rx"],
+                            s["rs"], s["rw"], s["ri"], stream)
+
+    def step(i):
+        plan_dispatch(i)
+        combine(i)
         M.mep_reset(m.h, stream)
 
     for i in range(warmup):
-        step(sets[i % len(sets)])
-    marks = [[ev() for _ in range(4)] for _ in range(steps)]
-    start, end = ev(), ev()
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(steps):
-        step(sets[i % len(sets)], marks[i])
-    end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    plan_ms = [mk[0].elapsed_time(mk[1]) for mk in marks]
-    disp_ms = [mk[1].elapsed_time(mk[2]) for mk in marks]
-    comb_ms = [mk[2].elapsed_time(mk[3]) for mk in marks]
+        step(i)
+    step_ms = _loop_ms(torch, stream, step, steps)
     assert M.mep_get_status(m.h, stream) == 0
-    return total_ms, plan_ms, disp_ms, comb_ms
+    times = {
+        "plan_dispatch": _loop_ms(torch, stream, plan_dispatch, steps),
+        "combine": _loop_ms(torch, stream, combine, steps),
+        "plan": _loop_ms(torch, stream, plan, steps),
+        "dispatch": _loop_ms(torch, stream, dispatch, steps),
+    }
+    M.mep_reset(m.h, stream)
+    return step_ms, times
 
 
 def time_decode(M, torch, wl, inp, reps, warmup):
-    """128-token latency: plan+dispatch and combine, bf16 both ways, identity
-    expert (combine reads the receive buffers)."""
+    """128-token latency, bf16 both ways, identity expert (combine reads the
+    receive buffers): plan+dispatch as one call sequence, and combine, each
+    between its own pair of events with the GPU idle before it."""
     T, H, R, cap, k = wl.tokens, wl.hidden, wl.ranks, wl.cap, wl.topk
     m = M.Mep(H, wl.experts_per_rank, k, cap, R, fp8=False)
     nsets = 4
@@ -175,24 +197,34 @@ def time_decode(M, torch, wl, inp, reps, warmup):
         })
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    res = {"plan": [], "dispatch": [], "plan_dispatch": [], "combine": []}
+    res = {"plan_dispatch": [], "combine": [], "plan": [], "dispatch": []}
     for i in range(warmup + reps):
         s = sets[i % nsets]
-        e = [ev() for _ in range(4)]
+        e = [ev() for _ in range(8)]
+        torch.cuda.synchronize()
         e[0].record(stream)
-        M.mep_plan(m.h, s["idx"], T, s["counts"], s["spos"], stream)
+        M.mep_plan_dispatch(m.h, s["idx"], T, s["counts"], s["spos"], s["x"], s["w"], s["rx"],
+                            None, s["rw"], s["ri"], stream)
         e[1].record(stream)
-        M.mep_dispatch(m.h, s["x"], s["w"], s["idx"], s["rx"], None, s["rw"], s["ri"], stream)
+        torch.cuda.synchronize()
         e[2].record(stream)
         M.mep_combine(m.h, M.MEP_RANK_MAJOR, s["rx"], s["w"], s["out"], stream)
         e[3].record(stream)
+        torch.cuda.synchronize()
+        e[4].record(stream)
+        M.mep_plan(m.h, s["idx"], T, s["counts"], s["spos"], stream)
+        e[5].record(stream)
+        torch.cuda.synchronize()
+        e[6].record(stream)
+        M.mep_dispatch(m.h, s["x"], s["w"], s["idx"], s["rx"], None, s["rw"], s["ri"], stream)
+        e[7].record(stream)
         M.mep_reset(m.h, stream)
-        torch.cuda.synchronize()  # latency: one call at a time
+        torch.cuda.synchronize()
         if i >= warmup:
-            res["plan"].append(e[0].elapsed_time(e[1]) * 1e3)
-            res["dispatch"].append(e[1].elapsed_time(e[2]) * 1e3)
-            res["plan_dispatch"].append(e[0].elapsed_time(e[2]) * 1e3)
+            res["plan_dispatch"].append(e[0].elapsed_time(e[1]) * 1e3)
             res["combine"].append(e[2].elapsed_time(e[3]) * 1e3)
+            res["plan"].append(e[4].elapsed_time(e[5]) * 1e3)
+            res["dispatch"].append(e[6].elapsed_time(e[7]) * 1e3)
     U = int(sets[0]["counts"].sum().item())
     out = {f"{k}_us": round(statistics.median(v), 2) for k, v in res.items()}
     out["tokens"] = T
@@ -200,6 +232,20 @@ def time_decode(M, torch, wl, inp, reps, warmup):
     out["dispatch_bytes"] = dispatch_bytes(T, H, k, U, False) + plan_bytes(T, k, R, U)
     out["combine_bytes"] = combine_bytes(T, H, k, U)
     return out
+
+
+def copy_ceiling(torch, nbytes=512 << 20, reps=20):
+    """Read+write rate of a plain device-to-device copy (torch's copy kernel) over
+    rotating 512 MiB buffers: the practical HBM ceiling for streaming traffic."""
+    n = 3
+    src = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(n)]
+    dst = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(n)]
+    stream = torch.cuda.current_stream()
+    for i in range(3):
+        dst[i % n].copy_(src[i % n])
+    ms = _loop_ms(torch, stream, lambda i: dst[i % n].copy_(src[(i + 1) % n]), reps)
+    del src, dst
+    return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
 
 
 def cpu_baseline(wl, inp, budget_s=20.0):
@@ -257,32 +303,31 @@ def main():
           f"epr={wl.experts_per_rank} k={wl.topk} sets={args.sets}", file=sys.stderr, flush=True)
     m, sets, U = setup_prefill(M, torch, wl, inp, args.sets)
     T, H, k, R = wl.tokens, wl.hidden, wl.topk, wl.ranks
-    total_ms, plan_ms, disp_ms, comb_ms = time_prefill(M, torch, m, sets, wl, args.steps,
-                                                       args.warmup)
-    ms_step = total_ms / args.steps
+    ms_step, times = time_prefill(M, torch, m, sets, wl, args.steps, args.warmup)
     b_plan, b_disp, b_comb = (plan_bytes(T, k, R, U), dispatch_bytes(T, H, k, U, True),
                               combine_bytes(T, H, k, U))
     step_bytes = b_plan + b_disp + b_comb
     value = step_bytes / (ms_step * 1e-3) / 1e9
     print(f"[bench] prefill done: {ms_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
 
-    avg = lambda v: sum(v) / len(v)  # noqa: E731
-    ops = {
-        "plan": {"us": round(avg(plan_ms) * 1e3, 2), "bytes": b_plan},
-        "dispatch": {"us": round(avg(disp_ms) * 1e3, 2), "bytes": b_disp},
-        "combine": {"us": round(avg(comb_ms) * 1e3, 2), "bytes": b_comb},
-    }
-    for o in ops.values():
-        o["GBps"] = round(o["bytes"] / (o["us"] * 1e-6) / 1e9, 1)
+    nbytes = {"plan_dispatch": b_plan + b_disp, "combine": b_comb, "plan": b_plan,
+              "dispatch": b_disp}
+    ops = {}
+    for name, ms in times.items():
+        o = {"us": round(ms * 1e3, 2), "bytes": nbytes[name]}
+        o["GBps"] = round(o["bytes"] / (ms * 1e-3) / 1e9, 1)
         o["frac"] = round(o["GBps"] / HBM_PEAK_GBS, 4)
-    dom = max(("dispatch", "combine"), key=lambda n: ops[n]["us"])
-    kernel_file = {"dispatch": "dispatch.hip", "combine": "combine.hip"}[dom]
+        ops[name] = o
+    dom = max(("plan_dispatch", "combine"), key=lambda n: ops[n]["us"])
+    kernel_file = {"plan_dispatch": "dispatch.hip", "combine": "combine.hip"}[dom]
     achieved = ops[dom]["bytes"] / (ops[dom]["us"] * 1e-6) / 1e9
     traffic = profile_traffic(f"{dom}_prefill_pmc.txt", src_digest(kernel_file))
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "algorithmic_bytes": ops[dom]["bytes"]}
 
+    copy_gbs = copy_ceiling(torch)
+    roofline["copy_ceiling_GBps"] = copy_gbs
     dwl = WORKLOADS["decode"]
     print("[bench] decode latency", file=sys.stderr, flush=True)
     decode = time_decode(M, torch, dwl, make_inputs(dwl, 0), args.decode_reps, 20)

@@ -12,6 +12,6 @@ from ._binding import (  # noqa: F401
     MEP_ERR_DEVICE, MEP_ERR_HIP, MEP_ERR_NULL, MEP_ERR_SHAPE, MEP_ERR_STATE, MEP_EXPERT_MAJOR,
     MEP_OK, MEP_QUANT_FP8_E4M3_BLOCK128, MEP_QUANT_NONE, MEP_RANK_MAJOR, LIB_PATH, MepConfig,
     MepError, Mep, lib, mep_combine, mep_create, mep_destroy, mep_dispatch, mep_error_string,
-    mep_get_route, mep_get_status, mep_plan, mep_probe_bf16, mep_probe_e4m3, mep_reset,
+    mep_get_route, mep_get_status, mep_plan, mep_plan_dispatch, mep_probe_bf16, mep_probe_e4m3, mep_reset,
     mep_to_expert_major, mep_workspace_bytes,
 )

@@ -69,6 +69,7 @@ def lib() -> C.CDLL:
             "mep_destroy": ([p], C.c_int),
             "mep_plan": ([p, p, i32, p, p, p], C.c_int),
             "mep_dispatch": ([p, p, p, p, p, p, p, p, p], C.c_int),
+            "mep_plan_dispatch": ([p, p, i32, p, p, p, p, p, p, p, p, p], C.c_int),
             "mep_to_expert_major": ([p, p, p, p, p, p, p, p, p, p, p, i64, p], C.c_int),
             "mep_combine": ([p, i32, p, p, p, p], C.c_int),
             "mep_reset": ([p, p], C.c_int),
@@ -140,6 +141,14 @@ def mep_dispatch(h, x, weights, indices, recv_x, recv_scales, recv_weights, recv
     _check("mep_dispatch", lib().mep_dispatch(h, _ptr(x), _ptr(weights), _ptr(indices),
                                               _ptr(recv_x), _ptr(recv_scales),
                                               _ptr(recv_weights), _ptr(recv_indices), s))
+
+
+def mep_plan_dispatch(h, indices, T, recv_counts, src_token_pos, x, weights, recv_x, recv_scales,
+                      recv_weights, recv_indices, stream=None) -> None:
+    s = _stream(stream, recv_x)
+    _check("mep_plan_dispatch", lib().mep_plan_dispatch(
+        h, _ptr(indices), T, _ptr(recv_counts), _ptr(src_token_pos), _ptr(x), _ptr(weights),
+        _ptr(recv_x), _ptr(recv_scales), _ptr(recv_weights), _ptr(recv_indices), s))
 
 
 def mep_to_expert_major(h, recv_x, recv_scales, recv_indices, recv_counts, src_token_pos, em_x,

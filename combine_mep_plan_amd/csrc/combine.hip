@@ -9,11 +9,11 @@
 // multiply-add per top-k position in order j = 0..k-1, then bf16 round to
 // nearest even -- a fixed order, so the result does not depend on timing.
 //
-// One wavefront per token; each lane owns 8 columns (16 bytes) of every row.
-// For each column group all k row loads are issued before the k FMAs, so a
-// wave keeps k * 1 KiB of loads in flight.  A rank row shared by two top-k
-// positions is loaded twice; the second load is served by the cache, so HBM
-// reads stay one per (token, rank).
+// A row is cut into slices of 2 x 16 bytes per lane (2 KiB per wave); one wave
+// handles one (token, slice), so a 4096-token batch runs ~29k short waves.
+// Each distinct expert-output row is loaded once (positions that share a rank
+// row reuse its registers) with non-temporal loads -- the rows are read
+// exactly once -- and all of a slice's loads are issued before the FMAs.
 #include "dev.h"
 #include "mep_internal.h"
 
@@ -21,12 +21,14 @@ namespace mep {
 
 namespace {
 
-template <int KMAX, int UNROLL>
+constexpr int kUnitsPerLane = 2;
+
+template <int KMAX, bool DEDUPE>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int lane = threadIdx.x & 63;
-  int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int g = first_lane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  const int t = g / a.slices, sl = g - t * a.slices;
   if (t >= a.T) return;
-  t = first_lane(t);
   const int nv = a.H / 8;
   int row[KMAX];
   float w[KMAX];
@@ -35,48 +37,75 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     row[j] = j < a.k ? a.rows[(size_t)t * a.k + j] : -1;
     w[j] = j < a.k ? a.w[(size_t)t * a.k + j] : 0.0f;
   }
+  // src[j]: first top-k position holding the same row as j (uniform)
+  int src[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    src[j] = j;
+    if (DEDUPE) {
+#pragma unroll
+      for (int jj = KMAX - 1; jj >= 0; --jj)
+        if (jj < j && row[jj] == row[j]) src[j] = jj;
+    }
+  }
   const u32x4* y = reinterpret_cast<const u32x4*>(a.y);
   u32x4* out = reinterpret_cast<u32x4*>(a.out) + (size_t)t * nv;
-  for (int v0 = 0; v0 < nv; v0 += kWave * UNROLL) {
-    u32x4 in[UNROLL][KMAX];
+  const int v0 = sl * (kWave * kUnitsPerLane) + lane;
+  u32x4 in[kUnitsPerLane][KMAX];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int v = v0 + u * kWave + lane;
+  for (int u = 0; u < kUnitsPerLane; ++u) {
+    const int v = v0 + u * kWave;
 #pragma unroll
-      for (int j = 0; j < KMAX; ++j)
-        if (row[j] >= 0 && v < nv) in[u][j] = y[(size_t)row[j] * nv + v];
+    for (int j = 0; j < KMAX; ++j) {
+      in[u][j] = u32x4{0, 0, 0, 0};
+      if (row[j] >= 0 && src[j] == j && v < nv)
+        in[u][j] = __builtin_nontemporal_load(y + (size_t)row[j] * nv + v);
     }
+  }
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int v = v0 + u * kWave + lane;
-      if (v >= nv) continue;
-      float acc[8];
+  for (int u = 0; u < kUnitsPerLane; ++u) {
+    const int v = v0 + u * kWave;
+    if (v >= nv) continue;
+    float acc[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
 #pragma unroll
-      for (int j = 0; j < KMAX; ++j) {
-        if (row[j] < 0) continue;  // uniform
+    for (int j = 0; j < KMAX; ++j) {
+      if (row[j] < 0) continue;  // uniform: position skipped (token not dispatched)
+      u32x4 x = in[u][j];
+      if (DEDUPE) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] = __builtin_fmaf(w[j], bf16_lo(in[u][j][i]), acc[2 * i]);
-          acc[2 * i + 1] = __builtin_fmaf(w[j], bf16_hi(in[u][j][i]), acc[2 * i + 1]);
-        }
+        for (int jj = 0; jj < j; ++jj)
+          if (src[j] == jj) x = in[u][jj];
       }
-      u32x4 o;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = pack_bf16_rne(acc[2 * i], acc[2 * i + 1]);
-      store_nt(out + v, o);
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = __builtin_fmaf(w[j], bf16_lo(x[i]), acc[2 * i]);
+        acc[2 * i + 1] = __builtin_fmaf(w[j], bf16_hi(x[i]), acc[2 * i + 1]);
+      }
     }
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16_rne(acc[2 * i], acc[2 * i + 1]);
+    store_nt(out + v, o);
   }
 }
 
 }  // namespace
 
-hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-  if (a.T == 0) return hipSuccess;
-  const int blocks = (a.T + 3) / 4;
-  if (a.k <= 8) combine_kernel<8, 2><<<blocks, 256, 0, s>>>(a);
-  else combine_kernel<kMaxTopk, 1><<<blocks, 256, 0, s>>>(a);
+hipError_t launch_combine(const CombineArgs& a0, hipStream_t s) {
+  if (a0.T == 0) return hipSuccess;
+  CombineArgs a = a0;
+  const int per = kWave * kUnitsPerLane;
+  a.slice_units = per;
+  a.slices = (a.H / 8 + per - 1) / per;
+  const int blocks = (int)(((int64_t)a.T * a.slices + 3) / 4);
+  if (a.k <= 8) {
+    if (a.distinct_rows) combine_kernel<8, false><<<blocks, 256, 0, s>>>(a);
+    else combine_kernel<8, true><<<blocks, 256, 0, s>>>(a);
+  } else {
+    combine_kernel<kMaxTopk, false><<<blocks, 256, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

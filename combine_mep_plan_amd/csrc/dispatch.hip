@@ -1,7 +1,6 @@
 // Dispatch: scatter each token's row (bf16 copy, or OCP E4M3 codes with one
 // fp32 scale per 128 columns) plus its k weights and k expert ids into the
-// receive buffer of every distinct destination rank, at the slot the plan
-// assigned.
+// receive buffer of every distinct destination rank, at the token's slot.
 //
 // Source: "MORI-EP User Guide", section 3 dispatch() (outputs: received rows,
 // weights, scales, indices); "Choosing an EP API and backend": the gfx950 FP8
@@ -9,18 +8,102 @@
 // columns, code = E4M3(x / scale), round to nearest even) is this library's
 // reading; the pages do not print the format.
 //
-// One wavefront per token.  The row is read from HBM once and held in
-// registers; each destination then receives 16-byte-per-lane stores (1 KiB
-// per wave instruction, fully coalesced).  Receive rows are written with
-// non-temporal stores: they are not read again by this launch.
-#include "dev.h"
-#include "mep_internal.h"
+// Layout of the work: a row is cut into 1 KiB-per-wave slices -- each lane owns
+// one 16-byte unit of input (bf16: 8 columns) or of output (FP8: 16 columns,
+// 8 lanes per 128-column scale block) -- and one wave handles one (token,
+// slice).  Many small waves keep enough writes in flight to approach the HBM
+// write rate; every receive-row store is a non-temporal 16-byte-per-lane
+// store (1 KiB per wave instruction).
+//
+// Where the destination slots come from:
+//   kRoute  : a prior plan's receive row of each (token, top-k position);
+//   kCounts : computed here from the count launch's per-chunk prefixes (the
+//             wave ballots its 64-token chunk's rank masks), which also writes
+//             the plan outputs -- a fused plan+dispatch;
+//   kInline : as kCounts, but the prefixes are recomputed from the ids of the
+//             earlier chunks, for small batches: plan+dispatch in one launch.
+#include "route.h"
 
 namespace mep {
 
 namespace {
 
-// Token row metadata: k weights and k expert ids, one lane per top-k entry.
+enum { kRoute = 0, kCounts = 1, kInline = 2 };
+
+// Where token t's rows go, as seen by one wave (fused modes).
+struct WaveRoute {
+  uint64_t tok_mask;  // ranks token t goes to (uniform)
+  uint64_t mask_l;    // rank mask of token (t's chunk)*64 + lane
+  int base;           // lane r: rows rank r received from tokens before t's chunk
+  int tl;             // t's lane in its chunk
+
+  // Receive slot of token t on rank r (r uniform, bit r set in tok_mask).
+  __device__ __forceinline__ int slot(int r) const {
+    const uint64_t b = ballot((mask_l >> r) & 1ull);
+    const uint64_t below = tl ? (b & (~0ull >> (64 - tl))) : 0ull;
+    return lane_value(base, r) + __popcll(below);
+  }
+};
+
+template <int MODE, int KMAX>
+__device__ __forceinline__ WaveRoute wave_route(const DispatchArgs& a, int t, int lane,
+                                                uint32_t& st) {
+  WaveRoute w;
+  w.tl = t & 63;
+  const int c = t >> 6;
+  const int tok = c * kChunk + lane;
+  w.base = 0;
+  if (MODE == kCounts) {
+    w.mask_l = tok < a.T ? a.mask[tok] : 0ull;
+    if (lane < a.R) {
+      int acc = a.chunk_cnt[(size_t)c * a.R + lane];
+      for (int b = 0; b < c / 16; ++b) acc += a.block_cnt[(size_t)b * a.R + lane];
+      w.base = acc;
+    }
+  } else {
+    int ids[KMAX];
+    for (int cc = 0; cc < c; ++cc) {
+      uint32_t ignore = 0;
+      const uint64_t m = load_token<KMAX>(a.idx, cc * kChunk + lane, a.k, a.E, a.rdiv, ids,
+                                          ignore);
+      w.base += ranks_popcount(m, a.R, lane);
+    }
+    w.mask_l = tok < a.T ? load_token<KMAX>(a.idx, tok, a.k, a.E, a.rdiv, ids, st) : 0ull;
+  }
+  w.tok_mask = lane_value64(w.mask_l, w.tl);
+  return w;
+}
+
+// Plan outputs for token t (fused modes; one wave per token does this):
+// receive row of each top-k position, first-occurrence bits, src_token_pos,
+// and -- from the last token's wave -- recv_counts.
+__device__ __forceinline__ void write_route(const DispatchArgs& a, const WaveRoute& w, int t,
+                                            int lane) {
+  const int e = lane < a.k ? a.idx[(size_t)t * a.k + lane] : 0;
+  if (w.tok_mask == 0) {
+    if (lane < a.k) a.rrow[(size_t)t * a.k + lane] = -1;
+    if (lane == 0) a.ufirst[t] = 0u;
+  } else {
+    const int rj = lane < a.k ? (int)a.rdiv((uint32_t)e) : -1;
+    int my = 0;
+    uint32_t first = 0;
+    for (uint64_t m = w.tok_mask; m; m &= m - 1) {
+      const int r = __builtin_ctzll(m);
+      const int s = w.slot(r);
+      const uint64_t b = ballot(rj == r);  // top-k positions naming rank r
+      first |= 1u << __builtin_ctzll(b);
+      if (rj == r) my = s;
+      if (lane == 0) a.spos[(size_t)r * a.cap + s] = a.spos_base + t;
+    }
+    if (lane < a.k) a.rrow[(size_t)t * a.k + lane] = rj * a.cap + my;
+    if (lane == 0) a.ufirst[t] = first;
+  }
+  if (t == a.T - 1) {
+    const int tot = w.base + ranks_popcount(w.mask_l, a.R, lane);
+    if (lane < a.R) a.recv_counts[lane] = tot;
+  }
+}
+
 __device__ __forceinline__ void store_meta(const DispatchArgs& a, int t, int row, int lane) {
   if (lane < a.k) {
     a.recv_w[(size_t)row * a.k + lane] = a.w[(size_t)t * a.k + lane];
@@ -28,124 +111,128 @@ __device__ __forceinline__ void store_meta(const DispatchArgs& a, int t, int row
   }
 }
 
-template <int UNROLL>
-__global__ __launch_bounds__(256) void dispatch_bf16_kernel(DispatchArgs a) {
-  const int lane = threadIdx.x & 63;
-  int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.T) return;
-  t = first_lane(t);
-  const uint32_t first = a.ufirst[t];
-  if (first == 0) return;  // token not dispatched (bad expert id)
-  const int nv = a.H / 8;  // 16-byte vectors per row
-  const u32x4* src = reinterpret_cast<const u32x4*>(a.x) + (size_t)t * nv;
-  const int32_t* rr = a.rrow + (size_t)t * a.k;
-  u32x4* dst_base = reinterpret_cast<u32x4*>(a.recv_x);
-  for (int v0 = 0; v0 < nv; v0 += kWave * UNROLL) {
-    u32x4 buf[UNROLL];
+// FP8: this lane's 16 columns (in0: 0..7, in1: 8..15) -> 16 codes; the block
+// scale is shared by the 8 lanes of a 128-column block.
+__device__ __forceinline__ u32x4 quant16(u32x4 in0, u32x4 in1, float& scale) {
+  float f[16];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int v = v0 + u * kWave + lane;
-      if (v < nv) buf[u] = src[v];
-    }
-    for (uint32_t m = first; m; m &= m - 1) {
-      const int row = rr[__builtin_ctz(m)];
-      u32x4* dst = dst_base + (size_t)row * nv;
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        const int v = v0 + u * kWave + lane;
-        if (v < nv) store_nt(dst + v, buf[u]);
-      }
-    }
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_lo(in0[i]);
+    f[2 * i + 1] = bf16_hi(in0[i]);
+    f[8 + 2 * i] = bf16_lo(in1[i]);
+    f[8 + 2 * i + 1] = bf16_hi(in1[i]);
   }
-  for (uint32_t m = first; m; m &= m - 1) store_meta(a, t, rr[__builtin_ctz(m)], lane);
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  amax = fmaxf(amax, __shfl_xor(amax, 4));
+  const float s = amax / 448.0f;
+  scale = s;
+  uint32_t w[4];
+  if (s == 0.0f) {  // all-zero block: signed zero codes
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = ((__float_as_uint(f[4 * i]) >> 31) << 7) |
+             ((__float_as_uint(f[4 * i + 1]) >> 31) << 15) |
+             ((__float_as_uint(f[4 * i + 2]) >> 31) << 23) |
+             ((__float_as_uint(f[4 * i + 3]) >> 31) << 31);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = pack_e4m3x4(f[4 * i] / s, f[4 * i + 1] / s, f[4 * i + 2] / s, f[4 * i + 3] / s);
+  }
+  return u32x4{w[0], w[1], w[2], w[3]};
 }
 
-// FP8: each lane owns 16 consecutive columns (32 input bytes -> 16 code bytes);
-// 8 neighbouring lanes cover one 128-column scale block.
-template <int UNROLL>
-__global__ __launch_bounds__(256) void dispatch_fp8_kernel(DispatchArgs a) {
+template <bool FP8, int MODE, int KMAX>
+__global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
   const int lane = threadIdx.x & 63;
-  int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int g = first_lane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  const int t = g / a.slices, sl = g - t * a.slices;
   if (t >= a.T) return;
-  t = first_lane(t);
-  const uint32_t first = a.ufirst[t];
-  if (first == 0) return;
-  const int nu = a.H / 16;   // 16-column units per row
-  const int nb = a.H / 128;  // scale blocks per row
+  if (MODE == kInline && g == 0 && lane == 0) *a.status_next = 0u;
+
+  // this wave's unit of the row: loads go out before the routing work
+  const int nu = FP8 ? a.H / 16 : a.H / 8;
+  const int v = sl * kWave + lane;
+  const bool on = v < nu;
   const u32x4* src = reinterpret_cast<const u32x4*>(a.x) + (size_t)t * (a.H / 8);
-  const int32_t* rr = a.rrow + (size_t)t * a.k;
-  u32x4* qbase = reinterpret_cast<u32x4*>(a.recv_x);
-  for (int v0 = 0; v0 < nu; v0 += kWave * UNROLL) {
-    u32x4 in0[UNROLL], in1[UNROLL];
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int v = v0 + u * kWave + lane;
-      if (v < nu) { in0[u] = src[2 * v]; in1[u] = src[2 * v + 1]; }
-      else { in0[u] = u32x4{0, 0, 0, 0}; in1[u] = u32x4{0, 0, 0, 0}; }
+  u32x4 in0 = u32x4{0, 0, 0, 0}, in1 = u32x4{0, 0, 0, 0};
+  if (on) {
+    if (FP8) { in0 = src[2 * v]; in1 = src[2 * v + 1]; }
+    else in0 = src[v];
+  }
+
+  uint32_t first = 0;
+  WaveRoute w{};
+  if (MODE == kRoute) {
+    first = a.ufirst[t];
+    if (first == 0) return;  // token not dispatched (bad expert id)
+  } else {
+    uint32_t st = 0;
+    w = wave_route<MODE, KMAX>(a, t, lane, st);
+    if (sl == 0) {
+      if (MODE == kInline) or_status(a.status, lane == w.tl ? st : 0u);
+      write_route(a, w, t, lane);
     }
-    u32x4 q[UNROLL];
-    float scale[UNROLL];
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      float f[16];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[2 * i] = bf16_lo(in0[u][i]);
-        f[2 * i + 1] = bf16_hi(in0[u][i]);
-        f[8 + 2 * i] = bf16_lo(in1[u][i]);
-        f[8 + 2 * i + 1] = bf16_hi(in1[u][i]);
-      }
-      float amax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
-      // lanes 8m..8m+7 share a block; units past the row end hold amax 0 and
-      // never leave their own 8-lane group (nu is a multiple of 8)
-      amax = fmaxf(amax, __shfl_xor(amax, 1));
-      amax = fmaxf(amax, __shfl_xor(amax, 2));
-      amax = fmaxf(amax, __shfl_xor(amax, 4));
-      const float s = amax / 448.0f;
-      scale[u] = s;
-      uint32_t w[4];
-      if (s == 0.0f) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          w[i] = ((__float_as_uint(f[4 * i]) >> 31) << 7) |
-                 ((__float_as_uint(f[4 * i + 1]) >> 31) << 15) |
-                 ((__float_as_uint(f[4 * i + 2]) >> 31) << 23) |
-                 ((__float_as_uint(f[4 * i + 3]) >> 31) << 31);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          w[i] = pack_e4m3x4(f[4 * i] / s, f[4 * i + 1] / s, f[4 * i + 2] / s, f[4 * i + 3] / s);
-      }
-      q[u] = u32x4{w[0], w[1], w[2], w[3]};
+    if (w.tok_mask == 0) return;
+  }
+
+  float scale = 0.0f;
+  const u32x4 q = FP8 ? quant16(in0, in1, scale) : in0;
+  const int nb = a.H / 128;
+  auto emit = [&](int row) {
+    if (on) {
+      store_nt(reinterpret_cast<u32x4*>(a.recv_x) + (size_t)row * nu + v, q);
+      if (FP8 && (v & 7) == 0) a.recv_scales[(size_t)row * nb + (v >> 3)] = scale;
     }
-    for (uint32_t m = first; m; m &= m - 1) {
-      const int row = rr[__builtin_ctz(m)];
-      u32x4* dq = qbase + (size_t)row * nu;
-      float* ds = a.recv_scales + (size_t)row * nb;
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        const int v = v0 + u * kWave + lane;
-        if (v < nu) {
-          store_nt(dq + v, q[u]);
-          if ((v & 7) == 0) ds[v >> 3] = scale[u];
-        }
-      }
+    if (sl == 0) store_meta(a, t, row, lane);
+  };
+  if (MODE == kRoute) {
+    const int32_t* rr = a.rrow + (size_t)t * a.k;
+    for (uint32_t m = first; m; m &= m - 1) emit(rr[__builtin_ctz(m)]);
+  } else {
+    for (uint64_t m = w.tok_mask; m; m &= m - 1) {
+      const int r = __builtin_ctzll(m);
+      emit(r * a.cap + w.slot(r));
     }
   }
-  for (uint32_t m = first; m; m &= m - 1) store_meta(a, t, rr[__builtin_ctz(m)], lane);
+}
+
+template <bool FP8, int MODE>
+hipError_t launch_mode(const DispatchArgs& a0, hipStream_t s) {
+  DispatchArgs a = a0;
+  const int units = FP8 ? a.H / 16 : a.H / 8;
+  a.slices = (units + kWave - 1) / kWave;
+  a.slice_units = kWave;
+  const int64_t waves = (int64_t)a.T * a.slices;
+  const int blocks = (int)((waves + 3) / 4);
+  if (a.k <= 8) dispatch_kernel<FP8, MODE, 8><<<blocks, 256, 0, s>>>(a);
+  else dispatch_kernel<FP8, MODE, kMaxTopk><<<blocks, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_dtype(const DispatchArgs& a, bool fp8, hipStream_t s) {
+  return fp8 ? launch_mode<true, MODE>(a, s) : launch_mode<false, MODE>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_dispatch(const DispatchArgs& a, bool fp8, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  const int blocks = (a.T + 3) / 4;
-  if (fp8) dispatch_fp8_kernel<7><<<blocks, 256, 0, s>>>(a);
-  else dispatch_bf16_kernel<14><<<blocks, 256, 0, s>>>(a);
-  return hipGetLastError();
+  return launch_dtype<kRoute>(a, fp8, s);
+}
+
+hipError_t launch_plan_dispatch(const PlanArgs& p, const DispatchArgs& a, bool fp8,
+                                hipStream_t s) {
+  if (a.T == 0) return launch_plan(p, s);
+  if (a.T <= kInlinePlanTokens) return launch_dtype<kInline>(a, fp8, s);
+  hipError_t e = launch_plan_counts(p, s);
+  if (e != hipSuccess) return e;
+  return launch_dtype<kCounts>(a, fp8, s);
 }
 
 }  // namespace mep

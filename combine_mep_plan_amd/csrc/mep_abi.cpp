@@ -14,6 +14,8 @@ struct mep_handle {
   mep::RankDiv rdiv;
   bool plan_valid;
   bool em_valid;
+  bool planned_since_reset;
+  uint32_t epoch;  // selects the status word; advanced by mep_reset
   int32_t plan_T;
 };
 
@@ -28,8 +30,9 @@ WsLayout ws_layout(const mep_config& c) {
   const size_t C = (cap + kChunk - 1) / kChunk;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
-  L.status = take(sizeof(uint32_t));
+  L.status = take(2 * sizeof(uint32_t));
   L.chunk_cnt = take(C * R * sizeof(int32_t));
+  L.block_cnt = take((C + 15) / 16 * R * sizeof(int32_t));
   L.mask = take(cap * sizeof(uint64_t));
   L.rrow = take(cap * k * sizeof(int32_t));
   L.ufirst = take(cap * sizeof(uint32_t));
@@ -82,6 +85,12 @@ static T* ws_ptr(mep_handle* h, size_t off) {
 
 static int hip_rc(hipError_t e) { return e == hipSuccess ? MEP_OK : MEP_ERR_HIP; }
 
+// The status word of a reset epoch.  A plan clears the word of the next epoch,
+// so that it is zero when mep_reset moves there.
+static uint32_t* status_word(mep_handle* h, uint32_t epoch) {
+  return ws_ptr<uint32_t>(h, h->lay.status) + (epoch & 1u);
+}
+
 extern "C" {
 
 const char* mep_error_string(int code) {
@@ -133,20 +142,17 @@ int mep_destroy(mep_handle* h) {
   return MEP_OK;
 }
 
-int mep_plan(mep_handle* h, const int32_t* indices, int32_t T, int32_t* recv_counts,
-             int32_t* src_token_pos, void* stream) {
-  if (!h || !recv_counts || !src_token_pos) return MEP_ERR_NULL;
-  if (T < 0 || T > h->cfg.max_num_inp_token_per_rank) return MEP_ERR_SHAPE;
-  if (T > 0 && !indices) return MEP_ERR_NULL;
-  if ((indices && !aligned16(indices)) || !aligned16(recv_counts) || !aligned16(src_token_pos))
-    return MEP_ERR_ALIGN;
+static mep::PlanArgs plan_args(mep_handle* h, const int32_t* indices, int32_t T,
+                               int32_t* recv_counts, int32_t* src_token_pos) {
   const mep_config& c = h->cfg;
   mep::PlanArgs a{};
   a.indices = indices;
   a.recv_counts = recv_counts;
   a.spos = src_token_pos;
-  a.status = ws_ptr<uint32_t>(h, h->lay.status);
+  a.status = status_word(h, h->epoch);
+  a.status_next = status_word(h, h->epoch + 1);
   a.chunk_cnt = ws_ptr<int32_t>(h, h->lay.chunk_cnt);
+  a.block_cnt = ws_ptr<int32_t>(h, h->lay.block_cnt);
   a.mask = ws_ptr<uint64_t>(h, h->lay.mask);
   a.rrow = ws_ptr<int32_t>(h, h->lay.rrow);
   a.ufirst = ws_ptr<uint32_t>(h, h->lay.ufirst);
@@ -157,23 +163,24 @@ int mep_plan(mep_handle* h, const int32_t* indices, int32_t T, int32_t* recv_cou
   a.cap = c.max_num_inp_token_per_rank;
   a.spos_base = c.rank * c.world_size * c.max_num_inp_token_per_rank;
   a.rdiv = h->rdiv;
-  h->plan_valid = false;
-  h->em_valid = false;
-  int rc = hip_rc(mep::launch_plan(a, (hipStream_t)stream));
-  if (rc != MEP_OK) return rc;
-  h->plan_valid = true;
-  h->plan_T = T;
+  return a;
+}
+
+static int check_plan_args(mep_handle* h, const int32_t* indices, int32_t T,
+                           const int32_t* recv_counts, const int32_t* src_token_pos) {
+  if (!h || !recv_counts || !src_token_pos) return MEP_ERR_NULL;
+  if (T < 0 || T > h->cfg.max_num_inp_token_per_rank) return MEP_ERR_SHAPE;
+  if (T > 0 && !indices) return MEP_ERR_NULL;
+  if ((indices && !aligned16(indices)) || !aligned16(recv_counts) || !aligned16(src_token_pos))
+    return MEP_ERR_ALIGN;
   return MEP_OK;
 }
 
-int mep_dispatch(mep_handle* h, const void* x, const float* weights, const int32_t* indices,
-                 void* recv_x, float* recv_scales, float* recv_weights, int32_t* recv_indices,
-                 void* stream) {
-  if (!h) return MEP_ERR_NULL;
-  if (!h->plan_valid) return MEP_ERR_STATE;
-  const mep_config& c = h->cfg;
-  const bool fp8 = c.quant == MEP_QUANT_FP8_E4M3_BLOCK128;
-  const int32_t T = h->plan_T;
+static int check_dispatch_args(mep_handle* h, int32_t T, const void* x, const float* weights,
+                               const int32_t* indices, const void* recv_x,
+                               const float* recv_scales, const float* recv_weights,
+                               const int32_t* recv_indices) {
+  const bool fp8 = h->cfg.quant == MEP_QUANT_FP8_E4M3_BLOCK128;
   if (!recv_x || !recv_weights || !recv_indices) return MEP_ERR_NULL;
   if (fp8 && !recv_scales) return MEP_ERR_NULL;
   if (T > 0 && (!x || !weights || !indices)) return MEP_ERR_NULL;
@@ -182,6 +189,14 @@ int mep_dispatch(mep_handle* h, const void* x, const float* weights, const int32
       (recv_scales && !aligned16(recv_scales)) || !aligned16(recv_weights) ||
       !aligned16(recv_indices))
     return MEP_ERR_ALIGN;
+  return MEP_OK;
+}
+
+static mep::DispatchArgs dispatch_args(mep_handle* h, int32_t T, const void* x,
+                                       const float* weights, const int32_t* indices,
+                                       void* recv_x, float* recv_scales, float* recv_weights,
+                                       int32_t* recv_indices) {
+  const mep_config& c = h->cfg;
   mep::DispatchArgs a{};
   a.x = x;
   a.w = weights;
@@ -192,10 +207,75 @@ int mep_dispatch(mep_handle* h, const void* x, const float* weights, const int32
   a.recv_scales = recv_scales;
   a.recv_w = recv_weights;
   a.recv_idx = recv_indices;
+  a.mask = ws_ptr<uint64_t>(h, h->lay.mask);
+  a.chunk_cnt = ws_ptr<int32_t>(h, h->lay.chunk_cnt);
+  a.block_cnt = ws_ptr<int32_t>(h, h->lay.block_cnt);
+  a.status = status_word(h, h->epoch);
+  a.status_next = status_word(h, h->epoch + 1);
   a.T = T;
   a.H = c.hidden_dim;
   a.k = c.num_experts_per_token;
-  return hip_rc(mep::launch_dispatch(a, fp8, (hipStream_t)stream));
+  a.R = c.world_size;
+  a.E = c.world_size * c.num_experts_per_rank;
+  a.cap = c.max_num_inp_token_per_rank;
+  a.spos_base = c.rank * c.world_size * c.max_num_inp_token_per_rank;
+  a.rdiv = h->rdiv;
+  return a;
+}
+
+int mep_plan(mep_handle* h, const int32_t* indices, int32_t T, int32_t* recv_counts,
+             int32_t* src_token_pos, void* stream) {
+  int rc = check_plan_args(h, indices, T, recv_counts, src_token_pos);
+  if (rc != MEP_OK) return rc;
+  const mep::PlanArgs a = plan_args(h, indices, T, recv_counts, src_token_pos);
+  h->plan_valid = false;
+  h->em_valid = false;
+  rc = hip_rc(mep::launch_plan(a, (hipStream_t)stream));
+  if (rc != MEP_OK) return rc;
+  h->plan_valid = true;
+  h->planned_since_reset = true;
+  h->plan_T = T;
+  return MEP_OK;
+}
+
+int mep_dispatch(mep_handle* h, const void* x, const float* weights, const int32_t* indices,
+                 void* recv_x, float* recv_scales, float* recv_weights, int32_t* recv_indices,
+                 void* stream) {
+  if (!h) return MEP_ERR_NULL;
+  if (!h->plan_valid) return MEP_ERR_STATE;
+  const int32_t T = h->plan_T;
+  int rc = check_dispatch_args(h, T, x, weights, indices, recv_x, recv_scales, recv_weights,
+                               recv_indices);
+  if (rc != MEP_OK) return rc;
+  const mep::DispatchArgs a = dispatch_args(h, T, x, weights, indices, recv_x, recv_scales,
+                                            recv_weights, recv_indices);
+  return hip_rc(mep::launch_dispatch(a, h->cfg.quant == MEP_QUANT_FP8_E4M3_BLOCK128,
+                                     (hipStream_t)stream));
+}
+
+int mep_plan_dispatch(mep_handle* h, const int32_t* indices, int32_t T, int32_t* recv_counts,
+                      int32_t* src_token_pos, const void* x, const float* weights,
+                      void* recv_x, float* recv_scales, float* recv_weights,
+                      int32_t* recv_indices, void* stream) {
+  int rc = check_plan_args(h, indices, T, recv_counts, src_token_pos);
+  if (rc != MEP_OK) return rc;
+  rc = check_dispatch_args(h, T, x, weights, indices, recv_x, recv_scales, recv_weights,
+                           recv_indices);
+  if (rc != MEP_OK) return rc;
+  const mep::PlanArgs p = plan_args(h, indices, T, recv_counts, src_token_pos);
+  mep::DispatchArgs a = dispatch_args(h, T, x, weights, indices, recv_x, recv_scales,
+                                      recv_weights, recv_indices);
+  a.recv_counts = recv_counts;
+  a.spos = src_token_pos;
+  h->plan_valid = false;
+  h->em_valid = false;
+  rc = hip_rc(mep::launch_plan_dispatch(p, a, h->cfg.quant == MEP_QUANT_FP8_E4M3_BLOCK128,
+                                        (hipStream_t)stream));
+  if (rc != MEP_OK) return rc;
+  h->plan_valid = true;
+  h->planned_since_reset = true;
+  h->plan_T = T;
+  return MEP_OK;
 }
 
 int mep_to_expert_major(mep_handle* h, const void* recv_x, const float* recv_scales,
@@ -233,7 +313,7 @@ int mep_to_expert_major(mep_handle* h, const void* recv_x, const float* recv_sca
   a.lmask = ws_ptr<uint64_t>(h, h->lay.em_lmask);
   a.ccnt = ws_ptr<int32_t>(h, h->lay.em_ccnt);
   a.cbase = ws_ptr<int32_t>(h, h->lay.em_cbase);
-  a.status = ws_ptr<uint32_t>(h, h->lay.status);
+  a.status = status_word(h, h->epoch);
   a.cap_em = cap_em;
   a.T = h->plan_T;
   a.H = c.hidden_dim;
@@ -267,6 +347,7 @@ int mep_combine(mep_handle* h, int32_t layout, const void* y, const float* weigh
   a.y = y;
   a.w = weights;
   a.rows = ws_ptr<int32_t>(h, layout == MEP_RANK_MAJOR ? h->lay.rrow : h->lay.em_row);
+  a.distinct_rows = layout == MEP_EXPERT_MAJOR ? 1 : 0;
   a.out = out;
   a.T = T;
   a.H = h->cfg.hidden_dim;
@@ -276,16 +357,18 @@ int mep_combine(mep_handle* h, int32_t layout, const void* y, const float* weigh
 
 int mep_reset(mep_handle* h, void* stream) {
   if (!h) return MEP_ERR_NULL;
-  int rc = hip_rc(mep::launch_reset(ws_ptr<uint32_t>(h, h->lay.status), (hipStream_t)stream));
+  (void)stream;  // nothing to launch: the last plan cleared the next status word
+  if (h->planned_since_reset) h->epoch++;
+  h->planned_since_reset = false;
   h->plan_valid = false;
   h->em_valid = false;
-  return rc;
+  return MEP_OK;
 }
 
 int mep_get_status(mep_handle* h, void* stream, int32_t* device_status) {
   if (!h || !device_status) return MEP_ERR_NULL;
   uint32_t v = 0;
-  hipError_t e = hipMemcpyAsync(&v, ws_ptr<uint32_t>(h, h->lay.status), sizeof(v),
+  hipError_t e = hipMemcpyAsync(&v, status_word(h, h->epoch), sizeof(v),
                                 hipMemcpyDeviceToHost, (hipStream_t)stream);
   if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
   if (e != hipSuccess) return MEP_ERR_HIP;

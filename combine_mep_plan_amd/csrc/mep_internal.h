@@ -26,8 +26,9 @@ struct RankDiv {
 
 // Byte offsets of the workspace sections (each 256-byte aligned).
 struct WsLayout {
-  size_t status;     // uint32: sticky MEP_DEV_* bits
-  size_t chunk_cnt;  // int32 [C][R]: rows each 64-token chunk sends to each rank
+  size_t status;     // uint32 [2]: sticky MEP_DEV_* bits, one word per reset epoch
+  size_t chunk_cnt;  // int32 [C][R]: rows earlier chunks of the same 16-chunk block send to each rank
+  size_t block_cnt;  // int32 [ceil(C/16)][R]: rows each 16-chunk block sends to each rank
   size_t mask;       // uint64 [cap]: destination-rank mask of each token (0 = dropped)
   size_t rrow;       // int32 [cap][k]: flat receive row r*cap+slot of (t, j), -1 if dropped
   size_t ufirst;     // uint32 [cap]: bit j set when top-k position j owns its rank's row
@@ -44,8 +45,10 @@ struct PlanArgs {
   const int32_t* indices;  // [T,k]
   int32_t* recv_counts;    // [R]
   int32_t* spos;           // [R,cap]
-  uint32_t* status;
+  uint32_t* status;       // this epoch's status word
+  uint32_t* status_next;  // the other epoch's word, cleared by the plan
   int32_t* chunk_cnt;
+  int32_t* block_cnt;
   uint64_t* mask;
   int32_t* rrow;
   uint32_t* ufirst;
@@ -57,14 +60,27 @@ struct DispatchArgs {
   const void* x;           // [T,H] bf16
   const float* w;          // [T,k]
   const int32_t* idx;      // [T,k]
-  const int32_t* rrow;
-  const uint32_t* ufirst;
+  int32_t* rrow;           // [T,k] receive row of (t, j): read after a plan, written when fused
+  uint32_t* ufirst;        // [T] first-occurrence bits: likewise
   void* recv_x;            // [R*cap, H] bf16 or e4m3
   float* recv_scales;      // [R*cap, H/128]
   float* recv_w;           // [R*cap, k]
   int32_t* recv_idx;       // [R*cap, k]
-  int32_t T, H, k;
+  // fused plan+dispatch only
+  const uint64_t* mask;    // per-token rank masks from the count launch
+  const int32_t* chunk_cnt;
+  const int32_t* block_cnt;
+  int32_t* recv_counts;    // [R]
+  int32_t* spos;           // [R,cap]
+  uint32_t* status;
+  uint32_t* status_next;
+  int32_t T, H, k, R, E, cap, spos_base;
+  RankDiv rdiv;
+  int32_t slices, slice_units;  // waves per token and 16-byte lane units per wave
 };
+
+// Batches up to this many tokens plan inside the dispatch launch itself.
+constexpr int kInlinePlanTokens = 256;
 
 struct CombineArgs {
   const void* y;           // bf16 rows
@@ -72,6 +88,8 @@ struct CombineArgs {
   const int32_t* rows;     // [T,k] row of (t, j) in y, -1 = skip
   void* out;               // [T,H] bf16
   int32_t T, H, k;
+  int32_t distinct_rows;   // 1: the k rows of a token are distinct (no dedupe needed)
+  int32_t slices, slice_units;  // waves per token and 16-byte lane units per wave
 };
 
 struct EmArgs {
@@ -97,10 +115,12 @@ struct EmArgs {
 
 // Launchers (return hipError_t of the launch).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_plan_counts(const PlanArgs& a, hipStream_t s);  // count launch only, T > 0
 hipError_t launch_dispatch(const DispatchArgs& a, bool fp8, hipStream_t s);
+hipError_t launch_plan_dispatch(const PlanArgs& p, const DispatchArgs& a, bool fp8,
+                                hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_to_expert_major(const EmArgs& a, hipStream_t s);
-hipError_t launch_reset(uint32_t* status, hipStream_t s);
 hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int64_t n, hipStream_t s);
 hipError_t launch_probe_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t s);
 hipError_t launch_probe_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);

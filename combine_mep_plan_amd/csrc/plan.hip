@@ -9,114 +9,201 @@
 // rows are in ascending token order (the only order that needs no atomics and
 // is reproducible run to run).
 //
-// Two launches over 64-token chunks (one wave per chunk):
-//   count: each wave builds its tokens' destination-rank masks and, with one
-//          ballot per rank, the chunk's per-rank row counts;
-//   slot:  each wave sums the counts of the chunks before it (exclusive
-//          prefix, from L2), then ranks its own tokens with ballot + mbcnt,
-//          writes src_token_pos, the flat receive row of every (t, j) and the
-//          first-occurrence bits.  The last chunk also writes recv_counts.
-#include "dev.h"
-#include "mep_internal.h"
+// Work unit: a chunk of 64 tokens = one wave, one token per lane.  For a
+// chunk, one ballot per rank gives the chunk's row count for that rank
+// (popcount) and each lane's offset among the chunk's tokens going there
+// (popcount of the ballot below the lane).  The ballots and the chunk's
+// per-rank base are put in LDS, so every lane finds the slot of each of its
+// top-k entries with one LDS read and a popcount -- no per-rank loop per lane.
+//
+// The per-rank base of a chunk is the exclusive prefix over earlier chunks,
+// built in two levels: inside a 16-chunk block through LDS, across blocks by
+// summing block totals.  Up to 1024 tokens one workgroup does everything in a
+// single launch; beyond that, a count launch writes the block-level prefixes
+// and a slot launch (one wave per chunk) finishes.
+#include "route.h"
 
 namespace mep {
 
-__global__ __launch_bounds__(256) void plan_count_kernel(PlanArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int C = (a.T + kChunk - 1) / kChunk;
-  if (c >= C) return;  // whole wave
-  const int t = c * kChunk + lane;
-  uint64_t mask = 0;
-  uint32_t st = 0;
-  if (t < a.T) {
-    const int32_t* ids = a.indices + (size_t)t * a.k;
-    bool bad = false, dup = false;
-    for (int j = 0; j < a.k; ++j) {
-      const int e = ids[j];
-      if (e < 0 || e >= a.E) {
-        bad = true;
-      } else {
-        mask |= 1ull << a.rdiv((uint32_t)e);
-        for (int jj = 0; jj < j; ++jj) dup |= (ids[jj] == e);
-      }
-    }
-    if (bad) { mask = 0; st |= MEP_DEV_BAD_INDEX; }
-    else if (dup) st |= MEP_DEV_DUP_EXPERT;
-    a.mask[t] = mask;
-  }
-  int mine = 0;
+namespace {
+
+constexpr int kBlockChunks = 16;  // chunks (waves) per count block
+
+// Slot phase for one chunk.  `base` in lane r is the number of rows rank r got
+// from all earlier tokens.  bal/bas are this wave's LDS scratch (64 entries).
+// Writes src_token_pos, the flat receive row of each (t, j) and the
+// first-occurrence bits.  Returns, in lane r, the rank-r count of the chunk.
+template <int KMAX>
+__device__ __forceinline__ int chunk_slots(const PlanArgs& a, int c, int lane, int base,
+                                           const int (&ids)[KMAX], uint64_t mask,
+                                           uint64_t* bal, int* bas) {
+  uint64_t mybal = 0;
   for (int r = 0; r < a.R; ++r) {
     const uint64_t b = ballot((mask >> r) & 1ull);
-    if (lane == r) mine = __popcll(b);
+    if (lane == r) mybal = b;
   }
-  if (lane < a.R) a.chunk_cnt[(size_t)c * a.R + lane] = mine;
-  const uint64_t any_bad = ballot(st & MEP_DEV_BAD_INDEX);
-  const uint64_t any_dup = ballot(st & MEP_DEV_DUP_EXPERT);
-  if (lane == 0 && (any_bad | any_dup)) {
-    atomicOr(a.status, (any_bad ? MEP_DEV_BAD_INDEX : 0u) | (any_dup ? MEP_DEV_DUP_EXPERT : 0u));
+  if (lane < a.R) { bal[lane] = mybal; bas[lane] = base; }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int t = c * kChunk + lane;
+  if (t < a.T) {
+    int32_t* rr = a.rrow + (size_t)t * a.k;
+    if (mask == 0) {
+      for (int j = 0; j < a.k; ++j) rr[j] = -1;
+      a.ufirst[t] = 0;
+    } else {
+      uint64_t seen = 0;
+      uint32_t first = 0;
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (j < a.k) {
+          const int r = (int)a.rdiv((uint32_t)ids[j]);
+          const int s = bas[r] + bits_below(bal[r]);
+          rr[j] = r * a.cap + s;
+          if (!((seen >> r) & 1ull)) {
+            first |= 1u << j;
+            a.spos[(size_t)r * a.cap + s] = a.spos_base + t;
+          }
+          seen |= 1ull << r;
+        }
+      }
+      a.ufirst[t] = first;
+    }
   }
+  return __popcll(mybal);
 }
 
-// LDS: per wave, the slot each lane's token got on each rank it goes to.
-__global__ __launch_bounds__(64) void plan_slot_kernel(PlanArgs a) {
-  __shared__ int32_t slot_of[kMaxRanks][kWave];
-  const int lane = threadIdx.x;
-  const int c = blockIdx.x;
-  const int C = (a.T + kChunk - 1) / kChunk;
-  // exclusive prefix over earlier chunks, lane r holding rank r
+// Whole plan in one workgroup of 16 waves (T <= 1024).
+template <int KMAX>
+__global__ __launch_bounds__(1024) void plan_single_kernel(PlanArgs a) {
+  __shared__ int cnt[kBlockChunks][kMaxRanks];
+  __shared__ uint64_t bal[kBlockChunks][kWave];
+  __shared__ int bas[kBlockChunks][kWave];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (threadIdx.x == 0) *a.status_next = 0u;
+  const int t = w * kChunk + lane;
+  int ids[KMAX];
+  uint32_t st = 0;
+  const uint64_t mask = t < a.T ? load_token<KMAX>(a.indices, t, a.k, a.E, a.rdiv, ids, st) : 0ull;
+  const int mine = ranks_popcount(mask, a.R, lane);
+  if (lane < a.R) cnt[w][lane] = mine;
+  or_status(a.status, st);
+  __syncthreads();
   int base = 0;
   if (lane < a.R) {
-    for (int cc = 0; cc < c; ++cc) base += a.chunk_cnt[(size_t)cc * a.R + lane];
-    if (c == C - 1) a.recv_counts[lane] = base + a.chunk_cnt[(size_t)c * a.R + lane];
-  }
-  const int t = c * kChunk + lane;
-  const bool valid = t < a.T;
-  const uint64_t mask = valid ? a.mask[t] : 0ull;
-  for (int r = 0; r < a.R; ++r) {
-    const uint64_t b = ballot((mask >> r) & 1ull);
-    if (b == 0) continue;  // uniform
-    const int s = lane_value(base, r) + bits_below(b);
-    if ((mask >> r) & 1ull) {
-      slot_of[r][lane] = s;
-      a.spos[(size_t)r * a.cap + s] = a.spos_base + t;
+    for (int ww = 0; ww < w; ++ww) base += cnt[ww][lane];
+    if (w == kBlockChunks - 1) {
+      a.recv_counts[lane] = base + mine;
     }
   }
-  if (!valid) return;  // no barrier below: each lane reads only its own column
-  int32_t* rr = a.rrow + (size_t)t * a.k;
-  if (mask == 0) {
-    for (int j = 0; j < a.k; ++j) rr[j] = -1;
-    a.ufirst[t] = 0;
-    return;
-  }
-  const int32_t* ids = a.indices + (size_t)t * a.k;
-  uint64_t seen = 0;
-  uint32_t first = 0;
-  for (int j = 0; j < a.k; ++j) {
-    const int r = (int)a.rdiv((uint32_t)ids[j]);
-    rr[j] = r * a.cap + slot_of[r][lane];
-    if (!((seen >> r) & 1ull)) first |= 1u << j;
-    seen |= 1ull << r;
-  }
-  a.ufirst[t] = first;
+  if (w * kChunk < a.T) chunk_slots<KMAX>(a, w, lane, base, ids, mask, bal[w], bas[w]);
 }
 
-__global__ void zero_i32_kernel(int32_t* p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0;
+// Count launch: per 16-chunk block, the exclusive prefix of every chunk inside
+// the block (chunk_cnt[c][r]) and the block totals (block_cnt[b][r]).
+template <int KMAX>
+__global__ __launch_bounds__(1024) void plan_count_kernel(PlanArgs a) {
+  __shared__ int cnt[kBlockChunks][kMaxRanks];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int b = blockIdx.x;
+  const int c = b * kBlockChunks + w;
+  const int C = (a.T + kChunk - 1) / kChunk;
+  if (b == 0 && threadIdx.x == 0) *a.status_next = 0u;
+  const int t = c * kChunk + lane;
+  int ids[KMAX];
+  uint32_t st = 0;
+  const uint64_t mask = t < a.T ? load_token<KMAX>(a.indices, t, a.k, a.E, a.rdiv, ids, st) : 0ull;
+  if (t < a.T) a.mask[t] = mask;
+  const int mine = ranks_popcount(mask, a.R, lane);
+  if (lane < a.R) cnt[w][lane] = mine;
+  or_status(a.status, st);
+  __syncthreads();
+  if (lane < a.R) {
+    int pre = 0;
+    for (int ww = 0; ww < w; ++ww) pre += cnt[ww][lane];
+    if (c < C) a.chunk_cnt[(size_t)c * a.R + lane] = pre;
+    if (w == kBlockChunks - 1) a.block_cnt[(size_t)b * a.R + lane] = pre + mine;
+  }
+}
+
+// Slot launch: one wave per chunk.
+template <int KMAX>
+__global__ __launch_bounds__(256) void plan_slot_kernel(PlanArgs a) {
+  __shared__ uint64_t bal[4][kWave];
+  __shared__ int bas[4][kWave];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = blockIdx.x * 4 + w;
+  const int C = (a.T + kChunk - 1) / kChunk;
+  if (c >= C) return;  // whole wave; no block barrier below
+  const int b = c / kBlockChunks;
+  int base = 0;
+  if (lane < a.R) {
+    base = a.chunk_cnt[(size_t)c * a.R + lane];
+    int acc[4] = {0, 0, 0, 0};
+    int bb = 0;
+    for (; bb + 4 <= b; bb += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] += a.block_cnt[(size_t)(bb + u) * a.R + lane];
+    }
+    for (; bb < b; ++bb) acc[0] += a.block_cnt[(size_t)bb * a.R + lane];
+    base += acc[0] + acc[1] + acc[2] + acc[3];
+  }
+  const int t = c * kChunk + lane;
+  int ids[KMAX];
+  uint64_t mask = 0;
+  if (t < a.T) {
+    const int32_t* p = a.indices + (size_t)t * a.k;
+    if (KMAX == 8 && a.k == 8) {
+      const int4 v0 = reinterpret_cast<const int4*>(p)[0];
+      const int4 v1 = reinterpret_cast<const int4*>(p)[1];
+      ids[0] = v0.x; ids[1] = v0.y; ids[2] = v0.z; ids[3] = v0.w;
+      ids[4] = v1.x; ids[5] = v1.y; ids[6] = v1.z; ids[7] = v1.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) ids[j] = j < a.k ? p[j] : 0;
+    }
+    mask = a.mask[t];
+  }
+  const int mine = chunk_slots<KMAX>(a, c, lane, base, ids, mask, bal[w], bas[w]);
+  if (c == C - 1 && lane < a.R) a.recv_counts[lane] = base + mine;
+}
+
+__global__ void zero_counts_kernel(PlanArgs a) {
+  const int i = threadIdx.x;
+  if (i == 0) *a.status_next = 0u;
+  if (i < a.R) a.recv_counts[i] = 0;
+}
+
+template <int KMAX>
+hipError_t launch_plan_k(const PlanArgs& a, hipStream_t s) {
+  const int C = (a.T + kChunk - 1) / kChunk;
+  if (C <= kBlockChunks) {
+    plan_single_kernel<KMAX><<<1, 1024, 0, s>>>(a);
+    return hipGetLastError();
+  }
+  hipError_t e = launch_plan_counts(a, s);
+  if (e != hipSuccess) return e;
+  plan_slot_kernel<KMAX><<<(C + 3) / 4, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_plan_counts(const PlanArgs& a, hipStream_t s) {
+  const int C = (a.T + kChunk - 1) / kChunk;
+  const int B = (C + kBlockChunks - 1) / kBlockChunks;
+  if (a.k <= 8) plan_count_kernel<8><<<B, 1024, 0, s>>>(a);
+  else plan_count_kernel<kMaxTopk><<<B, 1024, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
   if (a.T == 0) {
-    zero_i32_kernel<<<1, 64, 0, s>>>(a.recv_counts, a.R);
+    zero_counts_kernel<<<1, 64, 0, s>>>(a);
     return hipGetLastError();
   }
-  const int C = (a.T + kChunk - 1) / kChunk;
-  plan_count_kernel<<<(C + 3) / 4, 256, 0, s>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  plan_slot_kernel<<<C, 64, 0, s>>>(a);
-  return hipGetLastError();
+  return a.k <= 8 ? launch_plan_k<8>(a, s) : launch_plan_k<kMaxTopk>(a, s);
 }
 
 }  // namespace mep

@@ -1,19 +1,11 @@
-// Small launches: reset ("MORI-EP User Guide", section 3 reset()), a device
-// copy for route inspection, and probes that run the kernels' own device
-// conversions over caller arrays.
-//
-// Clearing is done with a fill kernel rather than a runtime memset so that a
-// caller may capture these calls in a graph.
+// Small launches: a device copy for route inspection, and probes that run the
+// kernels' own device conversions over caller arrays.
 #include "dev.h"
 #include "mep_internal.h"
 
 namespace mep {
 
 namespace {
-
-__global__ void reset_kernel(uint32_t* status) {
-  if (threadIdx.x == 0) *status = 0u;
-}
 
 __global__ void copy_i32_kernel(const int32_t* src, int32_t* dst, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
@@ -43,11 +35,6 @@ __global__ void probe_bf16_kernel(const float* in, uint16_t* out, int64_t n) {
 }
 
 }  // namespace
-
-hipError_t launch_reset(uint32_t* status, hipStream_t s) {
-  reset_kernel<<<1, 64, 0, s>>>(status);
-  return hipGetLastError();
-}
 
 hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int64_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;

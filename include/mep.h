@@ -87,8 +87,10 @@ const char *mep_error_string(int code);
 size_t mep_workspace_bytes(const mep_config *cfg);
 
 /* Check the config and bind it to a caller-owned device workspace of at least
- * mep_workspace_bytes(cfg) bytes.  Host-only: launches nothing, makes no HIP
- * call.  *out receives a host-heap handle freed by mep_destroy. */
+ * mep_workspace_bytes(cfg) bytes, which must be zero-filled before its first
+ * use (it holds the status words).  Host-only: launches nothing, makes no HIP
+ * call.  *out receives a host-heap handle freed by mep_destroy.  One
+ * workspace serves one handle at a time. */
 int mep_create(const mep_config *cfg, void *workspace, size_t workspace_bytes,
                mep_handle **out);
 int mep_destroy(mep_handle *h);
@@ -130,6 +132,18 @@ int mep_plan(mep_handle *h, const int32_t *indices, int32_t T, int32_t *recv_cou
 int mep_dispatch(mep_handle *h, const void *x, const float *weights, const int32_t *indices,
                  void *recv_x, float *recv_scales, float *recv_weights,
                  int32_t *recv_indices, void *stream);
+
+/*
+ * Fused routing plan + dispatch: the same outputs as mep_plan followed by
+ * mep_dispatch (recv_counts, src_token_pos, the receive rows, scales, weights
+ * and ids, and a valid plan in the handle), in fewer launches -- one launch up
+ * to 256 tokens, else two.  The pages pair the two steps the same way:
+ * dispatch() itself returns recv_num_token ("MORI-EP User Guide" section 3).
+ */
+int mep_plan_dispatch(mep_handle *h, const int32_t *indices, int32_t T, int32_t *recv_counts,
+                      int32_t *src_token_pos, const void *x, const float *weights,
+                      void *recv_x, float *recv_scales, float *recv_weights,
+                      int32_t *recv_indices, void *stream);
 
 /*
  * Standard-MoE layout ("MORI-EP User Guide" section 4,
@@ -174,10 +188,11 @@ int mep_combine(mep_handle *h, int32_t layout, const void *y, const float *weigh
                 void *stream);
 
 /*
- * Reset between iterations ("MORI-EP User Guide" section 3 reset()): clears
- * the device status word on `stream` and invalidates the plan (and the
- * expert-major maps) on the host.  Caller buffers are not touched: the
- * library writes a caller buffer only during the call that names it.
+ * Reset between iterations ("MORI-EP User Guide" section 3 reset()):
+ * invalidates the plan (and the expert-major maps) and starts a new status
+ * epoch, whose status word the last plan already cleared on the device, so no
+ * kernel is launched and `stream` is unused.  Caller buffers are not touched:
+ * the library writes a caller buffer only during the call that names it.
  */
 int mep_reset(mep_handle *h, void *stream);
 

@@ -67,16 +67,21 @@ class GpuRun:
     route: torch.Tensor
 
 
-def gpu_plan_dispatch(wl: Workload, inp: dict, src_rank: int = 0) -> GpuRun:
+def gpu_plan_dispatch(wl: Workload, inp: dict, src_rank: int = 0, fused: bool = False) -> GpuRun:
+    """Plan + dispatch through the C ABI: mep_plan then mep_dispatch, or the
+    fused mep_plan_dispatch."""
     T = inp["indices"].shape[0]
     m = M.Mep(wl.hidden, wl.experts_per_rank, wl.topk, wl.cap, wl.ranks, rank=src_rank,
               fp8=wl.quant == "fp8")
     x, w, idx = dev(inp["x"]), dev(inp["weights"]), dev(inp["indices"])
     counts = torch.full((wl.ranks,), SENT32, dtype=torch.int32, device="cuda")
     spos = torch.full((wl.ranks, wl.cap), SENT32, dtype=torch.int32, device="cuda")
-    M.mep_plan(m.h, idx, T, counts, spos)
     recv_x, recv_s, recv_w, recv_i = alloc_recv(wl)
-    M.mep_dispatch(m.h, x, w, idx, recv_x, recv_s, recv_w, recv_i)
+    if fused:
+        M.mep_plan_dispatch(m.h, idx, T, counts, spos, x, w, recv_x, recv_s, recv_w, recv_i)
+    else:
+        M.mep_plan(m.h, idx, T, counts, spos)
+        M.mep_dispatch(m.h, x, w, idx, recv_x, recv_s, recv_w, recv_i)
     route = torch.full((max(T, 1), wl.topk), SENT32, dtype=torch.int32, device="cuda")
     M.mep_get_route(m.h, route)
     torch.cuda.synchronize()
@@ -156,11 +161,11 @@ def check_combine(out_gpu_bits: np.ndarray, out_ref_bits: np.ndarray) -> dict:
             if diff.size else 1.0}
 
 
-def run_full(wl: Workload, seed: int, src_rank: int = 0) -> dict:
+def run_full(wl: Workload, seed: int, src_rank: int = 0, fused: bool = False) -> dict:
     """Whole path on the GPU and in the oracle; every check; returns stats."""
     inp = make_inputs(wl, seed)
     T = wl.tokens
-    g = gpu_plan_dispatch(wl, inp, src_rank)
+    g = gpu_plan_dispatch(wl, inp, src_rank, fused)
     pl, d = oracle_plan_dispatch(wl, inp, src_rank)
     check_plan_dispatch(wl, inp, g, pl, d)
     stats = {}

@@ -108,19 +108,26 @@ SMALL = [
 ]
 
 
+MODES = [False, True]  # mep_plan + mep_dispatch, or the fused mep_plan_dispatch
+
+
+@pytest.mark.parametrize("fused", MODES, ids=["separate", "fused"])
 @pytest.mark.parametrize("label,wl,seeds", SMALL, ids=[s[0] for s in SMALL])
-def test_parity_small(label, wl, seeds):
+def test_parity_small(label, wl, seeds, fused):
     for seed in seeds:
-        _say(f"[parity-small] {label} seed={seed} T={wl.tokens} H={wl.hidden} R={wl.ranks}")
-        st = run_full(wl, seed, src_rank=seed % wl.ranks)
+        _say(f"[parity-small] {label} fused={fused} seed={seed} T={wl.tokens} H={wl.hidden} "
+             f"R={wl.ranks}")
+        st = run_full(wl, seed, src_rank=seed % wl.ranks, fused=fused)
         _say(f"    U={st['U']} max_ulp={st['max_ulp']} exact={st['exact_frac']:.6f}")
 
 
+@pytest.mark.parametrize("fused", MODES, ids=["separate", "fused"])
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "skew", "stdmoe"])
-def test_parity_full_size(name):
+def test_parity_full_size(name, fused):
     wl = WORKLOADS[name]
-    _say(f"[parity-full] {name} T={wl.tokens} H={wl.hidden} R={wl.ranks} k={wl.topk}")
-    st = run_full(wl, 0)
+    _say(f"[parity-full] {name} fused={fused} T={wl.tokens} H={wl.hidden} R={wl.ranks} "
+         f"k={wl.topk}")
+    st = run_full(wl, 0, fused=fused)
     _say(f"    U={st['U']} max_ulp={st['max_ulp']} exact={st['exact_frac']:.6f}")
 
 
@@ -161,15 +168,17 @@ def test_full_capacity_and_single_rank_hotspot():
     assert host(g.counts)[0] == 256
 
 
-def test_bad_and_duplicate_expert_ids():
-    wl = _variant("tiny", tokens=16)
+@pytest.mark.parametrize("T", [16, 700])
+@pytest.mark.parametrize("fused", MODES, ids=["separate", "fused"])
+def test_bad_and_duplicate_expert_ids(fused, T):
+    wl = _variant("tiny", tokens=T, cap=1024)
     inp = make_inputs(wl, 5)
     idx = inp["indices"].copy()
     idx[3] = [1, 99]      # out of range -> token 3 not dispatched
     idx[7] = [-4, 2]      # negative -> token 7 not dispatched
     idx[9] = [5, 5]       # repeated expert -> still routed, status bit
     inp["indices"] = idx
-    g = gpu_plan_dispatch(wl, inp)
+    g = gpu_plan_dispatch(wl, inp, fused=fused)
     pl, d = oracle_plan_dispatch(wl, inp)
     assert pl["status"] == M.MEP_DEV_BAD_INDEX | M.MEP_DEV_DUP_EXPERT
     check_plan_dispatch(wl, inp, g, pl, d)
@@ -256,3 +265,37 @@ def test_expert_major_overflow_sets_status():
     assert em["status"] == O.ST_EM_OVERFLOW
     assert np.array_equal(host(em_c), em["em_counts"])
     assert np.array_equal(host(em_p), np.where(em["em_src_pos"] >= 0, em["em_src_pos"], SENT32))
+
+
+@pytest.mark.parametrize("fused", MODES, ids=["separate", "fused"])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025, 2049, 3000])
+def test_plan_block_boundaries(T, fused):
+    # mep_plan: one workgroup up to 1024 tokens, else count + slot launches split
+    # at 16-chunk blocks; fused: one launch up to 256 tokens, else count +
+    # dispatch launches
+    wl = _variant("skew", tokens=T, cap=3072, hidden=256)
+    inp = make_inputs(wl, T)
+    g = gpu_plan_dispatch(wl, inp, src_rank=3, fused=fused)
+    pl, d = oracle_plan_dispatch(wl, inp, src_rank=3)
+    check_plan_dispatch(wl, inp, g, pl, d)
+
+
+def test_status_is_sticky_until_reset():
+    wl = _variant("tiny", tokens=8)
+    inp = make_inputs(wl, 0)
+    bad = dict(inp, indices=inp["indices"].copy())
+    bad["indices"][2] = [0, 50]
+    g = gpu_plan_dispatch(wl, bad)
+    assert M.mep_get_status(g.m.h) == M.MEP_DEV_BAD_INDEX
+    # a second plan with clean ids in the same epoch keeps the bit
+    M.mep_plan(g.m.h, g.idx.copy_(dev(inp["indices"])), wl.tokens, g.counts, g.spos)
+    assert M.mep_get_status(g.m.h) == M.MEP_DEV_BAD_INDEX
+    M.mep_reset(g.m.h)
+    assert M.mep_get_status(g.m.h) == 0
+    M.mep_reset(g.m.h)  # reset without a plan in between
+    assert M.mep_get_status(g.m.h) == 0
+    M.mep_plan(g.m.h, dev(bad["indices"]), wl.tokens, g.counts, g.spos)
+    assert M.mep_get_status(g.m.h) == M.MEP_DEV_BAD_INDEX
+    M.mep_reset(g.m.h)
+    M.mep_plan(g.m.h, g.idx, wl.tokens, g.counts, g.spos)
+    assert M.mep_get_status(g.m.h) == 0
