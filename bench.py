@@ -1,19 +1,19 @@
 """Benchmark of the MoE dispatch/combine hot path on one MI355X.
 
-One step = the whole path on one batch: routing plan and FP8 dispatch
-(OCP E4M3, one fp32 scale per 128 columns) through the fused
-mep_plan_dispatch, bf16 combine, then reset, for
-4096 tokens x 7168 hidden, top-8 of 256 experts on 8 virtual ranks -- the
-shape of the MORI README bandwidth table ("4096 tokens, 7168 hidden, top-8,
-FP8 dispatch + BF16 combine").  Inputs are synthetic and already resident in
-HBM; the expert outputs combine reads are produced once, before timing, by
-the dequantise-times-0.5 stand-in.  Several buffer sets rotate so that no step
-finds its data in the 256 MB Infinity Cache.
+Headline step (`value`): the whole path on one batch of the prefill workload
+-- routing plan + FP8 dispatch through the fused mep_plan_dispatch (OCP E4M3,
+one fp32 scale per 128 columns), bf16 combine, reset -- for 4096 tokens x
+7168 hidden, top-8 of 256 experts on 8 virtual ranks: the shape of the MORI
+README bandwidth table ("4096 tokens, 7168 hidden, top-8, FP8 dispatch + BF16
+combine").  value = the step's algorithmic HBM bytes / step time.
 
-value = algorithmic HBM bytes of the step / step time (GB/s).  The JSON line
-also carries the decode latency (128 tokens, bf16 both ways), the roofline of
-the dominant kernel (achieved bytes per launch / its HIP-event duration on
-the library's stream) and the CPU oracle's rate on a bounded sample.
+Also measured, each on its own buffers: decode latency (128 tokens, bf16 both
+ways), the skewed-routing workload (Zipf 1.2, 16 ranks) and the standard-MoE
+workload (FP8 dispatch, expert-major conversion, combine from it).  Inputs are
+synthetic and resident in HBM; expert outputs are produced once, before
+timing, by the stand-in expert.  Buffer sets rotate so no step finds its data
+in the 256 MB Infinity Cache.  Kernel durations come from back-to-back loops
+of one call each between two HIP events on the library's stream.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -55,6 +55,16 @@ def combine_bytes(T, H, k, U):
     return U * H * 2 + T * k * 8 + T * H * 2
 
 
+def to_expert_major_bytes(T, H, k, U, fp8):
+    nb = H // 128 if fp8 else 0
+    b = 1 if fp8 else 2
+    return U * (H * b + nb * 4 + k * 4) + T * k * (H * b + nb * 4 + 4)
+
+
+def combine_em_bytes(T, H, k):
+    return T * k * H * 2 + T * k * 8 + T * H * 2
+
+
 def src_digest(*names):
     h = hashlib.sha256()
     for n in names:
@@ -63,10 +73,10 @@ def src_digest(*names):
     return h.hexdigest()[:16]
 
 
-def profile_traffic(kernel_file, digest):
+def profile_traffic(summary_file, digest):
     """HBM bytes per launch measured by rocprofv3 counters for the current kernel
     source, or None if no summary matches this source."""
-    p = os.path.join(ROOT, "profiles", kernel_file)
+    p = os.path.join(ROOT, "profiles", summary_file)
     if not os.path.exists(p):
         return None
     vals = {}
@@ -83,41 +93,6 @@ def profile_traffic(kernel_file, digest):
         return None
 
 
-# --------------------------------------------------------------------------
-
-def setup_prefill(M, torch, wl, inp, nsets):
-    """Device buffers for `nsets` independent copies of the workload."""
-    T, H, R, cap, k = wl.tokens, wl.hidden, wl.ranks, wl.cap, wl.topk
-    m = M.Mep(H, wl.experts_per_rank, k, cap, R, fp8=True)
-    sets = []
-    for _ in range(nsets):
-        s = {
-            "x": torch.from_numpy(inp["x"].view(np.int16)).cuda(),
-            "w": torch.from_numpy(inp["weights"]).cuda(),
-            "idx": torch.from_numpy(inp["indices"]).cuda(),
-            "counts": torch.zeros(R, dtype=torch.int32, device="cuda"),
-            "spos": torch.zeros((R, cap), dtype=torch.int32, device="cuda"),
-            "rx": torch.zeros((R, cap, H), dtype=torch.uint8, device="cuda"),
-            "rs": torch.zeros((R, cap, H // 128), dtype=torch.float32, device="cuda"),
-            "rw": torch.zeros((R, cap, k), dtype=torch.float32, device="cuda"),
-            "ri": torch.zeros((R, cap, k), dtype=torch.int32, device="cuda"),
-            "out": torch.empty((T, H), dtype=torch.int16, device="cuda"),
-        }
-        # expert outputs (harness, untimed): bf16(decode(q) * scale * 0.5) of this
-        # set's own dispatch
-        M.mep_plan(m.h, s["idx"], T, s["counts"], s["spos"])
-        M.mep_dispatch(m.h, s["x"], s["w"], s["idx"], s["rx"], s["rs"], s["rw"], s["ri"])
-        q = s["rx"].view(torch.float8_e4m3fn).float()
-        y = (q * s["rs"].repeat_interleave(128, dim=-1)) * 0.5
-        s["y"] = y.to(torch.bfloat16).view(torch.int16)
-        del q, y
-        M.mep_reset(m.h)
-        sets.append(s)
-    torch.cuda.synchronize()
-    U = int(sets[0]["counts"].sum().item())
-    return m, sets, U
-
-
 def _loop_ms(torch, stream, fn, n):
     """Average ms per call of fn(i) over n back-to-back calls on `stream`,
     timed by two HIP events (none inside the loop)."""
@@ -131,112 +106,166 @@ def _loop_ms(torch, stream, fn, n):
     return a.elapsed_time(b) / n
 
 
-def time_prefill(M, torch, m, sets, wl, steps, warmup):
-    """Headline loop: whole steps back to back.  Then one loop per kernel
-    (same rotation of buffer sets) for its average launch duration.  Every set
-    has the same routing, so the plan in the handle serves any set."""
-    T = wl.tokens
-    stream = torch.cuda.current_stream()
-    n = len(sets)
+# --------------------------------------------------------------------------
+# one workload: buffers, stand-in expert outputs, timed loops
+# --------------------------------------------------------------------------
 
-    def plan(i):
-        s = sets[i % n]
-        M.mep_plan(m.h, s["idx"], T, s["counts"], s["spos"], stream)
+class Runner:
+    def __init__(self, M, torch, wl, inp, nsets):
+        self.M, self.torch, self.wl = M, torch, wl
+        T, H, R, cap, k = wl.tokens, wl.hidden, wl.ranks, wl.cap, wl.topk
+        self.fp8 = wl.quant == "fp8"
+        self.em = wl.layout == "expert_major"
+        self.m = M.Mep(H, wl.experts_per_rank, k, cap, R, fp8=self.fp8)
+        self.stream = torch.cuda.current_stream()
+        dev = lambda a: torch.from_numpy(a).cuda()  # noqa: E731
+        self.sets = []
+        for _ in range(nsets):
+            s = {
+                "x": dev(inp["x"].view(np.int16)), "w": dev(inp["weights"]),
+                "idx": dev(inp["indices"]),
+                "counts": torch.zeros(R, dtype=torch.int32, device="cuda"),
+                "spos": torch.zeros((R, cap), dtype=torch.int32, device="cuda"),
+                "rx": torch.zeros((R, cap, H), dtype=torch.uint8 if self.fp8 else torch.int16,
+                                  device="cuda"),
+                "rs": (torch.zeros((R, cap, H // 128), dtype=torch.float32, device="cuda")
+                       if self.fp8 else None),
+                "rw": torch.zeros((R, cap, k), dtype=torch.float32, device="cuda"),
+                "ri": torch.zeros((R, cap, k), dtype=torch.int32, device="cuda"),
+                "out": torch.empty((T, H), dtype=torch.int16, device="cuda"),
+            }
+            if self.em:
+                ce = wl.cap_em
+                s["emx"] = torch.zeros((ce, H), dtype=torch.uint8 if self.fp8 else torch.int16,
+                                       device="cuda")
+                s["ems"] = (torch.zeros((ce, H // 128), dtype=torch.float32, device="cuda")
+                            if self.fp8 else None)
+                s["emc"] = torch.zeros(wl.experts, dtype=torch.int32, device="cuda")
+                s["emo"] = torch.zeros(wl.experts + 1, dtype=torch.int32, device="cuda")
+                s["emp"] = torch.zeros(ce, dtype=torch.int32, device="cuda")
+            self.plan_dispatch(s)
+            if self.em:
+                self.to_em(s)
+                s["y"] = self.stand_in(s["emx"], s["ems"])
+            else:
+                s["y"] = self.stand_in(s["rx"], s["rs"])
+            M.mep_reset(self.m.h, self.stream)
+            self.sets.append(s)
+        torch.cuda.synchronize()
+        self.U = int(self.sets[0]["counts"].sum().item())
 
-    def dispatch(i):
-        s = sets[i % n]
-        M.mep_dispatch(m.h, s["x"], s["w"], s["idx"], s["rx"], s["rs"], s["rw"], s["ri"], stream)
+    def stand_in(self, x, scales):
+        # expert outputs (harness, untimed): identity for bf16 payloads,
+        # bf16((decode(q) * scale) * mult) for E4M3 payloads
+        if scales is None:
+            return x
+        mult = 0.5 if self.wl.expert == "dequant_half" else 1.0
+        q = x.view(self.torch.float8_e4m3fn).float()
+        y = (q * scales.repeat_interleave(128, dim=-1)) * mult
+        return y.to(self.torch.bfloat16).view(self.torch.int16)
 
-    def combine(i):
-        s = sets[i % n]
-        M.mep_combine(m.h, M.MEP_RANK_MAJOR, s["y"], s["w"], s["out"], stream)
+    def plan_dispatch(self, s):
+        self.M.mep_plan_dispatch(self.m.h, s["idx"], self.wl.tokens, s["counts"], s["spos"],
+                                 s["x"], s["w"], s["rx"], s["rs"], s["rw"], s["ri"], self.stream)
 
-    def plan_dispatch(i):
-        s = sets[i % n]
-        M.mep_plan_dispatch(m.h, s["idx"], T, s["counts"], s["spos"], s["x"], s["w"], s["rx"],
-                            s["rs"], s["rw"], s["ri"], stream)
+    def plan(self, s):
+        self.M.mep_plan(self.m.h, s["idx"], self.wl.tokens, s["counts"], s["spos"], self.stream)
 
-    def step(i):
-        plan_dispatch(i)
-        combine(i)
-        M.mep_reset(m.h, stream)
+    def dispatch(self, s):
+        self.M.mep_dispatch(self.m.h, s["x"], s["w"], s["idx"], s["rx"], s["rs"], s["rw"],
+                            s["ri"], self.stream)
 
-    for i in range(warmup):
-        step(i)
-    step_ms = _loop_ms(torch, stream, step, steps)
-    assert M.mep_get_status(m.h, stream) == 0
-    times = {
-        "plan_dispatch": _loop_ms(torch, stream, plan_dispatch, steps),
-        "combine": _loop_ms(torch, stream, combine, steps),
-        "plan": _loop_ms(torch, stream, plan, steps),
-        "dispatch": _loop_ms(torch, stream, dispatch, steps),
-    }
-    M.mep_reset(m.h, stream)
-    return step_ms, times
+    def to_em(self, s):
+        self.M.mep_to_expert_major(self.m.h, s["rx"], s["rs"], s["ri"], s["counts"], s["spos"],
+                                   s["emx"], s["ems"], s["emc"], s["emo"], s["emp"],
+                                   self.wl.cap_em, self.stream)
+
+    def combine(self, s):
+        layout = self.M.MEP_EXPERT_MAJOR if self.em else self.M.MEP_RANK_MAJOR
+        self.M.mep_combine(self.m.h, layout, s["y"], s["w"], s["out"], self.stream)
+
+    def step(self, s):
+        self.plan_dispatch(s)
+        if self.em:
+            self.to_em(s)
+        self.combine(s)
+        self.M.mep_reset(self.m.h, self.stream)
+
+    def loop(self, fn, n):
+        return _loop_ms(self.torch, self.stream, lambda i: fn(self.sets[i % len(self.sets)]), n)
+
+    def bytes(self):
+        wl, U = self.wl, self.U
+        T, H, k, R = wl.tokens, wl.hidden, wl.topk, wl.ranks
+        b = {"plan": plan_bytes(T, k, R, U), "dispatch": dispatch_bytes(T, H, k, U, self.fp8)}
+        b["plan_dispatch"] = b["plan"] + b["dispatch"]
+        if self.em:
+            b["to_expert_major"] = to_expert_major_bytes(T, H, k, U, self.fp8)
+            b["combine"] = combine_em_bytes(T, H, k)
+        else:
+            b["combine"] = combine_bytes(T, H, k, U)
+        b["step"] = b["plan_dispatch"] + b["combine"] + b.get("to_expert_major", 0)
+        return b
+
+    def measure(self, steps, warmup):
+        """Step loop, then one loop per operation.  Every set has the same
+        routing, so the plan in the handle serves any set."""
+        for i in range(warmup):
+            self.step(self.sets[i % len(self.sets)])
+        times = {"step": self.loop(self.step, steps)}
+        assert self.M.mep_get_status(self.m.h, self.stream) == 0
+        times["plan_dispatch"] = self.loop(self.plan_dispatch, steps)
+        if self.em:
+            times["to_expert_major"] = self.loop(self.to_em, steps)
+        times["combine"] = self.loop(self.combine, steps)
+        times["plan"] = self.loop(self.plan, steps)
+        times["dispatch"] = self.loop(self.dispatch, steps)
+        self.M.mep_reset(self.m.h, self.stream)
+        nbytes = self.bytes()
+        ops = {}
+        for name, ms in times.items():
+            o = {"us": round(ms * 1e3, 2), "bytes": nbytes[name]}
+            o["GBps"] = round(o["bytes"] / (ms * 1e-3) / 1e9, 1)
+            o["frac"] = round(o["GBps"] / HBM_PEAK_GBS, 4)
+            ops[name] = o
+        return ops
 
 
 def time_decode(M, torch, wl, inp, reps, warmup):
     """128-token latency, bf16 both ways, identity expert (combine reads the
-    receive buffers): plan+dispatch as one call sequence, and combine, each
-    between its own pair of events with the GPU idle before it."""
-    T, H, R, cap, k = wl.tokens, wl.hidden, wl.ranks, wl.cap, wl.topk
-    m = M.Mep(H, wl.experts_per_rank, k, cap, R, fp8=False)
-    nsets = 4
-    sets = []
-    for _ in range(nsets):
-        sets.append({
-            "x": torch.from_numpy(inp["x"].view(np.int16)).cuda(),
-            "w": torch.from_numpy(inp["weights"]).cuda(),
-            "idx": torch.from_numpy(inp["indices"]).cuda(),
-            "counts": torch.zeros(R, dtype=torch.int32, device="cuda"),
-            "spos": torch.zeros((R, cap), dtype=torch.int32, device="cuda"),
-            "rx": torch.zeros((R, cap, H), dtype=torch.int16, device="cuda"),
-            "rw": torch.zeros((R, cap, k), dtype=torch.float32, device="cuda"),
-            "ri": torch.zeros((R, cap, k), dtype=torch.int32, device="cuda"),
-            "out": torch.empty((T, H), dtype=torch.int16, device="cuda"),
-        })
-    stream = torch.cuda.current_stream()
+    receive buffers): each call between its own pair of events, GPU idle before."""
+    r = Runner(M, torch, wl, inp, 4)
+    stream = r.stream
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def timed(fn, s):
+        a, b = ev(), ev()
+        torch.cuda.synchronize()
+        a.record(stream)
+        fn(s)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3
+
     res = {"plan_dispatch": [], "combine": [], "plan": [], "dispatch": []}
     for i in range(warmup + reps):
-        s = sets[i % nsets]
-        e = [ev() for _ in range(8)]
-        torch.cuda.synchronize()
-        e[0].record(stream)
-        M.mep_plan_dispatch(m.h, s["idx"], T, s["counts"], s["spos"], s["x"], s["w"], s["rx"],
-                            None, s["rw"], s["ri"], stream)
-        e[1].record(stream)
-        torch.cuda.synchronize()
-        e[2].record(stream)
-        M.mep_combine(m.h, M.MEP_RANK_MAJOR, s["rx"], s["w"], s["out"], stream)
-        e[3].record(stream)
-        torch.cuda.synchronize()
-        e[4].record(stream)
-        M.mep_plan(m.h, s["idx"], T, s["counts"], s["spos"], stream)
-        e[5].record(stream)
-        torch.cuda.synchronize()
-        e[6].record(stream)
-        M.mep_dispatch(m.h, s["x"], s["w"], s["idx"], s["rx"], None, s["rw"], s["ri"], stream)
-        e[7].record(stream)
-        M.mep_reset(m.h, stream)
-        torch.cuda.synchronize()
+        s = r.sets[i % len(r.sets)]
+        t = {"plan_dispatch": timed(r.plan_dispatch, s), "combine": timed(r.combine, s),
+             "plan": timed(r.plan, s), "dispatch": timed(r.dispatch, s)}
+        M.mep_reset(r.m.h, stream)
         if i >= warmup:
-            res["plan_dispatch"].append(e[0].elapsed_time(e[1]) * 1e3)
-            res["combine"].append(e[2].elapsed_time(e[3]) * 1e3)
-            res["plan"].append(e[4].elapsed_time(e[5]) * 1e3)
-            res["dispatch"].append(e[6].elapsed_time(e[7]) * 1e3)
-    U = int(sets[0]["counts"].sum().item())
+            for k, v in t.items():
+                res[k].append(v)
     out = {f"{k}_us": round(statistics.median(v), 2) for k, v in res.items()}
-    out["tokens"] = T
-    out["U"] = U
-    out["dispatch_bytes"] = dispatch_bytes(T, H, k, U, False) + plan_bytes(T, k, R, U)
-    out["combine_bytes"] = combine_bytes(T, H, k, U)
+    nb = r.bytes()
+    out.update({"tokens": wl.tokens, "U": r.U, "dispatch_bytes": nb["plan_dispatch"],
+                "combine_bytes": nb["combine"]})
     return out
 
 
 def copy_ceiling(torch, nbytes=512 << 20, reps=20):
-    """Read+write rate of a plain device-to-device copy (torch's copy kernel) over
-    rotating 512 MiB buffers: the practical HBM ceiling for streaming traffic."""
+    """Read+write rate of a plain device-to-device copy over rotating 512 MiB
+    buffers (also the calibration kernel for the traffic counters)."""
     n = 3
     src = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(n)]
     dst = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(n)]
@@ -287,6 +316,7 @@ def main():
     ap.add_argument("--sets", type=int, default=4)
     ap.add_argument("--decode-reps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="prefill and decode only")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -297,44 +327,50 @@ def main():
     import combine_mep_plan_amd as M
     from synthetic import WORKLOADS, make_inputs
 
+    say = lambda s: print(f"[bench] {s}", file=sys.stderr, flush=True)  # noqa: E731
     wl = WORKLOADS["prefill"]
     inp = make_inputs(wl, 0)
-    print(f"[bench] prefill setup: T={wl.tokens} H={wl.hidden} R={wl.ranks} "
-          f"epr={wl.experts_per_rank} k={wl.topk} sets={args.sets}", file=sys.stderr, flush=True)
-    m, sets, U = setup_prefill(M, torch, wl, inp, args.sets)
-    T, H, k, R = wl.tokens, wl.hidden, wl.topk, wl.ranks
-    ms_step, times = time_prefill(M, torch, m, sets, wl, args.steps, args.warmup)
-    b_plan, b_disp, b_comb = (plan_bytes(T, k, R, U), dispatch_bytes(T, H, k, U, True),
-                              combine_bytes(T, H, k, U))
-    step_bytes = b_plan + b_disp + b_comb
+    say(f"prefill: T={wl.tokens} H={wl.hidden} R={wl.ranks} epr={wl.experts_per_rank} "
+        f"k={wl.topk} sets={args.sets}")
+    run = Runner(M, torch, wl, inp, args.sets)
+    ops = run.measure(args.steps, args.warmup)
+    U = run.U
+    del run
+    torch.cuda.empty_cache()
+    ms_step = ops["step"]["us"] * 1e-3
+    step_bytes = ops["step"]["bytes"]
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    print(f"[bench] prefill done: {ms_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+    say(f"prefill step {ops['step']['us']} us, {value:.0f} GB/s")
 
-    nbytes = {"plan_dispatch": b_plan + b_disp, "combine": b_comb, "plan": b_plan,
-              "dispatch": b_disp}
-    ops = {}
-    for name, ms in times.items():
-        o = {"us": round(ms * 1e3, 2), "bytes": nbytes[name]}
-        o["GBps"] = round(o["bytes"] / (ms * 1e-3) / 1e9, 1)
-        o["frac"] = round(o["GBps"] / HBM_PEAK_GBS, 4)
-        ops[name] = o
     dom = max(("plan_dispatch", "combine"), key=lambda n: ops[n]["us"])
-    kernel_file = {"plan_dispatch": "dispatch.hip", "combine": "combine.hip"}[dom]
+    kfile = {"plan_dispatch": "dispatch.hip", "combine": "combine.hip"}[dom]
+    summary = {"plan_dispatch": "dispatch_prefill_pmc.txt",
+               "combine": "combine_prefill_pmc.txt"}[dom]
     achieved = ops[dom]["bytes"] / (ops[dom]["us"] * 1e-6) / 1e9
-    traffic = profile_traffic(f"{dom}_prefill_pmc.txt", src_digest(kernel_file))
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "algorithmic_bytes": ops[dom]["bytes"]}
+                "traffic": profile_traffic(summary, src_digest(kfile)),
+                "algorithmic_bytes": ops[dom]["bytes"]}
+    roofline["copy_ceiling_GBps"] = copy_ceiling(torch)
 
-    copy_gbs = copy_ceiling(torch)
-    roofline["copy_ceiling_GBps"] = copy_gbs
     dwl = WORKLOADS["decode"]
-    print("[bench] decode latency", file=sys.stderr, flush=True)
+    say("decode latency")
     decode = time_decode(M, torch, dwl, make_inputs(dwl, 0), args.decode_reps, 20)
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if not args.no_extra:
+        for name, nsets in (("skew", 3), ("stdmoe", 2)):
+            xwl = WORKLOADS[name]
+            say(f"{name}: T={xwl.tokens} R={xwl.ranks} epr={xwl.experts_per_rank}")
+            r = Runner(M, torch, xwl, make_inputs(xwl, 0), nsets)
+            extra[name] = {"U": r.U, "ops": r.measure(max(args.steps // 2, 10), 3)}
+            del r
+            torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        say("cpu baseline (oracle)")
         cpu = cpu_baseline(wl, inp)
 
     line = {
@@ -353,12 +389,14 @@ def main():
         "config": {"workload": "prefill: 4096 tokens x 7168 hidden, top-8 of 256 experts on 8 "
                                "virtual ranks x 32, FP8 E4M3 dispatch (fp32 scale per 128 "
                                "columns), bf16 combine with fp32 accumulation",
-                   "tokens": T, "hidden": H, "ranks": R, "experts_per_rank": wl.experts_per_rank,
-                   "topk": k, "unique_rows": U, "step_bytes": step_bytes,
+                   "tokens": wl.tokens, "hidden": wl.hidden, "ranks": wl.ranks,
+                   "experts_per_rank": wl.experts_per_rank, "topk": wl.topk,
+                   "unique_rows": U, "step_bytes": step_bytes,
                    "buffer_sets": args.sets, "hbm_frac": round(value / HBM_PEAK_GBS, 4)},
         "ops": ops,
         "decode_128": decode,
         "roofline": roofline,
+        "workloads": extra,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

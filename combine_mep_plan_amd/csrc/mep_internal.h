@@ -35,7 +35,6 @@ struct WsLayout {
   size_t em_row;     // int32 [cap][k]: expert-major row of (t, j), -1 if none
   size_t em_lmask;   // uint64 [R*cap]: local experts named by each receive row
   size_t em_ccnt;    // int32 [R][CR][epr]: per 64-row chunk, rows per local expert
-  size_t em_cbase;   // int32 [R][CR][epr]: first expert-major row of each chunk's run
   size_t total;
 };
 
@@ -107,10 +106,10 @@ struct EmArgs {
   int32_t* em_row;              // [T,k]
   uint64_t* lmask;              // [R*cap]
   int32_t* ccnt;                // [R][CR][epr]
-  int32_t* cbase;               // [R][CR][epr]
   uint32_t* status;
   int64_t cap_em;
   int32_t T, H, k, R, epr, cap, CR, nb, elem_bytes, spos_base;
+  int32_t slices;  // scatter: waves per receive row
 };
 
 // Launchers (return hipError_t of the launch).
