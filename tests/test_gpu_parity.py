@@ -299,3 +299,14 @@ def test_status_is_sticky_until_reset():
     M.mep_reset(g.m.h)
     M.mep_plan(g.m.h, g.idx, wl.tokens, g.counts, g.spos)
     assert M.mep_get_status(g.m.h) == 0
+
+
+@pytest.mark.parametrize("T", [4096, 4160])
+def test_fused_plan_dispatch_64_ranks(T):
+    # 64 ranks (the widest rank mask) over 64 and 65 count chunks
+    wl = Workload("wide", T, 256, 64, 2, 8, T, "fp8", "uniform", "dequant_half", "rank_major")
+    inp = make_inputs(wl, 1)
+    g = gpu_plan_dispatch(wl, inp, src_rank=5, fused=True)
+    pl, d = oracle_plan_dispatch(wl, inp, src_rank=5)
+    check_plan_dispatch(wl, inp, g, pl, d)
+    assert M.mep_get_status(g.m.h) == 0
