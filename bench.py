@@ -233,30 +233,59 @@ class Runner:
 
 def time_decode(M, torch, wl, inp, reps, warmup):
     """128-token latency, bf16 both ways, identity expert (combine reads the
-    receive buffers): each call between its own pair of events, GPU idle before."""
+    receive buffers).  device: the calls are queued behind a short GPU sleep, so
+    the two events bracket only GPU work (launch processing included, host
+    submission excluded); host: the GPU is idle when the first event is
+    recorded, so host submission time is included.  graph: plan+dispatch and
+    combine captured in one HIP graph and replayed (device timing)."""
     r = Runner(M, torch, wl, inp, 4)
     stream = r.stream
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
-    def timed(fn, s):
+    def timed(fns, s, queued):
         a, b = ev(), ev()
         torch.cuda.synchronize()
+        if queued:
+            torch.cuda._sleep(200_000)  # ~80 us of GPU spin while the host queues the calls
         a.record(stream)
-        fn(s)
+        for fn in fns:
+            fn(s)
         b.record(stream)
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e3
 
-    res = {"plan_dispatch": [], "combine": [], "plan": [], "dispatch": []}
+    seqs = {"plan_dispatch": [r.plan_dispatch], "combine": [r.combine], "plan": [r.plan],
+            "dispatch": [r.dispatch]}
+    res = {}
     for i in range(warmup + reps):
         s = r.sets[i % len(r.sets)]
-        t = {"plan_dispatch": timed(r.plan_dispatch, s), "combine": timed(r.combine, s),
-             "plan": timed(r.plan, s), "dispatch": timed(r.dispatch, s)}
+        for name, fns in seqs.items():
+            for queued in (True, False):
+                t = timed(fns, s, queued)
+                if i >= warmup:
+                    res.setdefault(f"{name}{'' if queued else '_host'}_us", []).append(t)
         M.mep_reset(r.m.h, stream)
+    out = {k: round(statistics.median(v), 2) for k, v in res.items()}
+    s = r.sets[0]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        r.stream = torch.cuda.current_stream()  # capture stream
+        r.plan_dispatch(s)
+        r.combine(s)
+    r.stream = stream
+    g_us = []
+    for i in range(warmup + reps):
+        a, b = ev(), ev()
+        torch.cuda.synchronize()
+        torch.cuda._sleep(200_000)
+        a.record(stream)
+        graph.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
         if i >= warmup:
-            for k, v in t.items():
-                res[k].append(v)
-    out = {f"{k}_us": round(statistics.median(v), 2) for k, v in res.items()}
+            g_us.append(a.elapsed_time(b) * 1e3)
+    out["graph_plan_dispatch_combine_us"] = round(statistics.median(g_us), 2)
+    del graph
     nb = r.bytes()
     out.update({"tokens": wl.tokens, "U": r.U, "dispatch_bytes": nb["plan_dispatch"],
                 "combine_bytes": nb["combine"]})

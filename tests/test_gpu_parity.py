@@ -310,3 +310,44 @@ def test_fused_plan_dispatch_64_ranks(T):
     pl, d = oracle_plan_dispatch(wl, inp, src_rank=5)
     check_plan_dispatch(wl, inp, g, pl, d)
     assert M.mep_get_status(g.m.h) == 0
+
+
+@pytest.mark.parametrize("T", [128, 700])
+def test_hip_graph_capture_replay(T):
+    # plan+dispatch and combine captured once in a HIP graph, replayed with new
+    # token rows and routing written in place between replays (with eager work
+    # and synchronisation in between); every replay must match the oracle
+    wl = _variant("prefill", tokens=T, cap=1024, hidden=1024)
+    R, epr, k, cap, H = wl.ranks, wl.experts_per_rank, wl.topk, wl.cap, wl.hidden
+    inp = make_inputs(wl, 100)
+    g = gpu_plan_dispatch(wl, inp, fused=True)  # eager warm-up, allocates everything
+    y = torch.zeros((R, cap, H), dtype=torch.int16, device="cuda")
+    out = torch.zeros((T, H), dtype=torch.int16, device="cuda")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        M.mep_plan_dispatch(g.m.h, g.idx, T, g.counts, g.spos, g.x, g.w, g.recv_x, g.recv_s,
+                            g.recv_w, g.recv_i)
+        M.mep_combine(g.m.h, M.MEP_RANK_MAJOR, y, g.w, out)
+    for rep in range(4):
+        new = make_inputs(wl, 200 + rep)
+        g.x.copy_(dev(new["x"]))
+        g.idx.copy_(dev(new["indices"]))
+        g.w.copy_(dev(new["weights"]))
+        pl, d = oracle_plan_dispatch(wl, new)
+        yo = O.expert_dequant(d["recv_x"], d["recv_scales"], 0.5)
+        y.copy_(dev(yo))  # the expert stand-in for this replay, written before it
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        counts = host(g.counts)
+        assert np.array_equal(counts, pl["recv_counts"]), rep
+        rx, rs = host(g.recv_x), host(g.recv_s)
+        for r in range(R):
+            n = int(counts[r])
+            assert np.array_equal(host(g.spos)[r, :n], pl["src_token_pos"][r, :n]), rep
+            assert np.array_equal(rx[r, :n], d["recv_x"][r, :n]), rep
+            assert np.array_equal(rs[r, :n].view(np.uint32),
+                                  d["recv_scales"][r, :n].view(np.uint32)), rep
+        ref = O.combine(yo, new["weights"], new["indices"], pl, epr, cap)
+        check_combine(host(out, np.uint16), ref)
+    assert M.mep_get_status(g.m.h) == 0
