@@ -45,6 +45,13 @@
  *   R8 a token naming an expert id outside [0, E) is not dispatched (all its
  *      slots are -1, status bit 1) and combines to +0; a token naming the
  *      same expert twice sets status bit 2 and is otherwise handled as usual.
+ *   R9 an already-quantized FP8 payload ([Backends]: the HIP backend carries
+ *      one) is a row of E4M3 bytes plus the caller's fp32 scale row of any
+ *      width; both travel unchanged.
+ *   R10 standard-MoE dispatch ([Guide] section 4, dispatch_standard_moe():
+ *      dispatch and convert_dispatch_output() in one call) produces exactly
+ *      what the two steps produce one after the other; it is not a function
+ *      of its own here.
  */
 #include <math.h>
 #include <stdint.h>
@@ -190,9 +197,15 @@ int32_t oracle_plan(const int32_t *idx, int32_t T, int32_t k, int32_t R, int32_t
 /* row, its k weights, its scales and its k expert ids; reading R5 for the   */
 /* FP8 payload).                                                             */
 /*                                                                          */
-/* x [T,H] bf16 bits; w, idx [T,k]; slot [T,k] from oracle_plan.             */
-/* quant == 0: recv_x is [R,cap,H] bf16 (bit copy), recv_scales unused.      */
-/* quant == 1: recv_x is [R,cap,H] E4M3 bytes, recv_scales [R,cap,H/128].    */
+/* w, idx [T,k]; slot [T,k] from oracle_plan.                               */
+/* quant == 0: x [T,H] bf16 bits; recv_x is [R,cap,H] bf16 (bit copy),      */
+/*             recv_scales unused.                                           */
+/* quant == 1: x [T,H] bf16 bits; recv_x is [R,cap,H] E4M3 bytes,           */
+/*             recv_scales [R,cap,H/128] (reading R5).                       */
+/* quant == 2: x [T,H] E4M3 bytes with xs [T,sd] fp32 scales, both copied    */
+/*             into recv_x [R,cap,H] bytes and recv_scales [R,cap,sd]        */
+/*             ([Backends]: the HIP backend carries already-quantized FP8    */
+/*             payloads; reading R9).                                        */
 /* recv_w [R,cap,k] f32, recv_idx [R,cap,k] i32.  Only written rows change.  */
 /* ------------------------------------------------------------------------ */
 
@@ -214,19 +227,24 @@ void oracle_quant_row(const uint16_t *x, int32_t H, uint8_t *q, float *scale) {
   }
 }
 
-void oracle_dispatch(const uint16_t *x, const float *w, const int32_t *idx,
-                     const int32_t *slot, int32_t T, int32_t H, int32_t k, int32_t R,
-                     int32_t epr, int32_t cap, int32_t quant, void *recv_x,
+void oracle_dispatch(const void *x, const float *xs, int32_t sd, const float *w,
+                     const int32_t *idx, const int32_t *slot, int32_t T, int32_t H, int32_t k,
+                     int32_t R, int32_t epr, int32_t cap, int32_t quant, void *recv_x,
                      float *recv_scales, float *recv_w, int32_t *recv_idx,
                      uint8_t *q_tmp /* [H] */, float *s_tmp /* [H/128] */) {
-  int32_t nb = H / 128;
+  int32_t nb = quant == 1 ? H / 128 : sd;
   (void)R;
   for (int32_t t = 0; t < T; t++) {
-    const uint16_t *xr = x + (int64_t)t * H;
     const int32_t *e = idx + (int64_t)t * k;
     const int32_t *sl = slot + (int64_t)t * k;
     if (sl[0] < 0) continue; /* R8: token not dispatched */
-    if (quant) oracle_quant_row(xr, H, q_tmp, s_tmp);
+    const uint16_t *xr = (const uint16_t *)x + (int64_t)t * H;
+    if (quant == 1) {
+      oracle_quant_row(xr, H, q_tmp, s_tmp);
+    } else if (quant == 2) {
+      memcpy(q_tmp, (const uint8_t *)x + (int64_t)t * H, (size_t)H);
+      if (sd > 0) memcpy(s_tmp, xs + (int64_t)t * sd, sizeof(float) * (size_t)sd);
+    }
     for (int32_t j = 0; j < k; j++) {
       int32_t r = e[j] / epr;
       int first = 1;
@@ -236,7 +254,7 @@ void oracle_dispatch(const uint16_t *x, const float *w, const int32_t *idx,
       int64_t row = (int64_t)r * cap + sl[j];
       if (quant) {
         memcpy((uint8_t *)recv_x + row * H, q_tmp, (size_t)H);
-        memcpy(recv_scales + row * nb, s_tmp, sizeof(float) * (size_t)nb);
+        if (nb > 0) memcpy(recv_scales + row * nb, s_tmp, sizeof(float) * (size_t)nb);
       } else {
         memcpy((uint16_t *)recv_x + row * H, xr, sizeof(uint16_t) * (size_t)H);
       }

@@ -57,7 +57,7 @@ def lib():
         L.oracle_plan.argtypes = [p, i32, i32, i32, i32, i32, i32, p, p, p]
         L.oracle_plan.restype = i32
         L.oracle_quant_row.argtypes = [p, i32, p, p]
-        L.oracle_dispatch.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, i32,
+        L.oracle_dispatch.argtypes = [p, p, i32, p, p, p, i32, i32, i32, i32, i32, i32, i32,
                                       p, p, p, p, p, p]
         L.oracle_combine.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, p]
         L.oracle_to_expert_major.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, i32,
@@ -120,19 +120,28 @@ def plan(indices: np.ndarray, R: int, epr: int, cap: int, src_rank: int = 0) -> 
 
 
 def dispatch(x: np.ndarray, weights: np.ndarray, indices: np.ndarray, pl: dict, R: int,
-             epr: int, cap: int, quant: bool, fill: int = 0) -> dict:
-    """Returns recv_x ([R,cap,H] uint16 bf16 bits, or uint8 E4M3 codes), recv_scales
-    ([R,cap,H/128] or None), recv_weights, recv_indices.  Unwritten rows keep
-    ``fill`` (bytes) so callers can see which rows were written."""
-    x = np.ascontiguousarray(x, dtype=np.uint16)
+             epr: int, cap: int, quant, fill: int = 0, scales: np.ndarray | None = None) -> dict:
+    """quant: 0/False bf16 copy, 1/True block quantisation, 2 carry (x holds
+    E4M3 bytes [T,H], scales [T,sd] fp32).  Returns recv_x ([R,cap,H] uint16
+    bf16 bits, or uint8 E4M3 codes), recv_scales ([R,cap,nb] or None),
+    recv_weights, recv_indices.  Unwritten rows keep ``fill`` (bytes) so callers
+    can see which rows were written."""
+    quant = int(quant)
+    x = np.ascontiguousarray(x, dtype=np.uint8 if quant == 2 else np.uint16)
     w = np.ascontiguousarray(weights, dtype=np.float32)
     idx = np.ascontiguousarray(indices, dtype=np.int32)
     T, H = x.shape
     k = idx.shape[1]
-    nb = H // 128 if quant else 0
+    if quant == 2:
+        xs = np.ascontiguousarray(scales if scales is not None else np.zeros((T, 0)),
+                                  dtype=np.float32)
+        nb = xs.shape[1]
+    else:
+        xs = np.zeros(1, dtype=np.float32)
+        nb = H // 128 if quant == 1 else 0
     if quant:
         rx = np.full((R, cap, H), fill, dtype=np.uint8)
-        rs = np.zeros((R, cap, nb), dtype=np.float32)
+        rs = np.zeros((R, cap, max(nb, 1)), dtype=np.float32)
     else:
         rx = np.full((R, cap, H), fill * 0x0101, dtype=np.uint16)
         rs = np.zeros(1, dtype=np.float32)
@@ -140,10 +149,22 @@ def dispatch(x: np.ndarray, weights: np.ndarray, indices: np.ndarray, pl: dict, 
     ri = np.full((R, cap, k), -1, dtype=np.int32)
     qt = np.empty(H, dtype=np.uint8)
     st = np.empty(max(nb, 1), dtype=np.float32)
-    lib().oracle_dispatch(_p(x), _p(w), _p(idx), _p(pl["slot"]), T, H, k, R, epr, cap,
-                          1 if quant else 0, _p(rx), _p(rs), _p(rw), _p(ri), _p(qt), _p(st))
-    return {"recv_x": rx, "recv_scales": rs if quant else None, "recv_weights": rw,
+    lib().oracle_dispatch(_p(x), _p(xs), nb, _p(w), _p(idx), _p(pl["slot"]), T, H, k, R, epr,
+                          cap, quant, _p(rx), _p(rs), _p(rw), _p(ri), _p(qt), _p(st))
+    return {"recv_x": rx, "recv_scales": rs if nb else None, "recv_weights": rw,
             "recv_indices": ri}
+
+
+def dispatch_standard_moe(x: np.ndarray, weights: np.ndarray, indices: np.ndarray, R: int,
+                          epr: int, cap: int, quant, cap_em: int, src_rank: int = 0,
+                          fill: int = 0, scales: np.ndarray | None = None) -> dict:
+    """Standard-MoE dispatch, reading R10: plan, dispatch and the expert-major
+    conversion one after the other."""
+    pl = plan(indices, R, epr, cap, src_rank)
+    disp = dispatch(x, weights, indices, pl, R, epr, cap, quant, fill=fill, scales=scales)
+    em = to_expert_major(disp, pl, R, epr, cap, indices.shape[0], cap_em, src_rank, fill=fill)
+    em["status"] |= pl["status"]
+    return em
 
 
 def combine(y: np.ndarray, weights: np.ndarray, indices: np.ndarray, pl: dict, epr: int,

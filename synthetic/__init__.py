@@ -6,4 +6,4 @@ arithmetic, so both the CPU oracle and the GPU path can take their inputs
 from it without sharing any of the method's code.
 """
 
-from .workloads import WORKLOADS, Workload, make_inputs  # noqa: F401
+from .workloads import WORKLOADS, Workload, make_fp8_payload, make_inputs  # noqa: F401

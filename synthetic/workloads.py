@@ -116,3 +116,16 @@ def make_inputs(wl: Workload, seed: int) -> dict:
     z = np.exp(logits - logits.max(axis=1, keepdims=True))
     w = (z / z.sum(axis=1, keepdims=True)).astype(np.float32)
     return {"x": x, "indices": np.ascontiguousarray(idx), "weights": np.ascontiguousarray(w)}
+
+
+def make_fp8_payload(T: int, H: int, scale_dim: int, seed: int) -> dict:
+    """An already-quantized payload for the carry mode: E4M3 bytes drawn
+    uniformly over the 254 non-NaN codes ([T,H] uint8) and fp32 scales drawn
+    uniformly from [2^-8, 1) ([T,scale_dim]).  Own generator, seeded apart
+    from make_inputs."""
+    rng = np.random.default_rng(10_000 + seed)
+    codes = rng.integers(0, 254, (T, H), dtype=np.int32)
+    codes += codes >= 0x7F   # skip 0x7F (NaN)
+    codes += codes >= 0xFF   # skip 0xFF (NaN)
+    scales = (2.0 ** -8 + rng.random((T, scale_dim)) * (1 - 2.0 ** -8)).astype(np.float32)
+    return {"q": codes.astype(np.uint8), "scales": scales}

@@ -475,3 +475,86 @@ def test_combine_is_fused_chain_in_top_k_order(oracle):
     assert np.array_equal(out, ref)
     # the data does tell a fused chain from a multiply-then-add chain
     assert np.count_nonzero(torch_bf16(unfused) != ref) > 0
+
+
+# ----------------------------------------------------------------------------
+# already-quantized FP8 payloads (carry) and standard-MoE dispatch
+# ----------------------------------------------------------------------------
+
+def test_carry_of_prequantized_rows_equals_quantising_dispatch(oracle):
+    # Carrying rows that were quantised beforehand must land exactly what the
+    # quantising dispatch writes: the two modes differ only in where R5 runs.
+    wl = WORKLOADS["prefill"].with_tokens(160)
+    inp = make_inputs(wl, 21)
+    R, epr, cap = wl.ranks, wl.experts_per_rank, wl.cap
+    pl = oracle.plan(inp["indices"], R, epr, cap)
+    dq = oracle.dispatch(inp["x"], inp["weights"], inp["indices"], pl, R, epr, cap, 1, fill=0x33)
+    rows = [oracle.quant_row(inp["x"][t]) for t in range(wl.tokens)]
+    q = np.stack([r[0] for r in rows])
+    s = np.stack([r[1] for r in rows])
+    dc = oracle.dispatch(q, inp["weights"], inp["indices"], pl, R, epr, cap, 2, fill=0x33,
+                         scales=s)
+    for key in ("recv_x", "recv_scales", "recv_weights", "recv_indices"):
+        assert np.array_equal(dq[key], dc[key]), key
+
+
+@pytest.mark.parametrize("sd", [0, 3, 56])
+def test_carry_copies_bytes_and_scale_rows(oracle, sd):
+    # Any bytes (NaN and inf codes included) and any scale width travel unchanged
+    # to the row of every distinct destination rank; other rows keep the fill.
+    rng = np.random.default_rng(5 + sd)
+    T, H, R, epr, k, cap = 70, 256, 4, 3, 3, 80
+    idx = np.stack([rng.choice(R * epr, k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k), dtype=np.float32)
+    x = rng.integers(0, 256, (T, H), dtype=np.uint8)
+    s = rng.standard_normal((T, sd)).astype(np.float32)
+    pl = oracle.plan(idx, R, epr, cap)
+    d = oracle.dispatch(x, w, idx, pl, R, epr, cap, 2, fill=0x77, scales=s)
+    written = np.zeros((R, cap), dtype=bool)
+    for t in range(T):
+        for j in range(k):
+            r = idx[t, j] // epr
+            row = pl["slot"][t, j]
+            written[r, row] = True
+            assert np.array_equal(d["recv_x"][r, row], x[t])
+            if sd:
+                assert np.array_equal(d["recv_scales"][r, row], s[t])
+            assert np.array_equal(d["recv_indices"][r, row], idx[t])
+    assert np.all(d["recv_x"][~written] == 0x77)
+    assert (d["recv_scales"] is None) == (sd == 0)
+
+
+def test_standard_moe_by_brute_force(oracle):
+    # Tiny case written out by hand: expert e's rows are the valid tokens naming
+    # e, ascending, each once (a repeated id maps the first position); segments
+    # start at multiples of 128; a token with an id outside [0, E) goes nowhere.
+    rng = np.random.default_rng(8)
+    T, H, R, epr, k, cap = 90, 128, 3, 2, 3, 96
+    E = R * epr
+    idx = rng.integers(0, E, (T, k)).astype(np.int32)  # repeats allowed
+    idx[7, 1] = E          # bad id
+    idx[40, 0] = -1        # bad id
+    w = rng.random((T, k), dtype=np.float32)
+    x = rng.integers(0, 1 << 16, (T, H), dtype=np.uint16)
+    x &= np.uint16(0xBFFF)  # keep away from inf/NaN patterns
+    cap_em = T * k + 127 * E
+    em = oracle.dispatch_standard_moe(x, w, idx, R, epr, cap, 0, cap_em, fill=0x11)
+    valid = [t for t in range(T) if np.all((idx[t] >= 0) & (idx[t] < E))]
+    assert em["status"] & oracle.ST_BAD_INDEX
+    assert em["status"] & oracle.ST_DUP_EXPERT
+    off = 0
+    for e in range(E):
+        toks = [t for t in valid if e in idx[t]]
+        assert em["em_counts"][e] == len(toks)
+        assert em["em_offsets"][e] == off
+        for i, t in enumerate(toks):
+            assert em["em_src_pos"][off + i] == t
+            assert np.array_equal(em["em_x"][off + i], x[t])
+            j = int(np.nonzero(idx[t] == e)[0][0])
+            assert em["tok_em_row"][t, j] == off + i
+        off += (len(toks) + 127) // 128 * 128
+    assert em["em_offsets"][E] == off
+    for t in range(T):
+        for j in range(k):
+            first = t in valid and idx[t, j] not in idx[t, :j]
+            assert (em["tok_em_row"][t, j] >= 0) == first
