@@ -9,7 +9,8 @@ combine").  value = the step's algorithmic HBM bytes / step time.
 
 Also measured, each on its own buffers: decode latency (128 tokens, bf16 both
 ways), the skewed-routing workload (Zipf 1.2, 16 ranks) and the standard-MoE
-workload (FP8 dispatch, expert-major conversion, combine from it).  Inputs are
+workload (FP8 dispatch, expert-major conversion, combine from it; and the
+single-call standard-MoE dispatch followed by the same combine).  Inputs are
 synthetic and resident in HBM; expert outputs are produced once, before
 timing, by the stand-in expert.  Buffer sets rotate so no step finds its data
 in the 256 MB Infinity Cache.  Kernel durations come from back-to-back loops
@@ -59,6 +60,14 @@ def to_expert_major_bytes(T, H, k, U, fp8):
     nb = H // 128 if fp8 else 0
     b = 1 if fp8 else 2
     return U * (H * b + nb * 4 + k * 4) + T * k * (H * b + nb * 4 + 4)
+
+
+def standard_moe_bytes(T, H, k, E, Uem, fp8):
+    # x and ids read once; each expert row written with its scales and source
+    # position; per-expert counts and offsets
+    nb = H // 128 if fp8 else 0
+    b = 1 if fp8 else 2
+    return T * H * 2 + T * k * 4 + Uem * (H * b + nb * 4 + 4) + E * 8
 
 
 def combine_em_bytes(T, H, k):
@@ -153,6 +162,7 @@ class Runner:
             self.sets.append(s)
         torch.cuda.synchronize()
         self.U = int(self.sets[0]["counts"].sum().item())
+        self.Uem = int(self.sets[0]["emc"].sum().item()) if self.em else 0
 
     def stand_in(self, x, scales):
         # expert outputs (harness, untimed): identity for bf16 payloads,
@@ -166,14 +176,25 @@ class Runner:
 
     def plan_dispatch(self, s):
         self.M.mep_plan_dispatch(self.m.h, s["idx"], self.wl.tokens, s["counts"], s["spos"],
-                                 s["x"], s["w"], s["rx"], s["rs"], s["rw"], s["ri"], self.stream)
+                                 s["x"], s["w"], None, s["rx"], s["rs"], s["rw"], s["ri"],
+                                 self.stream)
 
     def plan(self, s):
         self.M.mep_plan(self.m.h, s["idx"], self.wl.tokens, s["counts"], s["spos"], self.stream)
 
     def dispatch(self, s):
-        self.M.mep_dispatch(self.m.h, s["x"], s["w"], s["idx"], s["rx"], s["rs"], s["rw"],
+        self.M.mep_dispatch(self.m.h, s["x"], s["w"], None, s["idx"], s["rx"], s["rs"], s["rw"],
                             s["ri"], self.stream)
+
+    def standard_moe(self, s):
+        self.M.mep_dispatch_standard_moe(self.m.h, s["idx"], self.wl.tokens, s["x"], None,
+                                         s["emx"], s["ems"], s["emc"], s["emo"], s["emp"],
+                                         self.wl.cap_em, self.stream)
+
+    def step_standard(self, s):
+        self.standard_moe(s)
+        self.combine(s)
+        self.M.mep_reset(self.m.h, self.stream)
 
     def to_em(self, s):
         self.M.mep_to_expert_major(self.m.h, s["rx"], s["rs"], s["ri"], s["counts"], s["spos"],
@@ -202,6 +223,9 @@ class Runner:
         if self.em:
             b["to_expert_major"] = to_expert_major_bytes(T, H, k, U, self.fp8)
             b["combine"] = combine_em_bytes(T, H, k)
+            b["dispatch_standard_moe"] = standard_moe_bytes(T, H, k, wl.experts, self.Uem,
+                                                            self.fp8)
+            b["step_standard"] = b["dispatch_standard_moe"] + b["combine"]
         else:
             b["combine"] = combine_bytes(T, H, k, U)
         b["step"] = b["plan_dispatch"] + b["combine"] + b.get("to_expert_major", 0)
@@ -220,6 +244,12 @@ class Runner:
         times["combine"] = self.loop(self.combine, steps)
         times["plan"] = self.loop(self.plan, steps)
         times["dispatch"] = self.loop(self.dispatch, steps)
+        if self.em:
+            # standard-MoE dispatch straight into the expert-major layout, then
+            # the same expert-major combine
+            times["step_standard"] = self.loop(self.step_standard, steps)
+            assert self.M.mep_get_status(self.m.h, self.stream) == 0
+            times["dispatch_standard_moe"] = self.loop(self.standard_moe, steps)
         self.M.mep_reset(self.m.h, self.stream)
         nbytes = self.bytes()
         ops = {}

@@ -27,6 +27,7 @@ MEP_DEV_EM_OVERFLOW = 4
 
 MEP_QUANT_NONE = 0
 MEP_QUANT_FP8_E4M3_BLOCK128 = 1
+MEP_QUANT_FP8_CARRY = 2
 MEP_RANK_MAJOR = 0
 MEP_EXPERT_MAJOR = 1
 
@@ -68,8 +69,9 @@ def lib() -> C.CDLL:
             "mep_create": ([cfgp, p, sz, C.POINTER(p)], C.c_int),
             "mep_destroy": ([p], C.c_int),
             "mep_plan": ([p, p, i32, p, p, p], C.c_int),
-            "mep_dispatch": ([p, p, p, p, p, p, p, p, p], C.c_int),
-            "mep_plan_dispatch": ([p, p, i32, p, p, p, p, p, p, p, p, p], C.c_int),
+            "mep_dispatch": ([p, p, p, p, p, p, p, p, p, p], C.c_int),
+            "mep_plan_dispatch": ([p, p, i32, p, p, p, p, p, p, p, p, p, p], C.c_int),
+            "mep_dispatch_standard_moe": ([p, p, i32, p, p, p, p, p, p, p, i64, p], C.c_int),
             "mep_to_expert_major": ([p, p, p, p, p, p, p, p, p, p, p, i64, p], C.c_int),
             "mep_combine": ([p, i32, p, p, p, p], C.c_int),
             "mep_reset": ([p, p], C.c_int),
@@ -135,20 +137,29 @@ def mep_plan(h, indices, T, recv_counts, src_token_pos, stream=None) -> None:
                                       _ptr(src_token_pos), s))
 
 
-def mep_dispatch(h, x, weights, indices, recv_x, recv_scales, recv_weights, recv_indices,
-                 stream=None) -> None:
+def mep_dispatch(h, x, weights, scales, indices, recv_x, recv_scales, recv_weights,
+                 recv_indices, stream=None) -> None:
     s = _stream(stream, recv_x)
-    _check("mep_dispatch", lib().mep_dispatch(h, _ptr(x), _ptr(weights), _ptr(indices),
-                                              _ptr(recv_x), _ptr(recv_scales),
+    _check("mep_dispatch", lib().mep_dispatch(h, _ptr(x), _ptr(weights), _ptr(scales),
+                                              _ptr(indices), _ptr(recv_x), _ptr(recv_scales),
                                               _ptr(recv_weights), _ptr(recv_indices), s))
 
 
-def mep_plan_dispatch(h, indices, T, recv_counts, src_token_pos, x, weights, recv_x, recv_scales,
-                      recv_weights, recv_indices, stream=None) -> None:
+def mep_plan_dispatch(h, indices, T, recv_counts, src_token_pos, x, weights, scales, recv_x,
+                      recv_scales, recv_weights, recv_indices, stream=None) -> None:
     s = _stream(stream, recv_x)
     _check("mep_plan_dispatch", lib().mep_plan_dispatch(
         h, _ptr(indices), T, _ptr(recv_counts), _ptr(src_token_pos), _ptr(x), _ptr(weights),
-        _ptr(recv_x), _ptr(recv_scales), _ptr(recv_weights), _ptr(recv_indices), s))
+        _ptr(scales), _ptr(recv_x), _ptr(recv_scales), _ptr(recv_weights), _ptr(recv_indices),
+        s))
+
+
+def mep_dispatch_standard_moe(h, indices, T, x, scales, em_x, em_scales, em_counts, em_offsets,
+                              em_src_pos, cap_em, stream=None) -> None:
+    s = _stream(stream, em_x)
+    _check("mep_dispatch_standard_moe", lib().mep_dispatch_standard_moe(
+        h, _ptr(indices), T, _ptr(x), _ptr(scales), _ptr(em_x), _ptr(em_scales),
+        _ptr(em_counts), _ptr(em_offsets), _ptr(em_src_pos), cap_em, s))
 
 
 def mep_to_expert_major(h, recv_x, recv_scales, recv_indices, recv_counts, src_token_pos, em_x,
@@ -193,14 +204,20 @@ def mep_probe_bf16(inp, out, n, stream=None) -> None:
 
 class Mep:
     """A handle together with the device workspace it is bound to (allocated
-    here with torch, the only allocation on the Python side)."""
+    here with torch, the only allocation on the Python side).  ``fp8=True``
+    selects block quantisation; ``quant``/``scale_dim`` set the payload mode
+    explicitly (MEP_QUANT_FP8_CARRY takes the caller's scale columns)."""
 
     def __init__(self, hidden_dim, num_experts_per_rank, num_experts_per_token,
-                 max_num_inp_token_per_rank, world_size, rank=0, fp8=False, device="cuda"):
+                 max_num_inp_token_per_rank, world_size, rank=0, fp8=False, device="cuda",
+                 quant=None, scale_dim=None):
         import torch
-        self.cfg = MepConfig(hidden_dim, hidden_dim // 128 if fp8 else 0, num_experts_per_rank,
-                             num_experts_per_token, max_num_inp_token_per_rank, world_size, rank,
-                             MEP_QUANT_FP8_E4M3_BLOCK128 if fp8 else MEP_QUANT_NONE)
+        if quant is None:
+            quant = MEP_QUANT_FP8_E4M3_BLOCK128 if fp8 else MEP_QUANT_NONE
+        if scale_dim is None:
+            scale_dim = hidden_dim // 128 if quant != MEP_QUANT_NONE else 0
+        self.cfg = MepConfig(hidden_dim, scale_dim, num_experts_per_rank, num_experts_per_token,
+                             max_num_inp_token_per_rank, world_size, rank, quant)
         nbytes = mep_workspace_bytes(self.cfg)
         if nbytes == 0:
             raise MepError("mep_workspace_bytes", MEP_ERR_CONFIG)

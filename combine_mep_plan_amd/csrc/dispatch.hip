@@ -15,6 +15,11 @@
 // write rate; every receive-row store is a non-temporal 16-byte-per-lane
 // store (1 KiB per wave instruction).
 //
+// Payloads: bf16 rows copied; bf16 rows quantised to OCP E4M3 with per-128
+// scales; or rows that arrive already in E4M3 with the caller's scale rows
+// ("carry", "Choosing an EP API and backend": the HIP backend carries
+// already-quantized FP8 payloads), copied with their scales.
+//
 // Where the destination slots come from:
 //   kRoute  : a prior plan's receive row of each (token, top-k position);
 //   kCounts : computed here from the count launch's per-chunk prefixes (the
@@ -111,43 +116,12 @@ __device__ __forceinline__ void store_meta(const DispatchArgs& a, int t, int row
   }
 }
 
-// FP8: this lane's 16 columns (in0: 0..7, in1: 8..15) -> 16 codes; the block
-// scale is shared by the 8 lanes of a 128-column block.
-__device__ __forceinline__ u32x4 quant16(u32x4 in0, u32x4 in1, float& scale) {
-  float f[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = bf16_lo(in0[i]);
-    f[2 * i + 1] = bf16_hi(in0[i]);
-    f[8 + 2 * i] = bf16_lo(in1[i]);
-    f[8 + 2 * i + 1] = bf16_hi(in1[i]);
-  }
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
-  amax = fmaxf(amax, __shfl_xor(amax, 1));
-  amax = fmaxf(amax, __shfl_xor(amax, 2));
-  amax = fmaxf(amax, __shfl_xor(amax, 4));
-  const float s = amax / 448.0f;
-  scale = s;
-  uint32_t w[4];
-  if (s == 0.0f) {  // all-zero block: signed zero codes
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = ((__float_as_uint(f[4 * i]) >> 31) << 7) |
-             ((__float_as_uint(f[4 * i + 1]) >> 31) << 15) |
-             ((__float_as_uint(f[4 * i + 2]) >> 31) << 23) |
-             ((__float_as_uint(f[4 * i + 3]) >> 31) << 31);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = pack_e4m3x4(f[4 * i] / s, f[4 * i + 1] / s, f[4 * i + 2] / s, f[4 * i + 3] / s);
-  }
-  return u32x4{w[0], w[1], w[2], w[3]};
-}
-
-template <bool FP8, int MODE, int KMAX>
+// QUANT: MEP_QUANT_NONE (bf16 copy), MEP_QUANT_FP8_E4M3_BLOCK128 (quantise),
+// MEP_QUANT_FP8_CARRY (E4M3 bytes and the caller's scale rows copied).
+template <int QUANT, int MODE, int KMAX>
 __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
+  constexpr bool FP8 = QUANT == MEP_QUANT_FP8_E4M3_BLOCK128;
+  constexpr bool CARRY = QUANT == MEP_QUANT_FP8_CARRY;
   const int lane = threadIdx.x & 63;
   const int g = first_lane(blockIdx.x * 4 + (threadIdx.x >> 6));
   const int t = g / a.slices, sl = g - t * a.slices;
@@ -155,10 +129,12 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
   if (MODE == kInline && g == 0 && lane == 0) *a.status_next = 0u;
 
   // this wave's unit of the row: loads go out before the routing work
-  const int nu = FP8 ? a.H / 16 : a.H / 8;
+  // 16-byte output units per row: 16 E4M3 codes, or 8 bf16 values
+  const int nu = (FP8 || CARRY) ? a.H / 16 : a.H / 8;
   const int v = sl * kWave + lane;
   const bool on = v < nu;
-  const u32x4* src = reinterpret_cast<const u32x4*>(a.x) + (size_t)t * (a.H / 8);
+  const u32x4* src =
+      reinterpret_cast<const u32x4*>(a.x) + (size_t)t * (FP8 ? a.H / 8 : nu);
   u32x4 in0 = u32x4{0, 0, 0, 0}, in1 = u32x4{0, 0, 0, 0};
   if (on) {
     if (FP8) { in0 = src[2 * v]; in1 = src[2 * v + 1]; }
@@ -188,7 +164,12 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
       store_nt(reinterpret_cast<u32x4*>(a.recv_x) + (size_t)row * nu + v, q);
       if (FP8 && (v & 7) == 0) a.recv_scales[(size_t)row * nb + (v >> 3)] = scale;
     }
-    if (sl == 0) store_meta(a, t, row, lane);
+    if (sl == 0) {
+      store_meta(a, t, row, lane);
+      if (CARRY)
+        for (int i = lane; i < a.scale_dim; i += kWave)
+          a.recv_scales[(size_t)row * a.scale_dim + i] = a.x_scales[(size_t)t * a.scale_dim + i];
+    }
   };
   if (MODE == kRoute) {
     const int32_t* rr = a.rrow + (size_t)t * a.k;
@@ -201,38 +182,41 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
   }
 }
 
-template <bool FP8, int MODE>
+template <int QUANT, int MODE>
 hipError_t launch_mode(const DispatchArgs& a0, hipStream_t s) {
   DispatchArgs a = a0;
-  const int units = FP8 ? a.H / 16 : a.H / 8;
+  const int units = QUANT != MEP_QUANT_NONE ? a.H / 16 : a.H / 8;
   a.slices = (units + kWave - 1) / kWave;
   a.slice_units = kWave;
   const int64_t waves = (int64_t)a.T * a.slices;
   const int blocks = (int)((waves + 3) / 4);
-  if (a.k <= 8) dispatch_kernel<FP8, MODE, 8><<<blocks, 256, 0, s>>>(a);
-  else dispatch_kernel<FP8, MODE, kMaxTopk><<<blocks, 256, 0, s>>>(a);
+  if (a.k <= 8) dispatch_kernel<QUANT, MODE, 8><<<blocks, 256, 0, s>>>(a);
+  else dispatch_kernel<QUANT, MODE, kMaxTopk><<<blocks, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
 template <int MODE>
-hipError_t launch_dtype(const DispatchArgs& a, bool fp8, hipStream_t s) {
-  return fp8 ? launch_mode<true, MODE>(a, s) : launch_mode<false, MODE>(a, s);
+hipError_t launch_dtype(const DispatchArgs& a, hipStream_t s) {
+  switch (a.quant) {
+    case MEP_QUANT_FP8_E4M3_BLOCK128: return launch_mode<MEP_QUANT_FP8_E4M3_BLOCK128, MODE>(a, s);
+    case MEP_QUANT_FP8_CARRY: return launch_mode<MEP_QUANT_FP8_CARRY, MODE>(a, s);
+    default: return launch_mode<MEP_QUANT_NONE, MODE>(a, s);
+  }
 }
 
 }  // namespace
 
-hipError_t launch_dispatch(const DispatchArgs& a, bool fp8, hipStream_t s) {
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  return launch_dtype<kRoute>(a, fp8, s);
+  return launch_dtype<kRoute>(a, s);
 }
 
-hipError_t launch_plan_dispatch(const PlanArgs& p, const DispatchArgs& a, bool fp8,
-                                hipStream_t s) {
+hipError_t launch_plan_dispatch(const PlanArgs& p, const DispatchArgs& a, hipStream_t s) {
   if (a.T == 0) return launch_plan(p, s);
-  if (a.T <= kInlinePlanTokens) return launch_dtype<kInline>(a, fp8, s);
+  if (a.T <= kInlinePlanTokens) return launch_dtype<kInline>(a, s);
   hipError_t e = launch_plan_counts(p, s);
   if (e != hipSuccess) return e;
-  return launch_dtype<kCounts>(a, fp8, s);
+  return launch_dtype<kCounts>(a, s);
 }
 
 }  // namespace mep

@@ -138,7 +138,6 @@ __global__ __launch_bounds__(kOffThreads) void em_offsets_kernel(EmArgs a, int G
   }
   if (tid == kOffThreads - 1) {
     a.em_offsets[E] = part[tid];
-    if ((int64_t)part[tid] > a.cap_em) atomicOr(a.status, (uint32_t)MEP_DEV_EM_OVERFLOW);
   }
   __syncthreads();
 }
@@ -189,13 +188,10 @@ __global__ __launch_bounds__(256) void em_scatter_kernel(EmArgs a) {
   // row slice first: its loads do not depend on the placement
   const u32x4* src = reinterpret_cast<const u32x4*>(a.recv_x) + row * nv;
   u32x4 val[UPL];
-  float scl[UPL];
 #pragma unroll
   for (int q = 0; q < UPL; ++q) {
     const int v = (sl * UPL + q) * kWave + lane;
     val[q] = v < nv ? src[v] : u32x4{0, 0, 0, 0};
-    // FP8 rows: unit v holds columns 16v..16v+15, scale block v / 8
-    scl[q] = (a.nb > 0 && v < nv && (v & 7) == 0) ? a.recv_scales[row * a.nb + (v >> 3)] : 0.0f;
   }
   const int c = s / kChunk, sc = s % kChunk;
   const int peer = c * kChunk + lane;
@@ -222,11 +218,11 @@ __global__ __launch_bounds__(256) void em_scatter_kernel(EmArgs a) {
 #pragma unroll
     for (int q = 0; q < UPL; ++q) {
       const int v = (sl * UPL + q) * kWave + lane;
-      if (v < nv) {
-        store_nt(dst_x + (size_t)pos * nv + v, val[q]);
-        if (a.nb > 0 && (v & 7) == 0) a.em_scales[(size_t)pos * a.nb + (v >> 3)] = scl[q];
-      }
+      if (v < nv) store_nt(dst_x + (size_t)pos * nv + v, val[q]);
     }
+    if (sl == 0)  // the row's scale columns, one per lane
+      for (int i = lane; i < a.nb; i += kWave)
+        a.em_scales[(size_t)pos * a.nb + i] = a.recv_scales[row * a.nb + i];
     if (sl == 0) {
       const int e = r * a.epr + l;
       const uint64_t hit = ballot(myid == e);  // top-k position naming e

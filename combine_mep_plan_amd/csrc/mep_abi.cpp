@@ -39,6 +39,7 @@ WsLayout ws_layout(const mep_config& c) {
   L.em_row = take(cap * k * sizeof(int32_t));
   L.em_lmask = take(R * cap * sizeof(uint64_t));
   L.em_ccnt = take(R * C * epr * sizeof(int32_t));
+  L.sm_hist = take(C * R * epr * sizeof(int32_t));
   L.total = off;
   return L;
 }
@@ -65,6 +66,8 @@ static int check_config(const mep_config* c) {
     if (c->scale_dim != 0) return MEP_ERR_CONFIG;
   } else if (c->quant == MEP_QUANT_FP8_E4M3_BLOCK128) {
     if (H % 128 != 0 || c->scale_dim != H / 128) return MEP_ERR_CONFIG;
+  } else if (c->quant == MEP_QUANT_FP8_CARRY) {
+    if (H % 16 != 0 || c->scale_dim < 0 || c->scale_dim > (1 << 16)) return MEP_ERR_CONFIG;
   } else {
     return MEP_ERR_CONFIG;
   }
@@ -175,16 +178,24 @@ static int check_plan_args(mep_handle* h, const int32_t* indices, int32_t T,
   return MEP_OK;
 }
 
+// Scale columns the payload carries per row (0 for bf16 rows).
+static int scale_cols(const mep_config& c) {
+  return c.quant == MEP_QUANT_NONE ? 0 : c.scale_dim;
+}
+
 static int check_dispatch_args(mep_handle* h, int32_t T, const void* x, const float* weights,
-                               const int32_t* indices, const void* recv_x,
+                               const float* scales, const int32_t* indices, const void* recv_x,
                                const float* recv_scales, const float* recv_weights,
                                const int32_t* recv_indices) {
-  const bool fp8 = h->cfg.quant == MEP_QUANT_FP8_E4M3_BLOCK128;
+  const mep_config& c = h->cfg;
+  const bool carry = c.quant == MEP_QUANT_FP8_CARRY;
   if (!recv_x || !recv_weights || !recv_indices) return MEP_ERR_NULL;
-  if (fp8 && !recv_scales) return MEP_ERR_NULL;
+  if (scale_cols(c) > 0 && !recv_scales) return MEP_ERR_NULL;
   if (T > 0 && (!x || !weights || !indices)) return MEP_ERR_NULL;
+  if (T > 0 && carry && c.scale_dim > 0 && !scales) return MEP_ERR_NULL;
   if ((x && !aligned16(x)) || (weights && !aligned16(weights)) ||
       (indices && !aligned16(indices)) || !aligned16(recv_x) ||
+      (carry && scales && !aligned16(scales)) ||
       (recv_scales && !aligned16(recv_scales)) || !aligned16(recv_weights) ||
       !aligned16(recv_indices))
     return MEP_ERR_ALIGN;
@@ -192,12 +203,15 @@ static int check_dispatch_args(mep_handle* h, int32_t T, const void* x, const fl
 }
 
 static mep::DispatchArgs dispatch_args(mep_handle* h, int32_t T, const void* x,
-                                       const float* weights, const int32_t* indices,
-                                       void* recv_x, float* recv_scales, float* recv_weights,
-                                       int32_t* recv_indices) {
+                                       const float* weights, const float* scales,
+                                       const int32_t* indices, void* recv_x, float* recv_scales,
+                                       float* recv_weights, int32_t* recv_indices) {
   const mep_config& c = h->cfg;
   mep::DispatchArgs a{};
   a.x = x;
+  a.x_scales = c.quant == MEP_QUANT_FP8_CARRY ? scales : nullptr;
+  a.quant = c.quant;
+  a.scale_dim = scale_cols(c);
   a.w = weights;
   a.idx = indices;
   a.rrow = ws_ptr<int32_t>(h, h->lay.rrow);
@@ -237,39 +251,37 @@ int mep_plan(mep_handle* h, const int32_t* indices, int32_t T, int32_t* recv_cou
   return MEP_OK;
 }
 
-int mep_dispatch(mep_handle* h, const void* x, const float* weights, const int32_t* indices,
-                 void* recv_x, float* recv_scales, float* recv_weights, int32_t* recv_indices,
-                 void* stream) {
+int mep_dispatch(mep_handle* h, const void* x, const float* weights, const float* scales,
+                 const int32_t* indices, void* recv_x, float* recv_scales, float* recv_weights,
+                 int32_t* recv_indices, void* stream) {
   if (!h) return MEP_ERR_NULL;
   if (!h->plan_valid) return MEP_ERR_STATE;
   const int32_t T = h->plan_T;
-  int rc = check_dispatch_args(h, T, x, weights, indices, recv_x, recv_scales, recv_weights,
-                               recv_indices);
+  int rc = check_dispatch_args(h, T, x, weights, scales, indices, recv_x, recv_scales,
+                               recv_weights, recv_indices);
   if (rc != MEP_OK) return rc;
-  const mep::DispatchArgs a = dispatch_args(h, T, x, weights, indices, recv_x, recv_scales,
-                                            recv_weights, recv_indices);
-  return hip_rc(mep::launch_dispatch(a, h->cfg.quant == MEP_QUANT_FP8_E4M3_BLOCK128,
-                                     (hipStream_t)stream));
+  const mep::DispatchArgs a = dispatch_args(h, T, x, weights, scales, indices, recv_x,
+                                            recv_scales, recv_weights, recv_indices);
+  return hip_rc(mep::launch_dispatch(a, (hipStream_t)stream));
 }
 
 int mep_plan_dispatch(mep_handle* h, const int32_t* indices, int32_t T, int32_t* recv_counts,
                       int32_t* src_token_pos, const void* x, const float* weights,
-                      void* recv_x, float* recv_scales, float* recv_weights,
-                      int32_t* recv_indices, void* stream) {
+                      const float* scales, void* recv_x, float* recv_scales,
+                      float* recv_weights, int32_t* recv_indices, void* stream) {
   int rc = check_plan_args(h, indices, T, recv_counts, src_token_pos);
   if (rc != MEP_OK) return rc;
-  rc = check_dispatch_args(h, T, x, weights, indices, recv_x, recv_scales, recv_weights,
+  rc = check_dispatch_args(h, T, x, weights, scales, indices, recv_x, recv_scales, recv_weights,
                            recv_indices);
   if (rc != MEP_OK) return rc;
   const mep::PlanArgs p = plan_args(h, indices, T, recv_counts, src_token_pos);
-  mep::DispatchArgs a = dispatch_args(h, T, x, weights, indices, recv_x, recv_scales,
+  mep::DispatchArgs a = dispatch_args(h, T, x, weights, scales, indices, recv_x, recv_scales,
                                       recv_weights, recv_indices);
   a.recv_counts = recv_counts;
   a.spos = src_token_pos;
   h->plan_valid = false;
   h->em_valid = false;
-  rc = hip_rc(mep::launch_plan_dispatch(p, a, h->cfg.quant == MEP_QUANT_FP8_E4M3_BLOCK128,
-                                        (hipStream_t)stream));
+  rc = hip_rc(mep::launch_plan_dispatch(p, a, (hipStream_t)stream));
   if (rc != MEP_OK) return rc;
   h->plan_valid = true;
   h->planned_since_reset = true;
@@ -285,11 +297,12 @@ int mep_to_expert_major(mep_handle* h, const void* recv_x, const float* recv_sca
   if (!h) return MEP_ERR_NULL;
   if (!h->plan_valid) return MEP_ERR_STATE;
   const mep_config& c = h->cfg;
-  const bool fp8 = c.quant == MEP_QUANT_FP8_E4M3_BLOCK128;
+  const bool fp8 = c.quant != MEP_QUANT_NONE;  // 1-byte E4M3 rows
+  const int nb = scale_cols(c);
   if (!recv_x || !recv_indices || !recv_counts || !src_token_pos || !em_x || !em_counts ||
       !em_offsets || !em_src_pos)
     return MEP_ERR_NULL;
-  if (fp8 && (!recv_scales || !em_scales)) return MEP_ERR_NULL;
+  if (nb > 0 && (!recv_scales || !em_scales)) return MEP_ERR_NULL;
   if (cap_em < 0 || cap_em > INT32_MAX) return MEP_ERR_SHAPE;
   if (!aligned16(recv_x) || !aligned16(recv_indices) || !aligned16(recv_counts) ||
       !aligned16(src_token_pos) || !aligned16(em_x) || !aligned16(em_counts) ||
@@ -298,13 +311,13 @@ int mep_to_expert_major(mep_handle* h, const void* recv_x, const float* recv_sca
     return MEP_ERR_ALIGN;
   mep::EmArgs a{};
   a.recv_x = recv_x;
-  a.recv_scales = fp8 ? recv_scales : nullptr;
+  a.recv_scales = nb > 0 ? recv_scales : nullptr;
   a.recv_idx = recv_indices;
   a.recv_counts = recv_counts;
   a.spos = src_token_pos;
   a.rrow = ws_ptr<int32_t>(h, h->lay.rrow);
   a.em_x = em_x;
-  a.em_scales = fp8 ? em_scales : nullptr;
+  a.em_scales = nb > 0 ? em_scales : nullptr;
   a.em_counts = em_counts;
   a.em_offsets = em_offsets;
   a.em_src_pos = em_src_pos;
@@ -320,7 +333,7 @@ int mep_to_expert_major(mep_handle* h, const void* recv_x, const float* recv_sca
   a.epr = c.num_experts_per_rank;
   a.cap = c.max_num_inp_token_per_rank;
   a.CR = (c.max_num_inp_token_per_rank + mep::kChunk - 1) / mep::kChunk;
-  a.nb = fp8 ? c.hidden_dim / 128 : 0;
+  a.nb = nb;
   a.elem_bytes = fp8 ? 1 : 2;
   a.spos_base = c.rank * c.world_size * c.max_num_inp_token_per_rank;
   h->em_valid = false;
@@ -330,11 +343,61 @@ int mep_to_expert_major(mep_handle* h, const void* recv_x, const float* recv_sca
   return MEP_OK;
 }
 
+int mep_dispatch_standard_moe(mep_handle* h, const int32_t* indices, int32_t T, const void* x,
+                              const float* scales, void* em_x, float* em_scales,
+                              int32_t* em_counts, int32_t* em_offsets, int32_t* em_src_pos,
+                              int64_t cap_em, void* stream) {
+  if (!h) return MEP_ERR_NULL;
+  const mep_config& c = h->cfg;
+  const int nb = scale_cols(c);
+  const bool carry = c.quant == MEP_QUANT_FP8_CARRY;
+  if (T < 0 || T > c.max_num_inp_token_per_rank) return MEP_ERR_SHAPE;
+  if (cap_em < 0 || cap_em > INT32_MAX) return MEP_ERR_SHAPE;
+  if (!em_x || !em_counts || !em_offsets || !em_src_pos) return MEP_ERR_NULL;
+  if (nb > 0 && !em_scales) return MEP_ERR_NULL;
+  if (T > 0 && (!indices || !x)) return MEP_ERR_NULL;
+  if (T > 0 && carry && nb > 0 && !scales) return MEP_ERR_NULL;
+  if ((indices && !aligned16(indices)) || (x && !aligned16(x)) ||
+      (carry && scales && !aligned16(scales)) || !aligned16(em_x) ||
+      (em_scales && !aligned16(em_scales)) || !aligned16(em_counts) ||
+      !aligned16(em_offsets) || !aligned16(em_src_pos))
+    return MEP_ERR_ALIGN;
+  mep::SmArgs a{};
+  a.x = x;
+  a.x_scales = carry ? scales : nullptr;
+  a.idx = indices;
+  a.em_x = em_x;
+  a.em_scales = nb > 0 ? em_scales : nullptr;
+  a.em_counts = em_counts;
+  a.em_offsets = em_offsets;
+  a.em_src_pos = em_src_pos;
+  a.em_row = ws_ptr<int32_t>(h, h->lay.em_row);
+  a.chunk_hist = ws_ptr<int32_t>(h, h->lay.sm_hist);
+  a.status = status_word(h, h->epoch);
+  a.status_next = status_word(h, h->epoch + 1);
+  a.cap_em = cap_em;
+  a.T = T;
+  a.H = c.hidden_dim;
+  a.k = c.num_experts_per_token;
+  a.E = c.world_size * c.num_experts_per_rank;
+  a.quant = c.quant;
+  a.scale_dim = nb;
+  a.spos_base = c.rank * c.world_size * c.max_num_inp_token_per_rank;
+  h->plan_valid = false;  // no rank-major plan: only the expert-major combine follows
+  h->em_valid = false;
+  int rc = hip_rc(mep::launch_dispatch_standard_moe(a, (hipStream_t)stream));
+  if (rc != MEP_OK) return rc;
+  h->em_valid = true;
+  h->planned_since_reset = true;
+  h->plan_T = T;
+  return MEP_OK;
+}
+
 int mep_combine(mep_handle* h, int32_t layout, const void* y, const float* weights, void* out,
                 void* stream) {
   if (!h) return MEP_ERR_NULL;
   if (layout != MEP_RANK_MAJOR && layout != MEP_EXPERT_MAJOR) return MEP_ERR_SHAPE;
-  if (!h->plan_valid) return MEP_ERR_STATE;
+  if (layout == MEP_RANK_MAJOR && !h->plan_valid) return MEP_ERR_STATE;
   if (layout == MEP_EXPERT_MAJOR && !h->em_valid) return MEP_ERR_STATE;
   const int32_t T = h->plan_T;
   if (!out) return MEP_ERR_NULL;
@@ -375,13 +438,15 @@ int mep_get_status(mep_handle* h, void* stream, int32_t* device_status) {
 }
 
 int mep_get_route(mep_handle* h, int32_t* recv_row, int32_t* em_row, void* stream) {
-  if (!h || !recv_row) return MEP_ERR_NULL;
-  if (!h->plan_valid) return MEP_ERR_STATE;
+  if (!h || (!recv_row && !em_row)) return MEP_ERR_NULL;
+  if (recv_row && !h->plan_valid) return MEP_ERR_STATE;
   if (em_row && !h->em_valid) return MEP_ERR_STATE;
-  if (!aligned16(recv_row) || (em_row && !aligned16(em_row))) return MEP_ERR_ALIGN;
+  if ((recv_row && !aligned16(recv_row)) || (em_row && !aligned16(em_row))) return MEP_ERR_ALIGN;
   const int64_t n = (int64_t)h->plan_T * h->cfg.num_experts_per_token;
-  int rc = hip_rc(mep::launch_copy_i32(ws_ptr<int32_t>(h, h->lay.rrow), recv_row, n,
-                                       (hipStream_t)stream));
+  int rc = MEP_OK;
+  if (recv_row)
+    rc = hip_rc(mep::launch_copy_i32(ws_ptr<int32_t>(h, h->lay.rrow), recv_row, n,
+                                     (hipStream_t)stream));
   if (rc == MEP_OK && em_row)
     rc = hip_rc(mep::launch_copy_i32(ws_ptr<int32_t>(h, h->lay.em_row), em_row, n,
                                      (hipStream_t)stream));

@@ -35,6 +35,7 @@ struct WsLayout {
   size_t em_row;     // int32 [cap][k]: expert-major row of (t, j), -1 if none
   size_t em_lmask;   // uint64 [R*cap]: local experts named by each receive row
   size_t em_ccnt;    // int32 [R][CR][epr]: per 64-row chunk, rows per local expert
+  size_t sm_hist;    // int32 [C][E]: standard-MoE dispatch, per-chunk expert counts / prefixes
   size_t total;
 };
 
@@ -56,7 +57,8 @@ struct PlanArgs {
 };
 
 struct DispatchArgs {
-  const void* x;           // [T,H] bf16
+  const void* x;           // [T,H] bf16, or E4M3 bytes when carried
+  const float* x_scales;   // [T,scale_dim] carried scales (MEP_QUANT_FP8_CARRY)
   const float* w;          // [T,k]
   const int32_t* idx;      // [T,k]
   int32_t* rrow;           // [T,k] receive row of (t, j): read after a plan, written when fused
@@ -74,6 +76,7 @@ struct DispatchArgs {
   uint32_t* status;
   uint32_t* status_next;
   int32_t T, H, k, R, E, cap, spos_base;
+  int32_t quant, scale_dim;
   RankDiv rdiv;
   int32_t slices, slice_units;  // waves per token and 16-byte lane units per wave
 };
@@ -112,12 +115,29 @@ struct EmArgs {
   int32_t slices;  // scatter: waves per receive row
 };
 
+struct SmArgs {                // standard-MoE dispatch
+  const void* x;                // [T,H] bf16, or E4M3 bytes when carried
+  const float* x_scales;        // [T,scale_dim] carried scales
+  const int32_t* idx;           // [T,k]
+  void* em_x;                   // [cap_em,H]
+  float* em_scales;             // [cap_em,scale_dim]
+  int32_t* em_counts;           // [E]
+  int32_t* em_offsets;          // [E+1]
+  int32_t* em_src_pos;          // [cap_em]
+  int32_t* em_row;              // [T,k] expert-major row of (t, j)
+  int32_t* chunk_hist;          // [C][E]
+  uint32_t* status;
+  uint32_t* status_next;
+  int64_t cap_em;
+  int32_t T, H, k, E, quant, scale_dim, spos_base, slices;
+};
+
 // Launchers (return hipError_t of the launch).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_plan_counts(const PlanArgs& a, hipStream_t s);  // count launch only, T > 0
-hipError_t launch_dispatch(const DispatchArgs& a, bool fp8, hipStream_t s);
-hipError_t launch_plan_dispatch(const PlanArgs& p, const DispatchArgs& a, bool fp8,
-                                hipStream_t s);
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
+hipError_t launch_plan_dispatch(const PlanArgs& p, const DispatchArgs& a, hipStream_t s);
+hipError_t launch_dispatch_standard_moe(const SmArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_to_expert_major(const EmArgs& a, hipStream_t s);
 hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int64_t n, hipStream_t s);

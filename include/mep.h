@@ -56,6 +56,12 @@ extern "C" {
 #define MEP_QUANT_NONE 0              /* dispatch payload: bf16 bit copy        */
 #define MEP_QUANT_FP8_E4M3_BLOCK128 1 /* dispatch payload: OCP E4M3 codes with
                                          one fp32 scale per 128 columns          */
+#define MEP_QUANT_FP8_CARRY 2         /* dispatch payload arrives already as OCP
+                                         E4M3 bytes with scale_dim fp32 scales
+                                         per row; both are carried unchanged
+                                         ("Choosing an EP API and backend": the
+                                         HIP backend carries already-quantized
+                                         FP8 payloads)                           */
 #define MEP_RANK_MAJOR 0              /* combine input: [R, cap, H] bf16         */
 #define MEP_EXPERT_MAJOR 1            /* combine input: [cap_em, H] bf16         */
 
@@ -66,8 +72,10 @@ extern "C" {
  * meaning on one device and are absent.
  */
 typedef struct mep_config {
-  int32_t hidden_dim;                 /* H: > 0, multiple of 8; multiple of 128 with FP8  */
-  int32_t scale_dim;                  /* 0, or H/128 with MEP_QUANT_FP8_E4M3_BLOCK128      */
+  int32_t hidden_dim;                 /* H: > 0, multiple of 8; of 128 when quantising, of
+                                         16 when carrying E4M3                           */
+  int32_t scale_dim;                  /* 0 for bf16; H/128 when quantising; any >= 0 scale
+                                         columns per row when carrying                   */
   int32_t num_experts_per_rank;       /* epr: 1..64                                       */
   int32_t num_experts_per_token;      /* k: 1..32, k <= R*epr                              */
   int32_t max_num_inp_token_per_rank; /* cap: receive rows per rank and the largest T, >= 1 */
@@ -115,22 +123,26 @@ int mep_plan(mep_handle *h, const int32_t *indices, int32_t T, int32_t *recv_cou
              int32_t *src_token_pos, void *stream);
 
 /*
- * Dispatch ("MORI-EP User Guide" section 3 dispatch()): every planned
- * (token, rank) row receives
+ * Dispatch ("MORI-EP User Guide" section 3 dispatch(input, weights, scales,
+ * indices)): every planned (token, rank) row receives
  *   recv_x[r, s, :]       the token row: x[T,H] bf16 copied bit for bit
- *                         (MEP_QUANT_NONE, recv_x is [R,cap,H] bf16), or its
- *                         OCP E4M3 codes (FP8, recv_x is [R,cap,H] bytes):
- *                         per 128 columns b, scale = amax_b / 448 (fp32) and
- *                         code = E4M3_rne_satfinite(x / scale), signed zero
- *                         when amax_b == 0;
- *   recv_scales[r, s, b]  those scales (FP8 only; [R,cap,H/128] fp32, else NULL);
+ *                         (MEP_QUANT_NONE, recv_x is [R,cap,H] bf16); or its
+ *                         OCP E4M3 codes (MEP_QUANT_FP8_E4M3_BLOCK128, recv_x is
+ *                         [R,cap,H] bytes): per 128 columns b, scale =
+ *                         amax_b / 448 (fp32) and code =
+ *                         E4M3_rne_satfinite(x / scale), signed zero when
+ *                         amax_b == 0; or, MEP_QUANT_FP8_CARRY, the E4M3 bytes
+ *                         of x[T,H] copied;
+ *   recv_scales[r, s, :]  the block scales ([R,cap,H/128] fp32), or the carried
+ *                         scales[t, :] ([R,cap,scale_dim]); NULL for bf16;
  *   recv_weights[r, s, :] the token's k weights (fp32 [R,cap,k]);
  *   recv_indices[r, s, :] the token's k expert ids (int32 [R,cap,k]).
- * Rows past recv_counts[r] are not written.  Needs a valid plan; x, weights
- * and indices hold the planned T tokens.
+ * scales is the caller's [T,scale_dim] fp32 input for MEP_QUANT_FP8_CARRY and
+ * is ignored otherwise.  Rows past recv_counts[r] are not written.  Needs a
+ * valid plan; x, weights, scales and indices hold the planned T tokens.
  */
-int mep_dispatch(mep_handle *h, const void *x, const float *weights, const int32_t *indices,
-                 void *recv_x, float *recv_scales, float *recv_weights,
+int mep_dispatch(mep_handle *h, const void *x, const float *weights, const float *scales,
+                 const int32_t *indices, void *recv_x, float *recv_scales, float *recv_weights,
                  int32_t *recv_indices, void *stream);
 
 /*
@@ -142,8 +154,8 @@ int mep_dispatch(mep_handle *h, const void *x, const float *weights, const int32
  */
 int mep_plan_dispatch(mep_handle *h, const int32_t *indices, int32_t T, int32_t *recv_counts,
                       int32_t *src_token_pos, const void *x, const float *weights,
-                      void *recv_x, float *recv_scales, float *recv_weights,
-                      int32_t *recv_indices, void *stream);
+                      const float *scales, void *recv_x, float *recv_scales,
+                      float *recv_weights, int32_t *recv_indices, void *stream);
 
 /*
  * Standard-MoE layout ("MORI-EP User Guide" section 4,
@@ -170,6 +182,24 @@ int mep_to_expert_major(mep_handle *h, const void *recv_x, const float *recv_sca
                         int64_t cap_em, void *stream);
 
 /*
+ * Standard-MoE dispatch ("MORI-EP User Guide" section 4,
+ * dispatch_standard_moe(): dispatch and format conversion combined): the same
+ * em_x / em_scales / em_counts / em_offsets / em_src_pos as mep_plan +
+ * mep_dispatch + mep_to_expert_major would produce for these T tokens (rows of
+ * each expert in ascending token order, segments padded to 128 rows, padding
+ * not written), but written straight from x without the rank-major receive
+ * buffers.  A token naming one expert twice gets one row (mapped from the
+ * first position naming it).  Leaves the handle ready for
+ * mep_combine(MEP_EXPERT_MAJOR) and mep_get_route(NULL, em_row); the
+ * rank-major calls need a new mep_plan.  scales as for mep_dispatch.
+ * 0 <= T <= cap; cap_em as for mep_to_expert_major.
+ */
+int mep_dispatch_standard_moe(mep_handle *h, const int32_t *indices, int32_t T, const void *x,
+                              const float *scales, void *em_x, float *em_scales,
+                              int32_t *em_counts, int32_t *em_offsets, int32_t *em_src_pos,
+                              int64_t cap_em, void *stream);
+
+/*
  * Combine ("MORI-EP User Guide" section 3 combine(): expert outputs gathered
  * back to token order as a weighted combination; section 4
  * combine_standard_moe() for the expert-major input; "Choosing an EP API and
@@ -179,8 +209,9 @@ int mep_to_expert_major(mep_handle *h, const void *recv_x, const float *recv_sca
  * where y_j is the bf16 expert-output row holding (t, expert j):
  *   MEP_RANK_MAJOR:   y is [R,cap,H]; y_j = y[rank of expert j, slot of t];
  *                     a row shared by two experts is used once per expert;
- *   MEP_EXPERT_MAJOR: y is [cap_em,H] in the layout mep_to_expert_major
- *                     produced (needs that call after the current plan).
+ *   MEP_EXPERT_MAJOR: y is [cap_em,H] in the layout mep_to_expert_major or
+ *                     mep_dispatch_standard_moe produced (needs one of them
+ *                     after the current plan).
  * weights are token-major fp32 [T,k]; out is [T,H] bf16.  Tokens that were
  * not dispatched (bad expert id) produce +0.
  */
@@ -204,9 +235,10 @@ int mep_get_status(mep_handle *h, void *stream, int32_t *device_status);
  * Inspection of the current plan (for verification, "MORI-EP User Guide"
  * section 3 get_dispatch_src_token_pos()): copies, on `stream`, the flat
  * receive row r*cap + slot of every (token, top-k position) into
- * recv_row[T,k] (int32, -1 for tokens not dispatched), and, if em_row is not
- * NULL and mep_to_expert_major ran on this plan, the expert-major row of each
- * (token, top-k position) into em_row[T,k].
+ * recv_row[T,k] (int32, -1 for tokens not dispatched; needs a rank-major
+ * plan), and/or the expert-major row of each (token, top-k position) into
+ * em_row[T,k] (-1 where none; needs mep_to_expert_major or
+ * mep_dispatch_standard_moe).  Either pointer may be NULL, not both.
  */
 int mep_get_route(mep_handle *h, int32_t *recv_row, int32_t *em_row, void *stream);
 

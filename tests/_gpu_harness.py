@@ -78,10 +78,10 @@ def gpu_plan_dispatch(wl: Workload, inp: dict, src_rank: int = 0, fused: bool = 
     spos = torch.full((wl.ranks, wl.cap), SENT32, dtype=torch.int32, device="cuda")
     recv_x, recv_s, recv_w, recv_i = alloc_recv(wl)
     if fused:
-        M.mep_plan_dispatch(m.h, idx, T, counts, spos, x, w, recv_x, recv_s, recv_w, recv_i)
+        M.mep_plan_dispatch(m.h, idx, T, counts, spos, x, w, None, recv_x, recv_s, recv_w, recv_i)
     else:
         M.mep_plan(m.h, idx, T, counts, spos)
-        M.mep_dispatch(m.h, x, w, idx, recv_x, recv_s, recv_w, recv_i)
+        M.mep_dispatch(m.h, x, w, None, idx, recv_x, recv_s, recv_w, recv_i)
     route = torch.full((max(T, 1), wl.topk), SENT32, dtype=torch.int32, device="cuda")
     M.mep_get_route(m.h, route)
     torch.cuda.synchronize()

@@ -47,6 +47,9 @@ def cfg(**kw):
     dict(quant=M.MEP_QUANT_FP8_E4M3_BLOCK128, scale_dim=0),  # quant without scales
     dict(quant=M.MEP_QUANT_FP8_E4M3_BLOCK128, hidden_dim=7176, scale_dim=56),
     dict(quant=7),
+    dict(quant=M.MEP_QUANT_FP8_CARRY, hidden_dim=7176, scale_dim=56),  # E4M3 rows: H % 16
+    dict(quant=M.MEP_QUANT_FP8_CARRY, scale_dim=-1),
+    dict(quant=M.MEP_QUANT_FP8_CARRY, scale_dim=(1 << 16) + 1),
     dict(world_size=64, max_num_inp_token_per_rank=1 << 25),  # rows overflow int32
 ])
 def test_bad_configs_rejected(bad):
@@ -91,7 +94,7 @@ def test_call_order_and_argument_checks_before_any_launch():
     h = h.value
     f = FAKE
     # no plan yet: dispatch, expert-major conversion, combine and route inspection refuse
-    assert L.mep_dispatch(h, f, f, f, f, None, f, f, None) == M.MEP_ERR_STATE
+    assert L.mep_dispatch(h, f, f, None, f, f, None, f, f, None) == M.MEP_ERR_STATE
     assert L.mep_to_expert_major(h, f, None, f, f, f, f, None, f, f, f, 1000, None) \
         == M.MEP_ERR_STATE
     assert L.mep_combine(h, M.MEP_RANK_MAJOR, f, f, f, None) == M.MEP_ERR_STATE
@@ -111,6 +114,44 @@ def test_call_order_and_argument_checks_before_any_launch():
     assert L.mep_get_status(None, None, None) == M.MEP_ERR_NULL
     assert L.mep_destroy(h) == M.MEP_OK
     assert L.mep_destroy(None) == M.MEP_ERR_NULL
+
+
+@pytest.mark.parametrize("sd", [0, 3, 56, 1 << 16])
+def test_carry_configs_accepted(sd):
+    c = cfg(quant=M.MEP_QUANT_FP8_CARRY, scale_dim=sd)
+    h = C.c_void_p()
+    assert M.lib().mep_create(C.byref(c), FAKE, M.mep_workspace_bytes(c), C.byref(h)) == M.MEP_OK
+    M.lib().mep_destroy(h)
+
+
+def test_standard_moe_and_carry_argument_checks():
+    L = M.lib()
+    f = FAKE
+    c = cfg(quant=M.MEP_QUANT_FP8_CARRY, scale_dim=56)
+    h = C.c_void_p()
+    assert L.mep_create(C.byref(c), f, M.mep_workspace_bytes(c), C.byref(h)) == M.MEP_OK
+    h = h.value
+    sm = L.mep_dispatch_standard_moe
+    # (h, indices, T, x, scales, em_x, em_scales, em_counts, em_offsets, em_src_pos, cap_em, s)
+    assert sm(h, f, 4097, f, f, f, f, f, f, f, 1000, None) == M.MEP_ERR_SHAPE
+    assert sm(h, f, -1, f, f, f, f, f, f, f, 1000, None) == M.MEP_ERR_SHAPE
+    assert sm(h, f, 16, f, f, f, f, f, f, f, -1, None) == M.MEP_ERR_SHAPE
+    assert sm(h, f, 16, f, f, f, f, f, f, f, 1 << 31, None) == M.MEP_ERR_SHAPE
+    assert sm(h, f, 16, f, None, f, f, f, f, f, 1000, None) == M.MEP_ERR_NULL  # carried scales
+    assert sm(h, f, 16, f, f, f, None, f, f, f, 1000, None) == M.MEP_ERR_NULL
+    assert sm(h, None, 16, f, f, f, f, f, f, f, 1000, None) == M.MEP_ERR_NULL
+    assert sm(h, f, 16, None, f, f, f, f, f, f, 1000, None) == M.MEP_ERR_NULL
+    assert sm(h, f, 16, f, f, None, f, f, f, f, 1000, None) == M.MEP_ERR_NULL
+    assert sm(h, f, 16, f, f, f, f, f, f, None, 1000, None) == M.MEP_ERR_NULL
+    assert sm(h, f, 16, f, f + 4, f, f, f, f, f, 1000, None) == M.MEP_ERR_ALIGN
+    assert sm(h, f, 16, f, f, f, f, f, f + 8, f, 1000, None) == M.MEP_ERR_ALIGN
+    assert sm(None, f, 16, f, f, f, f, f, f, f, 1000, None) == M.MEP_ERR_NULL
+    # the rank-major dispatch of carried rows needs the scales too (checked
+    # before the call-order rule only once a plan exists, so here: state)
+    assert L.mep_dispatch(h, f, f, None, f, f, f, f, f, None) == M.MEP_ERR_STATE
+    assert L.mep_plan_dispatch(h, f, 16, f, f, f, f, None, f, f, f, f, None) == M.MEP_ERR_NULL
+    assert L.mep_plan_dispatch(h, f, 16, f, f, f, f, f + 4, f, f, f, f, None) == M.MEP_ERR_ALIGN
+    assert L.mep_destroy(h) == M.MEP_OK
 
 
 def test_error_strings():

@@ -147,7 +147,7 @@ def test_empty_batch():
     rx = torch.zeros((wl.ranks, wl.cap, wl.hidden), dtype=torch.int16, device="cuda")
     rw = torch.zeros((wl.ranks, wl.cap, wl.topk), dtype=torch.float32, device="cuda")
     ri = torch.zeros((wl.ranks, wl.cap, wl.topk), dtype=torch.int32, device="cuda")
-    M.mep_dispatch(m.h, None, None, None, rx, None, rw, ri)
+    M.mep_dispatch(m.h, None, None, None, None, rx, None, rw, ri)
     M.mep_combine(m.h, M.MEP_RANK_MAJOR, None, None, out)
     torch.cuda.synchronize()
     assert np.all(host(counts) == 0)
@@ -201,7 +201,7 @@ def test_reset_invalidates_plan():
     torch.cuda.synchronize()
     assert np.array_equal(host(g.counts), counts)  # caller buffers untouched
     with pytest.raises(M.MepError) as ei:
-        M.mep_dispatch(g.m.h, g.x, g.w, g.idx, g.recv_x, None, g.recv_w, g.recv_i)
+        M.mep_dispatch(g.m.h, g.x, g.w, None, g.idx, g.recv_x, None, g.recv_w, g.recv_i)
     assert ei.value.code == M.MEP_ERR_STATE
     with pytest.raises(M.MepError):
         M.mep_combine(g.m.h, M.MEP_RANK_MAJOR, g.recv_x, g.w, g.recv_x)
@@ -219,13 +219,13 @@ def test_routing_replay_and_determinism():
         x2 = torch.from_numpy(rng.standard_normal((wl.tokens, wl.hidden), dtype=np.float32)) \
             .to(torch.bfloat16).view(torch.int16)
         x2_np = x2.numpy().view(np.uint16)
-        M.mep_dispatch(g.m.h, x2.cuda(), g.w, g.idx, g.recv_x, g.recv_s, g.recv_w, g.recv_i)
+        M.mep_dispatch(g.m.h, x2.cuda(), g.w, None, g.idx, g.recv_x, g.recv_s, g.recv_w, g.recv_i)
         d = O.dispatch(x2_np, inp["weights"], inp["indices"], pl, wl.ranks, wl.experts_per_rank,
                        wl.cap, True)
         inp2 = dict(inp, x=x2_np)
         check_plan_dispatch(wl, inp2, g, pl, d)
     first = host(g.recv_x).copy()
-    M.mep_dispatch(g.m.h, x2.cuda(), g.w, g.idx, g.recv_x, g.recv_s, g.recv_w, g.recv_i)
+    M.mep_dispatch(g.m.h, x2.cuda(), g.w, None, g.idx, g.recv_x, g.recv_s, g.recv_w, g.recv_i)
     assert np.array_equal(first, host(g.recv_x))
 
 
@@ -325,7 +325,7 @@ def test_hip_graph_capture_replay(T):
     out = torch.zeros((T, H), dtype=torch.int16, device="cuda")
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        M.mep_plan_dispatch(g.m.h, g.idx, T, g.counts, g.spos, g.x, g.w, g.recv_x, g.recv_s,
+        M.mep_plan_dispatch(g.m.h, g.idx, T, g.counts, g.spos, g.x, g.w, None, g.recv_x, g.recv_s,
                             g.recv_w, g.recv_i)
         M.mep_combine(g.m.h, M.MEP_RANK_MAJOR, y, g.w, out)
     for rep in range(4):

@@ -1,0 +1,331 @@
+"""GPU parity of the standard-MoE dispatch and of already-quantized FP8 payloads.
+
+mep_dispatch_standard_moe writes the expert-major layout straight from the
+token rows; its oracle is plan -> dispatch -> expert-major conversion run one
+after the other ("MORI-EP User Guide" section 4: dispatch_standard_moe() is
+dispatch and convert_dispatch_output() in one call).  The carry mode moves
+rows that arrive as E4M3 bytes with the caller's scale rows ("Choosing an EP
+API and backend": the HIP backend carries already-quantized FP8 payloads).
+
+Bar: bit-exact for the layout, rows, scales, source positions, counts,
+offsets, route and status; combine within 1 bf16 ulp.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import combine_mep_plan_amd as M
+from oracle import oracle as O
+from synthetic import WORKLOADS, make_fp8_payload, make_inputs
+
+from _gpu_harness import (SENT8, SENT16, SENT32, check_combine, dev, host)
+
+pytestmark = pytest.mark.gpu
+
+QUANT = {"bf16": M.MEP_QUANT_NONE, "fp8": M.MEP_QUANT_FP8_E4M3_BLOCK128,
+         "carry": M.MEP_QUANT_FP8_CARRY}
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _wl(name, T, **kw):
+    wl = WORKLOADS[name].with_tokens(T)
+    return dataclasses.replace(wl, **kw) if kw else wl
+
+
+def _inputs(wl, seed, mode, sd):
+    """Token rows for the mode: bf16 bits (bf16, fp8) or E4M3 bytes + scales."""
+    inp = make_inputs(wl, seed)
+    if mode == "carry":
+        p = make_fp8_payload(wl.tokens, wl.hidden, sd, seed)
+        inp["x"], inp["scales"] = p["q"], p["scales"]
+    else:
+        inp["scales"] = None
+    return inp
+
+
+def _scale_cols(wl, mode, sd):
+    return {"bf16": 0, "fp8": wl.hidden // 128, "carry": sd}[mode]
+
+
+class StdRun:
+    """One mep_dispatch_standard_moe call on fresh sentinel-filled buffers."""
+
+    def __init__(self, wl, inp, mode, sd=0, cap_em=None, src_rank=0, T=None, m=None):
+        self.wl, self.mode = wl, mode
+        T = wl.tokens if T is None else T
+        self.T = T
+        H, E, k = wl.hidden, wl.experts, wl.topk
+        self.nb = _scale_cols(wl, mode, sd)
+        self.cap_em = wl.cap_em if cap_em is None else cap_em
+        self.m = m or M.Mep(H, wl.experts_per_rank, k, wl.cap, wl.ranks, rank=src_rank,
+                            quant=QUANT[mode], scale_dim=self.nb)
+        byte_rows = mode != "bf16"
+        ce = self.cap_em
+        self.em_x = torch.full((max(ce, 1), H), SENT8 if byte_rows else SENT16 - 0x10000,
+                               dtype=torch.uint8 if byte_rows else torch.int16, device="cuda")
+        self.em_s = (torch.full((max(ce, 1), self.nb), float("nan"), device="cuda")
+                     if self.nb else None)
+        self.em_counts = torch.full((E,), SENT32, dtype=torch.int32, device="cuda")
+        self.em_offsets = torch.full((E + 1,), SENT32, dtype=torch.int32, device="cuda")
+        self.em_src = torch.full((max(ce, 1),), SENT32, dtype=torch.int32, device="cuda")
+        self.x = dev(inp["x"][:T]) if T else None
+        self.idx = dev(inp["indices"][:T]) if T else None
+        self.w = dev(inp["weights"][:T]) if T else None
+        self.sc = dev(inp["scales"][:T]) if (T and inp["scales"] is not None and self.nb) else None
+        self.call()
+
+    def call(self):
+        M.mep_dispatch_standard_moe(self.m.h, self.idx, self.T, self.x, self.sc, self.em_x,
+                                    self.em_s, self.em_counts, self.em_offsets, self.em_src,
+                                    self.cap_em)
+
+    def route(self):
+        r = torch.full((max(self.T, 1), self.wl.topk), SENT32, dtype=torch.int32, device="cuda")
+        M.mep_get_route(self.m.h, None, r)
+        return host(r)[:self.T]
+
+
+def _oracle(wl, inp, mode, cap_em, src_rank=0, T=None):
+    T = wl.tokens if T is None else T
+    q = {"bf16": 0, "fp8": 1, "carry": 2}[mode]
+    sc = inp["scales"][:T] if inp["scales"] is not None else None
+    return O.dispatch_standard_moe(inp["x"][:T], inp["weights"][:T], inp["indices"][:T],
+                                   wl.ranks, wl.experts_per_rank, wl.cap, q, cap_em,
+                                   src_rank, scales=sc)
+
+
+def _check(g: StdRun, em: dict):
+    wl = g.wl
+    assert np.array_equal(host(g.em_counts), em["em_counts"])
+    offs = host(g.em_offsets)
+    assert np.array_equal(offs, em["em_offsets"])
+    used = np.zeros(g.cap_em, bool)
+    for e in range(wl.experts):
+        o, n = offs[e], em["em_counts"][e]
+        used[o:min(o + n, g.cap_em)] = True
+    byte_rows = g.mode != "bf16"
+    ex = host(g.em_x, np.uint8 if byte_rows else np.uint16)[:g.cap_em]
+    assert np.array_equal(ex[used], em["em_x"][used]), "expert-major rows differ"
+    assert np.all(ex[~used] == (SENT8 if byte_rows else SENT16)), "padding rows written"
+    if g.nb:
+        es = host(g.em_s)[:g.cap_em]
+        assert np.array_equal(es[used].view(np.uint32), em["em_scales"][used].view(np.uint32))
+        assert np.all(np.isnan(es[~used])), "padding scales written"
+    src = host(g.em_src)[:g.cap_em]
+    assert np.array_equal(src[used], em["em_src_pos"][used])
+    assert np.all(src[~used] == SENT32)
+    assert np.array_equal(g.route(), em["tok_em_row"])
+    assert M.mep_get_status(g.m.h) == em["status"]
+    return int(used.sum())
+
+
+def _stand_in(mode, rows_gpu, scales_np, rows_np):
+    """Expert outputs from the oracle's rows: identity for bf16 rows;
+    bf16(decode(q) * scale) for E4M3 rows with one scale per 128 columns, unit
+    scales for carried rows whose scale columns are laid out otherwise."""
+    if mode == "bf16":
+        return rows_gpu, rows_np
+    H = rows_np.shape[1]
+    if scales_np is None or scales_np.shape[1] != H // 128:
+        scales_np = np.ones((rows_np.shape[0], H // 128), np.float32)
+    y_np = O.expert_dequant(rows_np, scales_np, 1.0)
+    return dev(y_np), y_np
+
+
+# ---------------------------------------------------------------------------
+
+CASES = [
+    # (label, workload, T, mode, scale cols for carry)
+    ("stdmoe-1-fp8", "stdmoe", 1, "fp8", 0),
+    ("stdmoe-63-fp8", "stdmoe", 63, "fp8", 0),
+    ("stdmoe-300-fp8", "stdmoe", 300, "fp8", 0),
+    ("stdmoe-1000-bf16", "stdmoe", 1000, "bf16", 0),
+    ("stdmoe-700-carry56", "stdmoe", 700, "carry", 56),
+    ("stdmoe-257-carry3", "stdmoe", 257, "carry", 3),
+    ("stdmoe-200-carry0", "stdmoe", 200, "carry", 0),
+    ("skew-1500-fp8", "skew", 1500, "fp8", 0),
+    ("tiny-16-bf16", "tiny", 16, "bf16", 0),
+    ("stdmoe-4096-fp8", "stdmoe", 4096, "fp8", 0),
+    ("stdmoe-4096-carry56", "stdmoe", 4096, "carry", 56),
+]
+
+
+@pytest.mark.parametrize("label,name,T,mode,sd", CASES, ids=[c[0] for c in CASES])
+def test_standard_moe_matches_oracle(label, name, T, mode, sd):
+    wl = _wl(name, T)
+    _say(f"[std] {label}")
+    inp = _inputs(wl, 3, mode, sd)
+    g = StdRun(wl, inp, mode, sd)
+    em = _oracle(wl, inp, mode, g.cap_em)
+    rows = _check(g, em)
+    # combine from the expert-major rows this call wrote
+    y_gpu, y_np = _stand_in(mode, g.em_x, em["em_scales"], em["em_x"])
+    out = torch.empty((T, wl.hidden), dtype=torch.int16, device="cuda")
+    M.mep_combine(g.m.h, M.MEP_EXPERT_MAJOR, y_gpu, g.w, out)
+    ref = O.combine_em(y_np, inp["weights"], em["tok_em_row"])
+    torch.cuda.synchronize()
+    stats = check_combine(host(out, np.uint16), ref)
+    _say(f"[std] {label}: rows {rows}, combine {stats}")
+
+
+@pytest.mark.parametrize("R,epr,k,T", [(64, 64, 8, 2000), (7, 13, 5, 3000), (4, 1, 1, 1500),
+                                        (2, 3, 6, 130)])
+def test_standard_moe_expert_counts(R, epr, k, T):
+    # expert counts that split the per-expert prefix work differently: 4096
+    # experts (one work item each), 91 (eight items per expert), top-1, all
+    # experts named by every token
+    wl = _wl("stdmoe", T, ranks=R, experts_per_rank=epr, topk=k, hidden=256)
+    _say(f"[std] R={R} epr={epr} k={k} T={T}")
+    inp = _inputs(wl, 12, "fp8", 0)
+    g = StdRun(wl, inp, "fp8")
+    em = _oracle(wl, inp, "fp8", g.cap_em)
+    _check(g, em)
+    y_gpu, y_np = _stand_in("fp8", g.em_x, em["em_scales"], em["em_x"])
+    out = torch.empty((T, wl.hidden), dtype=torch.int16, device="cuda")
+    M.mep_combine(g.m.h, M.MEP_EXPERT_MAJOR, y_gpu, g.w, out)
+    ref = O.combine_em(y_np, inp["weights"], em["tok_em_row"])
+    torch.cuda.synchronize()
+    check_combine(host(out, np.uint16), ref)
+
+
+def test_standard_moe_src_rank_and_repeat_calls():
+    # src_token_pos offset of a non-zero source rank; a second call on the same
+    # handle with fewer tokens rewrites counts and offsets from scratch
+    wl = _wl("stdmoe", 600)
+    inp = _inputs(wl, 11, "fp8", 0)
+    g = StdRun(wl, inp, "fp8", src_rank=5)
+    _check(g, _oracle(wl, inp, "fp8", g.cap_em, src_rank=5))
+    g2 = StdRun(wl, inp, "fp8", src_rank=5, T=130, m=g.m)  # same handle, fresh buffers
+    _check(g2, _oracle(wl, inp, "fp8", g2.cap_em, src_rank=5, T=130))
+
+
+def test_standard_moe_empty_batch():
+    wl = _wl("stdmoe", 0)
+    inp = {"x": np.zeros((0, wl.hidden), np.uint16), "indices": np.zeros((0, wl.topk), np.int32),
+           "weights": np.zeros((0, wl.topk), np.float32), "scales": None}
+    g = StdRun(wl, inp, "fp8", T=0)
+    torch.cuda.synchronize()
+    assert np.all(host(g.em_counts) == 0)
+    assert np.all(host(g.em_offsets) == 0)
+    assert np.all(host(g.em_src) == SENT32)
+    assert M.mep_get_status(g.m.h) == 0
+    out = torch.empty((1, wl.hidden), dtype=torch.int16, device="cuda")
+    M.mep_combine(g.m.h, M.MEP_EXPERT_MAJOR, g.em_x, None, out)  # T = 0: nothing to do
+
+
+@pytest.mark.parametrize("T", [16, 700])
+def test_standard_moe_bad_and_repeated_ids(T):
+    wl = _wl("stdmoe", T)
+    inp = _inputs(wl, 7, "fp8", 0)
+    idx = inp["indices"]
+    idx[3, 2] = wl.experts          # out of range
+    idx[5, 0] = -4                  # negative
+    idx[9, 1] = idx[9, 6]           # one expert named twice
+    if T > 64:
+        idx[70, 7] = idx[70, 0]     # in the next chunk
+        idx[T - 1, 3] = 1 << 30
+    g = StdRun(wl, inp, "fp8")
+    em = _oracle(wl, inp, "fp8", g.cap_em)
+    assert em["status"] == O.ST_BAD_INDEX | O.ST_DUP_EXPERT
+    _check(g, em)
+    y_gpu, y_np = _stand_in("fp8", g.em_x, em["em_scales"], em["em_x"])
+    out = torch.empty((T, wl.hidden), dtype=torch.int16, device="cuda")
+    M.mep_combine(g.m.h, M.MEP_EXPERT_MAJOR, y_gpu, g.w, out)
+    ref = O.combine_em(y_np, inp["weights"], em["tok_em_row"])
+    torch.cuda.synchronize()
+    check_combine(host(out, np.uint16), ref)
+
+
+def test_standard_moe_overflow_sets_status():
+    wl = _wl("stdmoe", 256)
+    inp = _inputs(wl, 2, "fp8", 0)
+    g = StdRun(wl, inp, "fp8", cap_em=1000)
+    em = _oracle(wl, inp, "fp8", 1000)
+    assert em["status"] == O.ST_EM_OVERFLOW
+    _check(g, em)
+
+
+def test_standard_moe_state_rules():
+    wl = _wl("stdmoe", 128)
+    inp = _inputs(wl, 4, "fp8", 0)
+    g = StdRun(wl, inp, "fp8")
+    r = torch.empty((wl.tokens, wl.topk), dtype=torch.int32, device="cuda")
+    with pytest.raises(M.MepError) as e:
+        M.mep_get_route(g.m.h, r, None)  # no rank-major plan after the standard call
+    assert e.value.code == M.MEP_ERR_STATE
+    out = torch.empty((wl.tokens, wl.hidden), dtype=torch.int16, device="cuda")
+    with pytest.raises(M.MepError) as e:
+        M.mep_combine(g.m.h, M.MEP_RANK_MAJOR, g.em_x, g.w, out)
+    assert e.value.code == M.MEP_ERR_STATE
+    M.mep_reset(g.m.h)
+    with pytest.raises(M.MepError) as e:
+        M.mep_combine(g.m.h, M.MEP_EXPERT_MAJOR, g.em_x, g.w, out)
+    assert e.value.code == M.MEP_ERR_STATE
+    with pytest.raises(M.MepError) as e:  # more tokens than the handle's capacity
+        M.mep_dispatch_standard_moe(g.m.h, g.idx, wl.cap + 1, g.x, None, g.em_x, g.em_s,
+                                    g.em_counts, g.em_offsets, g.em_src, g.cap_em)
+    assert e.value.code == M.MEP_ERR_SHAPE
+
+
+# ---------------------------------------------------------------------------
+# carry mode through the rank-major dispatch
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+@pytest.mark.parametrize("T,sd", [(100, 5), (700, 56), (4096, 56)])
+def test_carry_rank_major_dispatch(T, sd, fused):
+    wl = _wl("prefill", T)
+    _say(f"[carry] T={T} sd={sd} fused={fused}")
+    inp = _inputs(wl, 9, "carry", sd)
+    R, cap, H, k, epr = wl.ranks, wl.cap, wl.hidden, wl.topk, wl.experts_per_rank
+    m = M.Mep(H, epr, k, cap, R, quant=M.MEP_QUANT_FP8_CARRY, scale_dim=sd)
+    x, w, idx, sc = dev(inp["x"]), dev(inp["weights"]), dev(inp["indices"]), dev(inp["scales"])
+    counts = torch.full((R,), SENT32, dtype=torch.int32, device="cuda")
+    spos = torch.full((R, cap), SENT32, dtype=torch.int32, device="cuda")
+    rx = torch.full((R, cap, H), SENT8, dtype=torch.uint8, device="cuda")
+    rs = torch.full((R, cap, sd), float("nan"), device="cuda")
+    rw = torch.full((R, cap, k), float("nan"), device="cuda")
+    ri = torch.full((R, cap, k), SENT32, dtype=torch.int32, device="cuda")
+    if fused:
+        M.mep_plan_dispatch(m.h, idx, T, counts, spos, x, w, sc, rx, rs, rw, ri)
+    else:
+        M.mep_plan(m.h, idx, T, counts, spos)
+        M.mep_dispatch(m.h, x, w, sc, idx, rx, rs, rw, ri)
+    pl = O.plan(inp["indices"], R, epr, cap)
+    d = O.dispatch(inp["x"], inp["weights"], inp["indices"], pl, R, epr, cap, 2,
+                   fill=SENT8, scales=inp["scales"])
+    torch.cuda.synchronize()
+    assert np.array_equal(host(counts), pl["recv_counts"])
+    written = np.arange(cap)[None, :] < pl["recv_counts"][:, None]
+    assert np.array_equal(host(spos)[written], pl["src_token_pos"][written])
+    assert np.array_equal(host(rx), d["recv_x"])
+    hs = host(rs)
+    assert np.array_equal(hs[written].view(np.uint32), d["recv_scales"][written].view(np.uint32))
+    assert np.all(np.isnan(hs[~written]))
+    assert np.array_equal(host(rw)[written].view(np.uint32),
+                          d["recv_weights"][written].view(np.uint32))
+    assert np.array_equal(host(ri)[written], d["recv_indices"][written])
+    assert M.mep_get_status(m.h) == 0
+    # the carried rows also convert to expert-major with their scale rows
+    ce = wl.cap_em
+    emx = torch.full((ce, H), SENT8, dtype=torch.uint8, device="cuda")
+    ems = torch.full((ce, sd), float("nan"), device="cuda")
+    emc = torch.empty(wl.experts, dtype=torch.int32, device="cuda")
+    emo = torch.empty(wl.experts + 1, dtype=torch.int32, device="cuda")
+    emp = torch.full((ce,), SENT32, dtype=torch.int32, device="cuda")
+    M.mep_to_expert_major(m.h, rx, rs, ri, counts, spos, emx, ems, emc, emo, emp, ce)
+    em = O.to_expert_major(d, pl, R, epr, cap, T, ce, fill=SENT8)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(emc), em["em_counts"])
+    assert np.array_equal(host(emx), em["em_x"])
+    offs, cnt = em["em_offsets"], em["em_counts"]
+    used = np.zeros(ce, bool)
+    for e in range(wl.experts):
+        used[offs[e]:offs[e] + cnt[e]] = True
+    assert np.array_equal(host(ems)[used].view(np.uint32), em["em_scales"][used].view(np.uint32))
