@@ -52,6 +52,20 @@
  *      dispatch and convert_dispatch_output() in one call) produces exactly
  *      what the two steps produce one after the other; it is not a function
  *      of its own here.
+ *   R11 FP4 payloads ([Backends]: FP4 conversion kernels on gfx950; the
+ *      block format is not given): OCP Microscaling MXFP4 -- blocks of 32
+ *      columns, E2M1 elements, one E8M0 scale per block.  Per the OCP MX
+ *      conversion: shared exponent = floor(log2(amax)) - 2 (2 = the largest
+ *      E2M1 exponent), clamped to [-127, 127]; scale byte = exponent + 127;
+ *      element = E2M1(x / 2^exponent), round to nearest, ties to the even
+ *      code, saturating at 6, sign kept; an all-zero block gets scale byte 0.
+ *      Two elements per byte, the even column in the low nibble; the H/32
+ *      scale bytes of a row fill H/128 32-bit scale words.  A carried FP4
+ *      payload is H/2 bytes per row with the caller's scale words.
+ *   R12 FP8 direct-cast combine payload ([Backends]/tuning matrix: quant type
+ *      fp8_direct_cast with a bf16 combine): each expert-output value is cast
+ *      to OCP E4M3 with no scale (round to nearest even, saturating at 448);
+ *      the combine accumulates the decoded values exactly as R6.
  */
 #include <math.h>
 #include <stdint.h>
@@ -206,8 +220,83 @@ int32_t oracle_plan(const int32_t *idx, int32_t T, int32_t k, int32_t R, int32_t
 /*             into recv_x [R,cap,H] bytes and recv_scales [R,cap,sd]        */
 /*             ([Backends]: the HIP backend carries already-quantized FP8    */
 /*             payloads; reading R9).                                        */
+/* quant == 3: as 2 for FP4 rows of H/2 bytes (reading R11).                 */
+/* quant == 4: x [T,H] bf16 bits quantised to MXFP4: recv_x [R,cap,H/2]      */
+/*             bytes, recv_scales [R,cap,H/128] words of E8M0 bytes (R11).   */
 /* recv_w [R,cap,k] f32, recv_idx [R,cap,k] i32.  Only written rows change.  */
 /* ------------------------------------------------------------------------ */
+
+/* ------------------------------------------------------------------------ */
+/* E2M1, the OCP MX FP4 element: sign, 2 exponent bits (bias 1), 1 mantissa */
+/* bit; no inf or NaN.  Code bits 0..2 give the magnitudes 0, 0.5, 1, 1.5,  */
+/* 2, 3, 4, 6; bit 3 is the sign.                                            */
+/* ------------------------------------------------------------------------ */
+double oracle_e2m1_decode(uint8_t c) {
+  int e = (c >> 1) & 3, m = c & 1;
+  double mag = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return (c & 8) ? -mag : mag;
+}
+
+/* Nearest E2M1 code of v (a double), ties to the even code, saturating at 6;
+ * the sign is kept, zero included. */
+uint8_t oracle_e2m1_encode(double v) {
+  uint8_t sign = signbit(v) ? 8 : 0;
+  double a = fabs(v);
+  int c = 0;
+  while (c < 7 && oracle_e2m1_decode((uint8_t)c) < a) c++;
+  if (c > 0 && oracle_e2m1_decode((uint8_t)c) >= a) {
+    double lo = oracle_e2m1_decode((uint8_t)(c - 1)), hi = oracle_e2m1_decode((uint8_t)c);
+    double mid = 0.5 * (lo + hi);
+    if (a < mid) c = c - 1;
+    else if (a == mid && (c & 1)) c = c - 1;
+  }
+  return (uint8_t)(sign | c);
+}
+
+/* R11 for one token row: q[H/2] packed codes, e8[H/32] scale bytes. */
+void oracle_mx4_quant_row(const uint16_t *x, int32_t H, uint8_t *q, uint8_t *e8) {
+  for (int32_t b = 0; b < H / 32; b++) {
+    double amax = 0.0;
+    for (int32_t i = 0; i < 32; i++) {
+      double v = fabs((double)oracle_bf16_to_f32(x[b * 32 + i]));
+      if (v > amax) amax = v;
+    }
+    int se = -127;
+    if (amax > 0.0) {
+      int ex;
+      frexp(amax, &ex); /* amax = m * 2^ex, m in [0.5, 1): floor(log2(amax)) = ex - 1 */
+      se = ex - 1 - 2;
+      if (se < -127) se = -127;
+      if (se > 127) se = 127;
+    }
+    e8[b] = (uint8_t)(se + 127);
+    for (int32_t i = 0; i < 32; i += 2) {
+      uint8_t c0, c1;
+      double v0 = oracle_bf16_to_f32(x[b * 32 + i]), v1 = oracle_bf16_to_f32(x[b * 32 + i + 1]);
+      if (amax == 0.0) {
+        c0 = signbit(v0) ? 8 : 0;
+        c1 = signbit(v1) ? 8 : 0;
+      } else {
+        c0 = oracle_e2m1_encode(ldexp(v0, -se));
+        c1 = oracle_e2m1_encode(ldexp(v1, -se));
+      }
+      q[(b * 32 + i) / 2] = (uint8_t)(c0 | (c1 << 4));
+    }
+  }
+}
+
+/* R11 decoding of one packed row: out[H] as doubles. */
+void oracle_mx4_decode_row(const uint8_t *q, const uint8_t *e8, int32_t H, double *out) {
+  for (int32_t i = 0; i < H; i++) {
+    uint8_t c = (q[i / 2] >> ((i & 1) * 4)) & 0xF;
+    out[i] = ldexp(oracle_e2m1_decode(c), (int)e8[i / 32] - 127);
+  }
+}
+
+/* R12: E4M3 direct cast (no scale) of n bf16 values. */
+void oracle_cast_fp8_direct(const uint16_t *y, int64_t n, uint8_t *y8) {
+  for (int64_t i = 0; i < n; i++) y8[i] = oracle_e4m3_encode(oracle_bf16_to_f32(y[i]));
+}
 
 /* R5 for one token row: fills q[H] and scale[H/128]. */
 void oracle_quant_row(const uint16_t *x, int32_t H, uint8_t *q, float *scale) {
@@ -231,8 +320,10 @@ void oracle_dispatch(const void *x, const float *xs, int32_t sd, const float *w,
                      const int32_t *idx, const int32_t *slot, int32_t T, int32_t H, int32_t k,
                      int32_t R, int32_t epr, int32_t cap, int32_t quant, void *recv_x,
                      float *recv_scales, float *recv_w, int32_t *recv_idx,
-                     uint8_t *q_tmp /* [H] */, float *s_tmp /* [H/128] */) {
-  int32_t nb = quant == 1 ? H / 128 : sd;
+                     uint8_t *q_tmp /* [H] */, float *s_tmp /* [scale words] */) {
+  /* bytes per received row, 32-bit scale words per row */
+  int64_t rowb = quant == 0 ? 2 * (int64_t)H : (quant >= 3 ? H / 2 : H);
+  int32_t nb = (quant == 1 || quant == 4) ? H / 128 : (quant == 0 ? 0 : sd);
   (void)R;
   for (int32_t t = 0; t < T; t++) {
     const int32_t *e = idx + (int64_t)t * k;
@@ -241,9 +332,11 @@ void oracle_dispatch(const void *x, const float *xs, int32_t sd, const float *w,
     const uint16_t *xr = (const uint16_t *)x + (int64_t)t * H;
     if (quant == 1) {
       oracle_quant_row(xr, H, q_tmp, s_tmp);
-    } else if (quant == 2) {
-      memcpy(q_tmp, (const uint8_t *)x + (int64_t)t * H, (size_t)H);
+    } else if (quant == 2 || quant == 3) {
+      memcpy(q_tmp, (const uint8_t *)x + (int64_t)t * rowb, (size_t)rowb);
       if (sd > 0) memcpy(s_tmp, xs + (int64_t)t * sd, sizeof(float) * (size_t)sd);
+    } else if (quant == 4) {
+      oracle_mx4_quant_row(xr, H, q_tmp, (uint8_t *)s_tmp);
     }
     for (int32_t j = 0; j < k; j++) {
       int32_t r = e[j] / epr;
@@ -253,7 +346,7 @@ void oracle_dispatch(const void *x, const float *xs, int32_t sd, const float *w,
       if (!first) continue; /* R2: one row per destination rank */
       int64_t row = (int64_t)r * cap + sl[j];
       if (quant) {
-        memcpy((uint8_t *)recv_x + row * H, q_tmp, (size_t)H);
+        memcpy((uint8_t *)recv_x + row * rowb, q_tmp, (size_t)rowb);
         if (nb > 0) memcpy(recv_scales + row * nb, s_tmp, sizeof(float) * (size_t)nb);
       } else {
         memcpy((uint16_t *)recv_x + row * H, xr, sizeof(uint16_t) * (size_t)H);

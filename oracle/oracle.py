@@ -57,6 +57,11 @@ def lib():
         L.oracle_plan.argtypes = [p, i32, i32, i32, i32, i32, i32, p, p, p]
         L.oracle_plan.restype = i32
         L.oracle_quant_row.argtypes = [p, i32, p, p]
+        L.oracle_e2m1_decode.argtypes, L.oracle_e2m1_decode.restype = [C.c_uint8], C.c_double
+        L.oracle_e2m1_encode.argtypes, L.oracle_e2m1_encode.restype = [C.c_double], C.c_uint8
+        L.oracle_mx4_quant_row.argtypes = [p, i32, p, p]
+        L.oracle_mx4_decode_row.argtypes = [p, p, i32, p]
+        L.oracle_cast_fp8_direct.argtypes = [p, i64, p]
         L.oracle_dispatch.argtypes = [p, p, i32, p, p, p, i32, i32, i32, i32, i32, i32, i32,
                                       p, p, p, p, p, p]
         L.oracle_combine.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, p]
@@ -107,6 +112,51 @@ def quant_row(x_row: np.ndarray):
     return q, s
 
 
+def e2m1_decode_table() -> np.ndarray:
+    return np.array([lib().oracle_e2m1_decode(c) for c in range(16)], dtype=np.float64)
+
+
+def e2m1_encode(v: float) -> int:
+    return int(lib().oracle_e2m1_encode(float(v)))
+
+
+def mx4_quant_row(x_row: np.ndarray):
+    """Reading R11 for one bf16 row: (packed codes [H/2] uint8, scale bytes [H/32])."""
+    x_row = np.ascontiguousarray(x_row, dtype=np.uint16)
+    H = x_row.shape[0]
+    q = np.empty(H // 2, dtype=np.uint8)
+    e8 = np.empty(H // 32, dtype=np.uint8)
+    lib().oracle_mx4_quant_row(_p(x_row), H, _p(q), _p(e8))
+    return q, e8
+
+
+def mx4_decode_row(q: np.ndarray, e8: np.ndarray) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    e8 = np.ascontiguousarray(e8, dtype=np.uint8)
+    H = 2 * q.shape[0]
+    out = np.empty(H, dtype=np.float64)
+    lib().oracle_mx4_decode_row(_p(q), _p(e8), H, _p(out))
+    return out
+
+
+def cast_fp8_direct(y_bits: np.ndarray) -> np.ndarray:
+    """Reading R12: E4M3 codes of bf16 values, no scale."""
+    y = np.ascontiguousarray(y_bits, dtype=np.uint16)
+    out = np.empty(y.shape, dtype=np.uint8)
+    lib().oracle_cast_fp8_direct(_p(y), y.size, _p(out))
+    return out
+
+
+def e4m3_to_bf16(codes: np.ndarray) -> np.ndarray:
+    """bf16 bits of E4M3 values (every E4M3 value is a bf16 value, so this is
+    exact); lets the combine run on direct-cast rows."""
+    tab = e4m3_decode_table().astype(np.float32)
+    f = np.ascontiguousarray(tab[np.asarray(codes, dtype=np.uint8)])
+    out = np.empty(f.shape, dtype=np.uint16)
+    lib().oracle_bf16_rne_array(_p(f), f.size, _p(out))
+    return out
+
+
 # --- the path -----------------------------------------------------------------
 
 def plan(indices: np.ndarray, R: int, epr: int, cap: int, src_rank: int = 0) -> dict:
@@ -121,26 +171,30 @@ def plan(indices: np.ndarray, R: int, epr: int, cap: int, src_rank: int = 0) -> 
 
 def dispatch(x: np.ndarray, weights: np.ndarray, indices: np.ndarray, pl: dict, R: int,
              epr: int, cap: int, quant, fill: int = 0, scales: np.ndarray | None = None) -> dict:
-    """quant: 0/False bf16 copy, 1/True block quantisation, 2 carry (x holds
-    E4M3 bytes [T,H], scales [T,sd] fp32).  Returns recv_x ([R,cap,H] uint16
-    bf16 bits, or uint8 E4M3 codes), recv_scales ([R,cap,nb] or None),
-    recv_weights, recv_indices.  Unwritten rows keep ``fill`` (bytes) so callers
-    can see which rows were written."""
+    """quant: 0/False bf16 copy, 1/True FP8 block quantisation, 2 FP8 carry (x
+    holds E4M3 bytes [T,H], scales [T,sd] 32-bit words), 3 FP4 carry (x holds
+    packed E2M1 bytes [T,H/2], scales [T,sd]), 4 MXFP4 quantisation (reading
+    R11).  Returns recv_x ([R,cap,H] uint16 bf16 bits, [R,cap,H] uint8 E4M3
+    codes, or [R,cap,H/2] uint8 packed E2M1), recv_scales ([R,cap,nb] float32
+    words, or None), recv_weights, recv_indices.  Unwritten rows keep ``fill``
+    (bytes) so callers can see which rows were written."""
     quant = int(quant)
-    x = np.ascontiguousarray(x, dtype=np.uint8 if quant == 2 else np.uint16)
+    x = np.ascontiguousarray(x, dtype=np.uint8 if quant in (2, 3) else np.uint16)
     w = np.ascontiguousarray(weights, dtype=np.float32)
     idx = np.ascontiguousarray(indices, dtype=np.int32)
     T, H = x.shape
+    if quant == 3:
+        H *= 2  # two E2M1 codes per byte
     k = idx.shape[1]
-    if quant == 2:
+    if quant in (2, 3):
         xs = np.ascontiguousarray(scales if scales is not None else np.zeros((T, 0)),
                                   dtype=np.float32)
         nb = xs.shape[1]
     else:
         xs = np.zeros(1, dtype=np.float32)
-        nb = H // 128 if quant == 1 else 0
+        nb = H // 128 if quant in (1, 4) else 0
     if quant:
-        rx = np.full((R, cap, H), fill, dtype=np.uint8)
+        rx = np.full((R, cap, H // 2 if quant >= 3 else H), fill, dtype=np.uint8)
         rs = np.zeros((R, cap, max(nb, 1)), dtype=np.float32)
     else:
         rx = np.full((R, cap, H), fill * 0x0101, dtype=np.uint16)
@@ -148,7 +202,7 @@ def dispatch(x: np.ndarray, weights: np.ndarray, indices: np.ndarray, pl: dict, 
     rw = np.zeros((R, cap, k), dtype=np.float32)
     ri = np.full((R, cap, k), -1, dtype=np.int32)
     qt = np.empty(H, dtype=np.uint8)
-    st = np.empty(max(nb, 1), dtype=np.float32)
+    st = np.empty(max(nb, H // 128, 1), dtype=np.float32)
     lib().oracle_dispatch(_p(x), _p(xs), nb, _p(w), _p(idx), _p(pl["slot"]), T, H, k, R, epr,
                           cap, quant, _p(rx), _p(rs), _p(rw), _p(ri), _p(qt), _p(st))
     return {"recv_x": rx, "recv_scales": rs if nb else None, "recv_weights": rw,

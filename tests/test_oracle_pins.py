@@ -11,6 +11,8 @@ on gfx950), ROCm/mori issue #57 (redundant transfer removed).
 
 import os
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -558,3 +560,146 @@ def test_standard_moe_by_brute_force(oracle):
         for j in range(k):
             first = t in valid and idx[t, j] not in idx[t, :j]
             assert (em["tok_em_row"][t, j] >= 0) == first
+
+
+# ----------------------------------------------------------------------------
+# FP4 (OCP MX: E2M1 elements, E8M0 block scales) and the FP8 direct cast
+# ----------------------------------------------------------------------------
+
+E2M1_MAGNITUDES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]  # OCP MX spec, FP4 E2M1
+
+
+def test_e2m1_decode_table(oracle):
+    tab = oracle.e2m1_decode_table()
+    assert list(tab[:8]) == E2M1_MAGNITUDES
+    assert list(tab[8:]) == [-m for m in E2M1_MAGNITUDES]
+    assert np.signbit(tab[8])
+
+
+def _e2m1_nearest(v):
+    # brute force: the closest magnitude; on a tie the even code; sign kept
+    mags = np.array(E2M1_MAGNITUDES)
+    a = min(abs(v), 6.0)
+    d = np.abs(mags - a)
+    best = np.flatnonzero(d == d.min())
+    c = int(best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0])
+    return c | (8 if np.signbit(v) else 0)
+
+
+def test_e2m1_encode_matches_brute_force(oracle):
+    grid = np.arange(-8 * 64, 8 * 64 + 1) / 64.0  # every midpoint lies on this grid
+    rng = np.random.default_rng(3)
+    vals = np.concatenate([grid, rng.standard_normal(2000) * 3, [-0.0, 1e-30, -1e-30, 7.9, 100.0]])
+    for v in vals:
+        assert oracle.e2m1_encode(v) == _e2m1_nearest(v), v
+
+
+def _bf16_of(v64):
+    return torch_bf16(np.asarray(v64, dtype=np.float32))
+
+
+def test_mx4_exact_blocks_round_trip(oracle):
+    # Blocks built from E2M1 codes times 2^s, with a largest magnitude of 4 or 6,
+    # quantise back to the same codes and to scale byte s + 127.
+    rng = np.random.default_rng(17)
+    H = 32 * 24
+    codes = rng.integers(0, 16, H).astype(np.uint8)
+    s = rng.integers(-100, 100, H // 32)
+    for b in range(H // 32):
+        codes[b * 32 + rng.integers(0, 32)] = rng.choice([6, 7, 14, 15])
+    vals = np.array([oracle.e2m1_decode_table()[c] for c in codes]) * np.repeat(2.0 ** s, 32)
+    x = _bf16_of(vals)
+    assert np.array_equal(bf16_f32(x).astype(np.float64), vals)  # exact in bf16
+    q, e8 = oracle.mx4_quant_row(x)
+    assert np.array_equal(e8, (s + 127).astype(np.uint8))
+    lo, hi = q & 0xF, q >> 4
+    # a code of 8 (negative zero) decodes like 0: compare values, then signs
+    assert np.array_equal(np.stack([lo, hi], 1).reshape(-1) & 7, codes & 7)
+    assert np.array_equal(oracle.mx4_decode_row(q, e8), vals)
+
+
+def test_mx4_scale_and_error_bound(oracle):
+    wl = WORKLOADS["prefill"].with_tokens(24)
+    x = make_inputs(wl, 9)["x"]
+    rng = np.random.default_rng(2)
+    x[3, :32] = 0                                       # zero block
+    x[3, 32:64] = 0x8000                                # negative zeros
+    x[4, :32] = _bf16_of(rng.standard_normal(32) * 2.0 ** -130)  # below the lowest scale
+    x[5, :32] = _bf16_of(rng.standard_normal(32) * 2.0 ** 120)
+    for t in range(wl.tokens):
+        q, e8 = oracle.mx4_quant_row(x[t])
+        v = bf16_f32(x[t]).astype(np.float64).reshape(-1, 32)
+        amax = np.abs(v).max(1)
+        with np.errstate(divide="ignore"):
+            se = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1))) - 2, -127)
+        se = np.clip(se, -127, 127)
+        assert np.array_equal(e8.astype(np.int64), (se + 127).astype(np.int64))
+        X = np.repeat(2.0 ** se, 32)
+        dq = oracle.mx4_decode_row(q, e8)
+        a = np.abs(v.reshape(-1)) / X
+        half_step = np.where(a < 2, 0.25, np.where(a < 4, 0.5, 1.0))
+        bound = np.where(a > 6, a - 6, half_step) * X
+        assert np.all(np.abs(dq - v.reshape(-1)) <= bound)
+        assert np.all(np.abs(dq) <= 6 * X)
+    q, e8 = oracle.mx4_quant_row(x[3])
+    assert e8[0] == 0 and e8[1] == 0
+    assert np.all(q[:16] == 0) and np.all(q[16:32] == 0x88)
+
+
+def test_mxfp4_dispatch_and_fp4_carry(oracle):
+    wl = WORKLOADS["prefill"].with_tokens(96)
+    inp = make_inputs(wl, 23)
+    R, epr, cap = wl.ranks, wl.experts_per_rank, wl.cap
+    pl = oracle.plan(inp["indices"], R, epr, cap)
+    d4 = oracle.dispatch(inp["x"], inp["weights"], inp["indices"], pl, R, epr, cap, 4,
+                         fill=0x3C)
+    rows = [oracle.mx4_quant_row(inp["x"][t]) for t in range(wl.tokens)]
+    assert d4["recv_x"].shape == (R, cap, wl.hidden // 2)
+    assert d4["recv_scales"].shape == (R, cap, wl.hidden // 128)
+    written = np.zeros((R, cap), bool)
+    for t in range(wl.tokens):
+        for j in range(wl.topk):
+            r, s = inp["indices"][t, j] // epr, pl["slot"][t, j]
+            written[r, s] = True
+            assert np.array_equal(d4["recv_x"][r, s], rows[t][0])
+            assert np.array_equal(d4["recv_scales"][r, s].view(np.uint8), rows[t][1])
+    assert np.all(d4["recv_x"][~written] == 0x3C)
+    # carrying the pre-quantised rows lands the same bytes
+    q = np.stack([r[0] for r in rows])
+    sw = np.stack([r[1] for r in rows]).view(np.float32)
+    dc = oracle.dispatch(q, inp["weights"], inp["indices"], pl, R, epr, cap, 3, fill=0x3C,
+                         scales=sw)
+    assert np.array_equal(dc["recv_x"], d4["recv_x"])
+    assert np.array_equal(dc["recv_scales"].view(np.uint32), d4["recv_scales"].view(np.uint32))
+
+
+def test_fp8_direct_cast_combine(oracle):
+    # Expert outputs that are E4M3 values already survive the cast, so the
+    # combine of the cast rows equals the bf16 combine bit for bit; other
+    # outputs stay within the cast's error: 2^-4 relative, 2^-10 absolute
+    # below the smallest normal (half a subnormal step).
+    wl = dataclasses.replace(WORKLOADS["decode"].with_tokens(64), ranks=4, experts_per_rank=8,
+                             cap=64, hidden=1024)
+    inp = make_inputs(wl, 31)
+    R, epr, cap = wl.ranks, wl.experts_per_rank, wl.cap
+    pl = oracle.plan(inp["indices"], R, epr, cap)
+    rng = np.random.default_rng(4)
+    codes = rng.integers(0, 254, (R, cap, wl.hidden)).astype(np.uint8)
+    codes[codes >= 0x7F] += 1
+    y = oracle.e4m3_to_bf16(codes)
+    assert np.array_equal(oracle.cast_fp8_direct(y), codes)
+    a = oracle.combine(y, inp["weights"], inp["indices"], pl, epr, cap)
+    b = oracle.combine(oracle.e4m3_to_bf16(oracle.cast_fp8_direct(y)), inp["weights"],
+                       inp["indices"], pl, epr, cap)
+    assert np.array_equal(a, b)
+    d = oracle.dispatch(inp["x"], inp["weights"], inp["indices"], pl, R, epr, cap, False)
+    y2 = d["recv_x"]
+    ref = bf16_f32(oracle.combine(y2, inp["weights"], inp["indices"], pl, epr, cap))
+    got = bf16_f32(oracle.combine(oracle.e4m3_to_bf16(oracle.cast_fp8_direct(y2)),
+                                  inp["weights"], inp["indices"], pl, epr, cap))
+    wsum = np.abs(inp["weights"]).sum(1)[:, None]
+    yabs = np.abs(bf16_f32(inp["x"]))
+    bound = 2.0 ** -4 * wsum * yabs + 2.0 ** -10 * wsum + _ulp_bf16(ref) + _ulp_bf16(got)
+    assert np.all(np.abs(got - ref) <= bound)
+    big = oracle.cast_fp8_direct(_bf16_of(np.array([1000.0, -1000.0, 448.0, 464.0])))
+    assert list(big) == [0x7E, 0xFE, 0x7E, 0x7E]  # saturates at +-448
