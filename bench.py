@@ -10,7 +10,9 @@ combine").  value = the step's algorithmic HBM bytes / step time.
 Also measured, each on its own buffers: decode latency (128 tokens, bf16 both
 ways), the skewed-routing workload (Zipf 1.2, 16 ranks) and the standard-MoE
 workload (FP8 dispatch, expert-major conversion, combine from it; and the
-single-call standard-MoE dispatch followed by the same combine).  Inputs are
+single-call standard-MoE dispatch followed by the same combine), and the
+prefill shape with an MXFP4 dispatch payload and with the FP8 direct-cast
+combine payload.  Inputs are
 synthetic and resident in HBM; expert outputs are produced once, before
 timing, by the stand-in expert.  Buffer sets rotate so no step finds its data
 in the 256 MB Infinity Cache.  Kernel durations come from back-to-back loops
@@ -46,38 +48,50 @@ def plan_bytes(T, k, R, U):
     return T * k * 4 + U * 4 + R * 4            # ids in; src_token_pos, counts out
 
 
-def dispatch_bytes(T, H, k, U, fp8):
-    nb = H // 128 if fp8 else 0
-    b = 1 if fp8 else 2
-    return T * H * 2 + T * k * 8 + U * (H * b + nb * 4 + k * 8)
+def row_bytes(H, quant):
+    # received row and its scales: bf16; E4M3 + fp32 per 128; E2M1 + E8M0 per 32
+    return {"none": H * 2, "fp8": H + H // 128 * 4, "mxfp4": H // 2 + H // 32}[quant]
+
+
+def dispatch_bytes(T, H, k, U, quant):
+    return T * H * 2 + T * k * 8 + U * (row_bytes(H, quant) + k * 8)
 
 
 def combine_bytes(T, H, k, U):
     return U * H * 2 + T * k * 8 + T * H * 2
 
 
-def to_expert_major_bytes(T, H, k, U, fp8):
-    nb = H // 128 if fp8 else 0
-    b = 1 if fp8 else 2
-    return U * (H * b + nb * 4 + k * 4) + T * k * (H * b + nb * 4 + 4)
+def to_expert_major_bytes(T, H, k, U, quant):
+    rb = row_bytes(H, quant)
+    return U * (rb + k * 4) + T * k * (rb + 4)
 
 
-def standard_moe_bytes(T, H, k, E, Uem, fp8):
+def standard_moe_bytes(T, H, k, E, Uem, quant):
     # x and ids read once; each expert row written with its scales and source
     # position; per-expert counts and offsets
-    nb = H // 128 if fp8 else 0
-    b = 1 if fp8 else 2
-    return T * H * 2 + T * k * 4 + Uem * (H * b + nb * 4 + 4) + E * 8
+    return T * H * 2 + T * k * 4 + Uem * (row_bytes(H, quant) + 4) + E * 8
+
+
+def cast_fp8_bytes(H, U):
+    return U * H * 3          # bf16 rows read, E4M3 rows written
+
+
+def combine_fp8_bytes(T, H, k, U):
+    return U * H + T * k * 8 + T * H * 2
 
 
 def combine_em_bytes(T, H, k):
     return T * k * H * 2 + T * k * 8 + T * H * 2
 
 
-def src_digest(*names):
+def src_digest(name):
+    """Digest of a kernel source file and every header beside it (a change to
+    a shared header changes the kernel too)."""
+    import glob
+    csrc = os.path.join(ROOT, "combine_mep_plan_amd", "csrc")
     h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "combine_mep_plan_amd", "csrc", n), "rb") as f:
+    for p in [os.path.join(csrc, name)] + sorted(glob.glob(os.path.join(csrc, "*.h"))):
+        with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -123,11 +137,18 @@ class Runner:
     def __init__(self, M, torch, wl, inp, nsets):
         self.M, self.torch, self.wl = M, torch, wl
         T, H, R, cap, k = wl.tokens, wl.hidden, wl.ranks, wl.cap, wl.topk
-        self.fp8 = wl.quant == "fp8"
+        self.quant = wl.quant
         self.em = wl.layout == "expert_major"
-        self.m = M.Mep(H, wl.experts_per_rank, k, cap, R, fp8=self.fp8)
+        self.fp8c = wl.combine == "fp8_direct"
+        qmode = {"none": M.MEP_QUANT_NONE, "fp8": M.MEP_QUANT_FP8_E4M3_BLOCK128,
+                 "mxfp4": M.MEP_QUANT_MXFP4}[wl.quant]
+        self.m = M.Mep(H, wl.experts_per_rank, k, cap, R, quant=qmode)
         self.stream = torch.cuda.current_stream()
         dev = lambda a: torch.from_numpy(a).cuda()  # noqa: E731
+        # received rows: bf16 values, E4M3 bytes, or packed E2M1 bytes
+        rcols, rdt = {"none": (H, torch.int16), "fp8": (H, torch.uint8),
+                      "mxfp4": (H // 2, torch.uint8)}[wl.quant]
+        nb = wl.scale_dim
         self.sets = []
         for _ in range(nsets):
             s = {
@@ -135,20 +156,18 @@ class Runner:
                 "idx": dev(inp["indices"]),
                 "counts": torch.zeros(R, dtype=torch.int32, device="cuda"),
                 "spos": torch.zeros((R, cap), dtype=torch.int32, device="cuda"),
-                "rx": torch.zeros((R, cap, H), dtype=torch.uint8 if self.fp8 else torch.int16,
-                                  device="cuda"),
-                "rs": (torch.zeros((R, cap, H // 128), dtype=torch.float32, device="cuda")
-                       if self.fp8 else None),
+                "rx": torch.zeros((R, cap, rcols), dtype=rdt, device="cuda"),
+                "rs": (torch.zeros((R, cap, nb), dtype=torch.float32, device="cuda")
+                       if nb else None),
                 "rw": torch.zeros((R, cap, k), dtype=torch.float32, device="cuda"),
                 "ri": torch.zeros((R, cap, k), dtype=torch.int32, device="cuda"),
                 "out": torch.empty((T, H), dtype=torch.int16, device="cuda"),
             }
             if self.em:
                 ce = wl.cap_em
-                s["emx"] = torch.zeros((ce, H), dtype=torch.uint8 if self.fp8 else torch.int16,
-                                       device="cuda")
-                s["ems"] = (torch.zeros((ce, H // 128), dtype=torch.float32, device="cuda")
-                            if self.fp8 else None)
+                s["emx"] = torch.zeros((ce, rcols), dtype=rdt, device="cuda")
+                s["ems"] = (torch.zeros((ce, nb), dtype=torch.float32, device="cuda")
+                            if nb else None)
                 s["emc"] = torch.zeros(wl.experts, dtype=torch.int32, device="cuda")
                 s["emo"] = torch.zeros(wl.experts + 1, dtype=torch.int32, device="cuda")
                 s["emp"] = torch.zeros(ce, dtype=torch.int32, device="cuda")
@@ -158,6 +177,8 @@ class Runner:
                 s["y"] = self.stand_in(s["emx"], s["ems"])
             else:
                 s["y"] = self.stand_in(s["rx"], s["rs"])
+            if self.fp8c:
+                s["y8"] = torch.zeros(s["y"].shape, dtype=torch.uint8, device="cuda")
             M.mep_reset(self.m.h, self.stream)
             self.sets.append(s)
         torch.cuda.synchronize()
@@ -166,13 +187,22 @@ class Runner:
 
     def stand_in(self, x, scales):
         # expert outputs (harness, untimed): identity for bf16 payloads,
-        # bf16((decode(q) * scale) * mult) for E4M3 payloads
+        # bf16((decode(q) * scale) * mult) for E4M3 and MX FP4 payloads
+        torch = self.torch
         if scales is None:
             return x
         mult = 0.5 if self.wl.expert == "dequant_half" else 1.0
-        q = x.view(self.torch.float8_e4m3fn).float()
-        y = (q * scales.repeat_interleave(128, dim=-1)) * mult
-        return y.to(self.torch.bfloat16).view(self.torch.int16)
+        if self.quant == "mxfp4":
+            lut = torch.tensor([0, .5, 1, 1.5, 2, 3, 4, 6, -0., -.5, -1, -1.5, -2, -3, -4, -6],
+                               dtype=torch.float32, device=x.device)
+            b = x.long()
+            q = torch.stack([lut[b & 15], lut[b >> 4]], dim=-1).flatten(-2)
+            e = scales.view(torch.uint8).float()
+            s = torch.exp2(e - 127.0).repeat_interleave(32, dim=-1)
+        else:
+            q = x.view(torch.float8_e4m3fn).float()
+            s = scales.repeat_interleave(128, dim=-1)
+        return ((q * s) * mult).to(torch.bfloat16).view(torch.int16)
 
     def plan_dispatch(self, s):
         self.M.mep_plan_dispatch(self.m.h, s["idx"], self.wl.tokens, s["counts"], s["spos"],
@@ -201,14 +231,24 @@ class Runner:
                                    s["emx"], s["ems"], s["emc"], s["emo"], s["emp"],
                                    self.wl.cap_em, self.stream)
 
+    def layout(self):
+        return self.M.MEP_EXPERT_MAJOR if self.em else self.M.MEP_RANK_MAJOR
+
+    def cast(self, s):
+        self.M.mep_cast_fp8_direct(self.m.h, self.layout(), s["y"], s["y8"], self.stream)
+
     def combine(self, s):
-        layout = self.M.MEP_EXPERT_MAJOR if self.em else self.M.MEP_RANK_MAJOR
-        self.M.mep_combine(self.m.h, layout, s["y"], s["w"], s["out"], self.stream)
+        if self.fp8c:
+            self.M.mep_combine_fp8(self.m.h, self.layout(), s["y8"], s["w"], s["out"], self.stream)
+        else:
+            self.M.mep_combine(self.m.h, self.layout(), s["y"], s["w"], s["out"], self.stream)
 
     def step(self, s):
         self.plan_dispatch(s)
         if self.em:
             self.to_em(s)
+        if self.fp8c:
+            self.cast(s)
         self.combine(s)
         self.M.mep_reset(self.m.h, self.stream)
 
@@ -218,17 +258,21 @@ class Runner:
     def bytes(self):
         wl, U = self.wl, self.U
         T, H, k, R = wl.tokens, wl.hidden, wl.topk, wl.ranks
-        b = {"plan": plan_bytes(T, k, R, U), "dispatch": dispatch_bytes(T, H, k, U, self.fp8)}
+        b = {"plan": plan_bytes(T, k, R, U), "dispatch": dispatch_bytes(T, H, k, U, self.quant)}
         b["plan_dispatch"] = b["plan"] + b["dispatch"]
         if self.em:
-            b["to_expert_major"] = to_expert_major_bytes(T, H, k, U, self.fp8)
+            b["to_expert_major"] = to_expert_major_bytes(T, H, k, U, self.quant)
             b["combine"] = combine_em_bytes(T, H, k)
             b["dispatch_standard_moe"] = standard_moe_bytes(T, H, k, wl.experts, self.Uem,
-                                                            self.fp8)
+                                                            self.quant)
             b["step_standard"] = b["dispatch_standard_moe"] + b["combine"]
+        elif self.fp8c:
+            b["cast_fp8_direct"] = cast_fp8_bytes(H, U)
+            b["combine"] = combine_fp8_bytes(T, H, k, U)
         else:
             b["combine"] = combine_bytes(T, H, k, U)
-        b["step"] = b["plan_dispatch"] + b["combine"] + b.get("to_expert_major", 0)
+        b["step"] = (b["plan_dispatch"] + b["combine"] + b.get("to_expert_major", 0)
+                     + b.get("cast_fp8_direct", 0))
         return b
 
     def measure(self, steps, warmup):
@@ -241,6 +285,8 @@ class Runner:
         times["plan_dispatch"] = self.loop(self.plan_dispatch, steps)
         if self.em:
             times["to_expert_major"] = self.loop(self.to_em, steps)
+        if self.fp8c:
+            times["cast_fp8_direct"] = self.loop(self.cast, steps)
         times["combine"] = self.loop(self.combine, steps)
         times["plan"] = self.loop(self.plan, steps)
         times["dispatch"] = self.loop(self.dispatch, steps)
@@ -348,7 +394,7 @@ def cpu_baseline(wl, inp, budget_s=20.0):
     d = O.dispatch(sub["x"], sub["weights"], sub["indices"], pl, R, epr, cap, True)
     y = O.expert_dequant(d["recv_x"], d["recv_scales"], 0.5)
     U = int(pl["recv_counts"].sum())
-    nbytes = (plan_bytes(ts, k, R, U) + dispatch_bytes(ts, H, k, U, True)
+    nbytes = (plan_bytes(ts, k, R, U) + dispatch_bytes(ts, H, k, U, "fp8")
               + combine_bytes(ts, H, k, U))
     times = []
     t_end = time.perf_counter() + budget_s
@@ -419,7 +465,8 @@ def main():
 
     extra = {}
     if not args.no_extra:
-        for name, nsets in (("skew", 3), ("stdmoe", 2)):
+        for name, nsets in (("skew", 3), ("stdmoe", 2), ("prefill_mxfp4", 3),
+                            ("prefill_fp8direct", 3)):
             xwl = WORKLOADS[name]
             say(f"{name}: T={xwl.tokens} R={xwl.ranks} epr={xwl.experts_per_rank}")
             r = Runner(M, torch, xwl, make_inputs(xwl, 0), nsets)

@@ -28,6 +28,8 @@ MEP_DEV_EM_OVERFLOW = 4
 MEP_QUANT_NONE = 0
 MEP_QUANT_FP8_E4M3_BLOCK128 = 1
 MEP_QUANT_FP8_CARRY = 2
+MEP_QUANT_FP4_CARRY = 3
+MEP_QUANT_MXFP4 = 4
 MEP_RANK_MAJOR = 0
 MEP_EXPERT_MAJOR = 1
 
@@ -74,6 +76,8 @@ def lib() -> C.CDLL:
             "mep_dispatch_standard_moe": ([p, p, i32, p, p, p, p, p, p, p, i64, p], C.c_int),
             "mep_to_expert_major": ([p, p, p, p, p, p, p, p, p, p, p, i64, p], C.c_int),
             "mep_combine": ([p, i32, p, p, p, p], C.c_int),
+            "mep_combine_fp8": ([p, i32, p, p, p, p], C.c_int),
+            "mep_cast_fp8_direct": ([p, i32, p, p, p], C.c_int),
             "mep_reset": ([p, p], C.c_int),
             "mep_get_status": ([p, p, C.POINTER(i32)], C.c_int),
             "mep_get_route": ([p, p, p, p], C.c_int),
@@ -175,6 +179,17 @@ def mep_to_expert_major(h, recv_x, recv_scales, recv_indices, recv_counts, src_t
 def mep_combine(h, layout, y, weights, out, stream=None) -> None:
     s = _stream(stream, out)
     _check("mep_combine", lib().mep_combine(h, layout, _ptr(y), _ptr(weights), _ptr(out), s))
+
+
+def mep_combine_fp8(h, layout, y8, weights, out, stream=None) -> None:
+    s = _stream(stream, out)
+    _check("mep_combine_fp8", lib().mep_combine_fp8(h, layout, _ptr(y8), _ptr(weights), _ptr(out),
+                                                    s))
+
+
+def mep_cast_fp8_direct(h, layout, y, y8, stream=None) -> None:
+    s = _stream(stream, y8)
+    _check("mep_cast_fp8_direct", lib().mep_cast_fp8_direct(h, layout, _ptr(y), _ptr(y8), s))
 
 
 def mep_reset(h, stream=None) -> None:

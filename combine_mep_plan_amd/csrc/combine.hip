@@ -14,6 +14,13 @@
 // Each distinct expert-output row is loaded once (positions that share a rank
 // row reuse its registers) with non-temporal loads -- the rows are read
 // exactly once -- and all of a slice's loads are issued before the FMAs.
+//
+// FP8 direct-cast payload (the intra-node tuning matrix pairs quant type
+// fp8_direct_cast with a bf16 combine; the cast rule -- OCP E4M3, no scale,
+// round to nearest even, saturating at 448 -- is this library's reading): a
+// cast launch turns the routed bf16 expert-output rows into E4M3 rows, and the
+// E4M3 combine decodes each value exactly to fp32 and accumulates as above.
+// A lane owns 16 columns there: one 16-byte E4M3 unit in, two bf16 units out.
 #include "dev.h"
 #include "mep_internal.h"
 
@@ -91,6 +98,110 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   }
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Every top-k position loads its row, also when it shares a rank row with an
+// earlier position (the repeat is a cache hit): selecting among already
+// loaded registers, as the bf16 kernel does, here made the compiler wait on
+// each load in turn.
+template <int KMAX>
+__global__ __launch_bounds__(256) void combine_fp8_kernel(CombineArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int g = first_lane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  const int t = g / a.slices, sl = g - t * a.slices;
+  if (t >= a.T) return;
+  const int nv8 = a.H / 16;  // 16-byte E4M3 units per row
+  int row[KMAX];
+  float w[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    row[j] = j < a.k ? a.rows[(size_t)t * a.k + j] : -1;
+    w[j] = j < a.k ? a.w[(size_t)t * a.k + j] : 0.0f;
+  }
+  const u32x4* y = reinterpret_cast<const u32x4*>(a.y);
+  const int v = sl * kWave + lane;
+  u32x4 in[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    in[j] = u32x4{0, 0, 0, 0};
+    if (row[j] >= 0 && v < nv8) in[j] = __builtin_nontemporal_load(y + (size_t)row[j] * nv8 + v);
+  }
+  if (v >= nv8) return;
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (row[j] < 0) continue;  // uniform
+    const u32x4 x = in[j];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[i], false);  // bytes 0, 1
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[i], true);   // bytes 2, 3
+      acc[4 * i] = __builtin_fmaf(w[j], lo.x, acc[4 * i]);
+      acc[4 * i + 1] = __builtin_fmaf(w[j], lo.y, acc[4 * i + 1]);
+      acc[4 * i + 2] = __builtin_fmaf(w[j], hi.x, acc[4 * i + 2]);
+      acc[4 * i + 3] = __builtin_fmaf(w[j], hi.y, acc[4 * i + 3]);
+    }
+  }
+  u32x4 o0, o1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o0[i] = pack_bf16_rne(acc[2 * i], acc[2 * i + 1]);
+    o1[i] = pack_bf16_rne(acc[8 + 2 * i], acc[8 + 2 * i + 1]);
+  }
+  u32x4* out = reinterpret_cast<u32x4*>(a.out) + (size_t)t * (a.H / 8) + 2 * v;
+  store_nt(out, o0);
+  store_nt(out + 1, o1);
+}
+
+// E4M3 of a bf16 pair's values, clamped to +-448 first so that the convert
+// saturates.
+__device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
+
+// One wave per (token, slice); the token's distinct rows in groups of 8, all
+// loads of a group issued before its converts.
+template <bool RANK_MAJOR>
+__global__ __launch_bounds__(256) void cast_fp8_kernel(CastArgs a) {
+  constexpr int G = 8;
+  const int lane = threadIdx.x & 63;
+  const int g = first_lane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  const int t = g / a.slices, sl = g - t * a.slices;
+  if (t >= a.T) return;
+  const int nv8 = a.H / 16, nv = a.H / 8;
+  const int v = sl * kWave + lane;
+  const bool on = v < nv8;
+  const uint32_t own = RANK_MAJOR ? a.ufirst[t] : 0xFFFFFFFFu;  // uniform
+  const u32x4* y = reinterpret_cast<const u32x4*>(a.y);
+  u32x4* y8 = reinterpret_cast<u32x4*>(a.y8);
+  for (int j0 = 0; j0 < a.k; j0 += G) {
+    int row[G];
+    u32x4 in[G][2];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int j = j0 + u;
+      row[u] = (j < a.k && (own >> j & 1u)) ? a.rows[(size_t)t * a.k + j] : -1;
+      in[u][0] = in[u][1] = u32x4{0, 0, 0, 0};
+      if (row[u] >= 0 && on) {
+        in[u][0] = __builtin_nontemporal_load(y + (size_t)row[u] * nv + 2 * v);
+        in[u][1] = __builtin_nontemporal_load(y + (size_t)row[u] * nv + 2 * v + 1);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      if (row[u] < 0 || !on) continue;
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {  // output word i: columns 4i..4i+3
+        const uint32_t p0 = in[u][i / 2][(2 * i) % 4], p1 = in[u][i / 2][(2 * i) % 4 + 1];
+        o[i] = pack_e4m3x4(clamp448(bf16_lo(p0)), clamp448(bf16_hi(p0)), clamp448(bf16_lo(p1)),
+                           clamp448(bf16_hi(p1)));
+      }
+      store_nt(y8 + (size_t)row[u] * nv8 + v, o);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a0, hipStream_t s) {
@@ -106,6 +217,27 @@ hipError_t launch_combine(const CombineArgs& a0, hipStream_t s) {
   } else {
     combine_kernel<kMaxTopk, false><<<blocks, 256, 0, s>>>(a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_fp8(const CombineArgs& a0, hipStream_t s) {
+  if (a0.T == 0) return hipSuccess;
+  CombineArgs a = a0;
+  a.slice_units = kWave;
+  a.slices = (a.H / 16 + kWave - 1) / kWave;
+  const int blocks = (int)(((int64_t)a.T * a.slices + 3) / 4);
+  if (a.k <= 8) combine_fp8_kernel<8><<<blocks, 256, 0, s>>>(a);
+  else combine_fp8_kernel<kMaxTopk><<<blocks, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_fp8(const CastArgs& a0, hipStream_t s) {
+  if (a0.T == 0) return hipSuccess;
+  CastArgs a = a0;
+  a.slices = (a.H / 16 + kWave - 1) / kWave;
+  const int blocks = (int)(((int64_t)a.T * a.slices + 3) / 4);
+  if (a.ufirst) cast_fp8_kernel<true><<<blocks, 256, 0, s>>>(a);
+  else cast_fp8_kernel<false><<<blocks, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

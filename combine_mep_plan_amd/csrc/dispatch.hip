@@ -1,6 +1,8 @@
-// Dispatch: scatter each token's row (bf16 copy, or OCP E4M3 codes with one
-// fp32 scale per 128 columns) plus its k weights and k expert ids into the
-// receive buffer of every distinct destination rank, at the token's slot.
+// Dispatch: scatter each token's row (bf16 copy; OCP E4M3 codes with one fp32
+// scale per 128 columns; OCP MX FP4 with one E8M0 scale per 32 columns; or an
+// already-quantized FP8/FP4 row with the caller's scales) plus its k weights
+// and k expert ids into the receive buffer of every distinct destination
+// rank, at the token's slot.
 //
 // Source: "MORI-EP User Guide", section 3 dispatch() (outputs: received rows,
 // weights, scales, indices); "Choosing an EP API and backend": the gfx950 FP8
@@ -9,16 +11,11 @@
 // reading; the pages do not print the format.
 //
 // Layout of the work: a row is cut into 1 KiB-per-wave slices -- each lane owns
-// one 16-byte unit of input (bf16: 8 columns) or of output (FP8: 16 columns,
-// 8 lanes per 128-column scale block) -- and one wave handles one (token,
-// slice).  Many small waves keep enough writes in flight to approach the HBM
+// one 16-byte unit of the received row (bf16: 8 columns; FP8: 16 columns, 8
+// lanes per 128-column scale block; FP4: 32 columns, one MX block) -- and one
+// wave handles one (token, slice).  Many small waves keep enough writes in flight to approach the HBM
 // write rate; every receive-row store is a non-temporal 16-byte-per-lane
 // store (1 KiB per wave instruction).
-//
-// Payloads: bf16 rows copied; bf16 rows quantised to OCP E4M3 with per-128
-// scales; or rows that arrive already in E4M3 with the caller's scale rows
-// ("carry", "Choosing an EP API and backend": the HIP backend carries
-// already-quantized FP8 payloads), copied with their scales.
 //
 // Where the destination slots come from:
 //   kRoute  : a prior plan's receive row of each (token, top-k position);
@@ -27,6 +24,7 @@
 //             the plan outputs -- a fused plan+dispatch;
 //   kInline : as kCounts, but the prefixes are recomputed from the ids of the
 //             earlier chunks, for small batches: plan+dispatch in one launch.
+#include "payload.h"
 #include "route.h"
 
 namespace mep {
@@ -116,12 +114,9 @@ __device__ __forceinline__ void store_meta(const DispatchArgs& a, int t, int row
   }
 }
 
-// QUANT: MEP_QUANT_NONE (bf16 copy), MEP_QUANT_FP8_E4M3_BLOCK128 (quantise),
-// MEP_QUANT_FP8_CARRY (E4M3 bytes and the caller's scale rows copied).
+// QUANT: a MEP_QUANT_* payload mode (see payload.h).
 template <int QUANT, int MODE, int KMAX>
 __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
-  constexpr bool FP8 = QUANT == MEP_QUANT_FP8_E4M3_BLOCK128;
-  constexpr bool CARRY = QUANT == MEP_QUANT_FP8_CARRY;
   const int lane = threadIdx.x & 63;
   const int g = first_lane(blockIdx.x * 4 + (threadIdx.x >> 6));
   const int t = g / a.slices, sl = g - t * a.slices;
@@ -129,17 +124,11 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
   if (MODE == kInline && g == 0 && lane == 0) *a.status_next = 0u;
 
   // this wave's unit of the row: loads go out before the routing work
-  // 16-byte output units per row: 16 E4M3 codes, or 8 bf16 values
-  const int nu = (FP8 || CARRY) ? a.H / 16 : a.H / 8;
+  const int nu = payload_units(QUANT, a.H);
   const int v = sl * kWave + lane;
   const bool on = v < nu;
-  const u32x4* src =
-      reinterpret_cast<const u32x4*>(a.x) + (size_t)t * (FP8 ? a.H / 8 : nu);
-  u32x4 in0 = u32x4{0, 0, 0, 0}, in1 = u32x4{0, 0, 0, 0};
-  if (on) {
-    if (FP8) { in0 = src[2 * v]; in1 = src[2 * v + 1]; }
-    else in0 = src[v];
-  }
+  Unit<QUANT> unit;
+  unit.load(a.x, t, a.H, v, on);
 
   uint32_t first = 0;
   WaveRoute w{};
@@ -157,18 +146,16 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
   }
 
   float scale = 0.0f;
-  const u32x4 q = FP8 ? quant16(in0, in1, scale) : in0;
-  const int nb = a.H / 128;
+  uint32_t e8 = 0;
+  const u32x4 q = unit.convert(scale, e8);
   auto emit = [&](int row) {
     if (on) {
       store_nt(reinterpret_cast<u32x4*>(a.recv_x) + (size_t)row * nu + v, q);
-      if (FP8 && (v & 7) == 0) a.recv_scales[(size_t)row * nb + (v >> 3)] = scale;
+      store_unit_scale<QUANT>(a.recv_scales, (size_t)row, a.H, v, scale, e8);
     }
     if (sl == 0) {
       store_meta(a, t, row, lane);
-      if (CARRY)
-        for (int i = lane; i < a.scale_dim; i += kWave)
-          a.recv_scales[(size_t)row * a.scale_dim + i] = a.x_scales[(size_t)t * a.scale_dim + i];
+      if (is_carry(QUANT)) copy_scale_row(a.recv_scales, (size_t)row, a.x_scales, t, a.scale_dim, lane);
     }
   };
   if (MODE == kRoute) {
@@ -185,8 +172,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
 template <int QUANT, int MODE>
 hipError_t launch_mode(const DispatchArgs& a0, hipStream_t s) {
   DispatchArgs a = a0;
-  const int units = QUANT != MEP_QUANT_NONE ? a.H / 16 : a.H / 8;
-  a.slices = (units + kWave - 1) / kWave;
+  a.slices = (payload_units(QUANT, a.H) + kWave - 1) / kWave;
   a.slice_units = kWave;
   const int64_t waves = (int64_t)a.T * a.slices;
   const int blocks = (int)((waves + 3) / 4);
@@ -200,6 +186,8 @@ hipError_t launch_dtype(const DispatchArgs& a, hipStream_t s) {
   switch (a.quant) {
     case MEP_QUANT_FP8_E4M3_BLOCK128: return launch_mode<MEP_QUANT_FP8_E4M3_BLOCK128, MODE>(a, s);
     case MEP_QUANT_FP8_CARRY: return launch_mode<MEP_QUANT_FP8_CARRY, MODE>(a, s);
+    case MEP_QUANT_FP4_CARRY: return launch_mode<MEP_QUANT_FP4_CARRY, MODE>(a, s);
+    case MEP_QUANT_MXFP4: return launch_mode<MEP_QUANT_MXFP4, MODE>(a, s);
     default: return launch_mode<MEP_QUANT_NONE, MODE>(a, s);
   }
 }

@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256) void em_scatter_kernel(EmArgs a) {
   const int s = u - prefix[r];
   const int cnt = prefix[r + 1] - prefix[r];
   const size_t row = (size_t)r * a.cap + s;
-  const int nv = a.H * a.elem_bytes / 16;  // 16-byte units per row
+  const int nv = a.row_units;  // 16-byte units per row
   // row slice first: its loads do not depend on the placement
   const u32x4* src = reinterpret_cast<const u32x4*>(a.recv_x) + row * nv;
   u32x4 val[UPL];
@@ -249,7 +249,7 @@ hipError_t launch_to_expert_major(const EmArgs& a0, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // one wave per (receive row, kEmUnits x 64 units); rows <= T * min(k, R)
-  const int nv = a.H * a.elem_bytes / 16;
+  const int nv = a.row_units;
   const int per = kEmUnitsPerLane * kWave;
   a.slices = (nv + per - 1) / per;
   const int64_t rows = (int64_t)a.T * std::min(a.k, a.R);

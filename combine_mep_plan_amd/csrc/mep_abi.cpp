@@ -68,6 +68,10 @@ static int check_config(const mep_config* c) {
     if (H % 128 != 0 || c->scale_dim != H / 128) return MEP_ERR_CONFIG;
   } else if (c->quant == MEP_QUANT_FP8_CARRY) {
     if (H % 16 != 0 || c->scale_dim < 0 || c->scale_dim > (1 << 16)) return MEP_ERR_CONFIG;
+  } else if (c->quant == MEP_QUANT_FP4_CARRY) {
+    if (H % 32 != 0 || c->scale_dim < 0 || c->scale_dim > (1 << 16)) return MEP_ERR_CONFIG;
+  } else if (c->quant == MEP_QUANT_MXFP4) {
+    if (H % 128 != 0 || c->scale_dim != H / 128) return MEP_ERR_CONFIG;
   } else {
     return MEP_ERR_CONFIG;
   }
@@ -188,7 +192,7 @@ static int check_dispatch_args(mep_handle* h, int32_t T, const void* x, const fl
                                const float* recv_scales, const float* recv_weights,
                                const int32_t* recv_indices) {
   const mep_config& c = h->cfg;
-  const bool carry = c.quant == MEP_QUANT_FP8_CARRY;
+  const bool carry = mep::is_carry(c.quant);
   if (!recv_x || !recv_weights || !recv_indices) return MEP_ERR_NULL;
   if (scale_cols(c) > 0 && !recv_scales) return MEP_ERR_NULL;
   if (T > 0 && (!x || !weights || !indices)) return MEP_ERR_NULL;
@@ -209,7 +213,7 @@ static mep::DispatchArgs dispatch_args(mep_handle* h, int32_t T, const void* x,
   const mep_config& c = h->cfg;
   mep::DispatchArgs a{};
   a.x = x;
-  a.x_scales = c.quant == MEP_QUANT_FP8_CARRY ? scales : nullptr;
+  a.x_scales = mep::is_carry(c.quant) ? scales : nullptr;
   a.quant = c.quant;
   a.scale_dim = scale_cols(c);
   a.w = weights;
@@ -297,7 +301,6 @@ int mep_to_expert_major(mep_handle* h, const void* recv_x, const float* recv_sca
   if (!h) return MEP_ERR_NULL;
   if (!h->plan_valid) return MEP_ERR_STATE;
   const mep_config& c = h->cfg;
-  const bool fp8 = c.quant != MEP_QUANT_NONE;  // 1-byte E4M3 rows
   const int nb = scale_cols(c);
   if (!recv_x || !recv_indices || !recv_counts || !src_token_pos || !em_x || !em_counts ||
       !em_offsets || !em_src_pos)
@@ -334,7 +337,7 @@ int mep_to_expert_major(mep_handle* h, const void* recv_x, const float* recv_sca
   a.cap = c.max_num_inp_token_per_rank;
   a.CR = (c.max_num_inp_token_per_rank + mep::kChunk - 1) / mep::kChunk;
   a.nb = nb;
-  a.elem_bytes = fp8 ? 1 : 2;
+  a.row_units = mep::payload_units(c.quant, c.hidden_dim);
   a.spos_base = c.rank * c.world_size * c.max_num_inp_token_per_rank;
   h->em_valid = false;
   int rc = hip_rc(mep::launch_to_expert_major(a, (hipStream_t)stream));
@@ -350,7 +353,7 @@ int mep_dispatch_standard_moe(mep_handle* h, const int32_t* indices, int32_t T, 
   if (!h) return MEP_ERR_NULL;
   const mep_config& c = h->cfg;
   const int nb = scale_cols(c);
-  const bool carry = c.quant == MEP_QUANT_FP8_CARRY;
+  const bool carry = mep::is_carry(c.quant);
   if (T < 0 || T > c.max_num_inp_token_per_rank) return MEP_ERR_SHAPE;
   if (cap_em < 0 || cap_em > INT32_MAX) return MEP_ERR_SHAPE;
   if (!em_x || !em_counts || !em_offsets || !em_src_pos) return MEP_ERR_NULL;
@@ -393,12 +396,20 @@ int mep_dispatch_standard_moe(mep_handle* h, const int32_t* indices, int32_t T, 
   return MEP_OK;
 }
 
-int mep_combine(mep_handle* h, int32_t layout, const void* y, const float* weights, void* out,
-                void* stream) {
-  if (!h) return MEP_ERR_NULL;
+// Layout and call-order checks shared by the combine-side entry points.
+static int check_combine_layout(mep_handle* h, int32_t layout) {
   if (layout != MEP_RANK_MAJOR && layout != MEP_EXPERT_MAJOR) return MEP_ERR_SHAPE;
   if (layout == MEP_RANK_MAJOR && !h->plan_valid) return MEP_ERR_STATE;
   if (layout == MEP_EXPERT_MAJOR && !h->em_valid) return MEP_ERR_STATE;
+  return MEP_OK;
+}
+
+static int combine_common(mep_handle* h, int32_t layout, const void* y, const float* weights,
+                          void* out, void* stream, bool fp8) {
+  if (!h) return MEP_ERR_NULL;
+  int rc = check_combine_layout(h, layout);
+  if (rc != MEP_OK) return rc;
+  if (fp8 && h->cfg.hidden_dim % 16 != 0) return MEP_ERR_SHAPE;
   const int32_t T = h->plan_T;
   if (!out) return MEP_ERR_NULL;
   if (T > 0 && (!y || !weights)) return MEP_ERR_NULL;
@@ -413,7 +424,38 @@ int mep_combine(mep_handle* h, int32_t layout, const void* y, const float* weigh
   a.T = T;
   a.H = h->cfg.hidden_dim;
   a.k = h->cfg.num_experts_per_token;
-  return hip_rc(mep::launch_combine(a, (hipStream_t)stream));
+  return hip_rc(fp8 ? mep::launch_combine_fp8(a, (hipStream_t)stream)
+                    : mep::launch_combine(a, (hipStream_t)stream));
+}
+
+int mep_combine(mep_handle* h, int32_t layout, const void* y, const float* weights, void* out,
+                void* stream) {
+  return combine_common(h, layout, y, weights, out, stream, false);
+}
+
+int mep_combine_fp8(mep_handle* h, int32_t layout, const void* y8, const float* weights,
+                    void* out, void* stream) {
+  return combine_common(h, layout, y8, weights, out, stream, true);
+}
+
+int mep_cast_fp8_direct(mep_handle* h, int32_t layout, const void* y, void* y8, void* stream) {
+  if (!h) return MEP_ERR_NULL;
+  int rc = check_combine_layout(h, layout);
+  if (rc != MEP_OK) return rc;
+  if (h->cfg.hidden_dim % 16 != 0) return MEP_ERR_SHAPE;
+  const int32_t T = h->plan_T;
+  if (T > 0 && (!y || !y8)) return MEP_ERR_NULL;
+  if ((y && !aligned16(y)) || (y8 && !aligned16(y8))) return MEP_ERR_ALIGN;
+  mep::CastArgs a{};
+  a.y = y;
+  a.y8 = y8;
+  const bool rm = layout == MEP_RANK_MAJOR;
+  a.rows = ws_ptr<int32_t>(h, rm ? h->lay.rrow : h->lay.em_row);
+  a.ufirst = rm ? ws_ptr<uint32_t>(h, h->lay.ufirst) : nullptr;
+  a.T = T;
+  a.H = h->cfg.hidden_dim;
+  a.k = h->cfg.num_experts_per_token;
+  return hip_rc(mep::launch_cast_fp8(a, (hipStream_t)stream));
 }
 
 int mep_reset(mep_handle* h, void* stream) {

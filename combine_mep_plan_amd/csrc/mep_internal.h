@@ -16,6 +16,19 @@ constexpr int kMaxTopk = 32;     // first-occurrence bits of a token fit 32 bits
 constexpr int kMaxEpr = 64;      // a row's local experts fit one 64-bit mask
 constexpr int kChunk = 64;       // tokens (or receive rows) per scan chunk = one wave
 
+// 16-byte units per received row of a payload mode: 8 bf16 values, 16 E4M3
+// codes or 32 packed E2M1 codes per unit.
+__host__ __device__ constexpr int payload_units(int quant, int H) {
+  return quant == MEP_QUANT_NONE ? H / 8
+         : (quant == MEP_QUANT_FP4_CARRY || quant == MEP_QUANT_MXFP4) ? H / 32
+                                                                       : H / 16;
+}
+
+// Modes whose rows arrive already quantised, with the caller's scale words.
+__host__ __device__ constexpr bool is_carry(int quant) {
+  return quant == MEP_QUANT_FP8_CARRY || quant == MEP_QUANT_FP4_CARRY;
+}
+
 // Expert id -> rank without a hardware divide: for e < 4096 and epr <= 64,
 // (e * m) >> 20 with m = ceil(2^20 / epr) equals e / epr (checked on the host
 // for every expert id when a handle is created).
@@ -94,6 +107,14 @@ struct CombineArgs {
   int32_t slices, slice_units;  // waves per token and 16-byte lane units per wave
 };
 
+struct CastArgs {           // E4M3 direct cast of the routed expert-output rows
+  const void* y;             // bf16 rows
+  void* y8;                  // E4M3 rows, same row indices
+  const int32_t* rows;       // [T,k] row of (t, j), -1 = none
+  const uint32_t* ufirst;    // [T] positions owning a distinct row (rank-major), or null
+  int32_t T, H, k, slices;
+};
+
 struct EmArgs {
   const void* recv_x;
   const float* recv_scales;
@@ -111,7 +132,7 @@ struct EmArgs {
   int32_t* ccnt;                // [R][CR][epr]
   uint32_t* status;
   int64_t cap_em;
-  int32_t T, H, k, R, epr, cap, CR, nb, elem_bytes, spos_base;
+  int32_t T, H, k, R, epr, cap, CR, nb, row_units, spos_base;  // row_units: 16-byte units per row
   int32_t slices;  // scatter: waves per receive row
 };
 
@@ -139,6 +160,8 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
 hipError_t launch_plan_dispatch(const PlanArgs& p, const DispatchArgs& a, hipStream_t s);
 hipError_t launch_dispatch_standard_moe(const SmArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_combine_fp8(const CombineArgs& a, hipStream_t s);  // y holds E4M3 rows
+hipError_t launch_cast_fp8(const CastArgs& a, hipStream_t s);
 hipError_t launch_to_expert_major(const EmArgs& a, hipStream_t s);
 hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int64_t n, hipStream_t s);
 hipError_t launch_probe_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t s);

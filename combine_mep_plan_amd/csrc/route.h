@@ -70,42 +70,4 @@ __device__ __forceinline__ uint64_t lane_value64(uint64_t v, int lane) {
   return (uint64_t)lo | ((uint64_t)hi << 32);
 }
 
-// FP8 block quantisation of one lane's 16 columns (in0: columns 0..7, in1:
-// 8..15, bf16) into 16 OCP E4M3 codes: the 8 lanes of a 128-column block share
-// scale = amax / 448 (fp32 division); codes are E4M3(x / scale) by correctly
-// rounded division and the packed convert (round to nearest even); an all-zero
-// block gives scale 0 and signed-zero codes.
-__device__ __forceinline__ u32x4 quant16(u32x4 in0, u32x4 in1, float& scale) {
-  float f[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = bf16_lo(in0[i]);
-    f[2 * i + 1] = bf16_hi(in0[i]);
-    f[8 + 2 * i] = bf16_lo(in1[i]);
-    f[8 + 2 * i + 1] = bf16_hi(in1[i]);
-  }
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
-  amax = fmaxf(amax, __shfl_xor(amax, 1));
-  amax = fmaxf(amax, __shfl_xor(amax, 2));
-  amax = fmaxf(amax, __shfl_xor(amax, 4));
-  const float s = amax / 448.0f;
-  scale = s;
-  uint32_t w[4];
-  if (s == 0.0f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = ((__float_as_uint(f[4 * i]) >> 31) << 7) |
-             ((__float_as_uint(f[4 * i + 1]) >> 31) << 15) |
-             ((__float_as_uint(f[4 * i + 2]) >> 31) << 23) |
-             ((__float_as_uint(f[4 * i + 3]) >> 31) << 31);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = pack_e4m3x4(f[4 * i] / s, f[4 * i + 1] / s, f[4 * i + 2] / s, f[4 * i + 3] / s);
-  }
-  return u32x4{w[0], w[1], w[2], w[3]};
-}
-
 }  // namespace mep

@@ -24,6 +24,7 @@
 // When the histograms are large (chunks x experts above 32768), one workgroup
 // first turns them into prefixes and offsets ("offsets" below) and the route
 // workgroups read those instead of summing the histograms each.
+#include "payload.h"
 #include "route.h"
 
 namespace mep {
@@ -293,51 +294,36 @@ __global__ __launch_bounds__(256) void sm_scatter_kernel(SmArgs a) {
   const int t = g / a.slices, sl = g - t * a.slices;
   if (t >= a.T) return;
   // this wave's slice of the row: loads go out first
-  const bool fp8_out = QUANT != MEP_QUANT_NONE;
-  const int nu = fp8_out ? a.H / 16 : a.H / 8;  // 16-byte output units per row
+  const int nu = payload_units(QUANT, a.H);
   const int v = sl * kWave + lane;
   const bool on = v < nu;
-  u32x4 in0 = u32x4{0, 0, 0, 0}, in1 = u32x4{0, 0, 0, 0};
-  if (on) {
-    if (QUANT == MEP_QUANT_FP8_E4M3_BLOCK128) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(a.x) + (size_t)t * (a.H / 8);
-      in0 = src[2 * v];
-      in1 = src[2 * v + 1];
-    } else {
-      const u32x4* src = reinterpret_cast<const u32x4*>(a.x) + (size_t)t * nu;
-      in0 = src[v];
-    }
-  }
+  Unit<QUANT> unit;
+  unit.load(a.x, t, a.H, v, on);
   // the token's rows, placed by the route launch (-1: no row)
   int rows[KMAX];
   const int32_t* rr = a.em_row + (size_t)t * a.k;
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) rows[j] = j < a.k ? rr[j] : -1;
   float scale = 0.0f;
-  u32x4 q = in0;
-  if (QUANT == MEP_QUANT_FP8_E4M3_BLOCK128) q = quant16(in0, in1, scale);
-  const int nb = a.H / 128;
+  uint32_t e8 = 0;
+  const u32x4 q = unit.convert(scale, e8);
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
     const int pos = rows[j];
     if (pos < 0) continue;
     if (on) {
       store_nt(reinterpret_cast<u32x4*>(a.em_x) + (size_t)pos * nu + v, q);
-      if (QUANT == MEP_QUANT_FP8_E4M3_BLOCK128 && (v & 7) == 0)
-        a.em_scales[(size_t)pos * nb + (v >> 3)] = scale;
+      store_unit_scale<QUANT>(a.em_scales, (size_t)pos, a.H, v, scale, e8);
     }
-    if (QUANT == MEP_QUANT_FP8_CARRY && sl == 0) {
-      for (int i = lane; i < a.scale_dim; i += kWave)
-        a.em_scales[(size_t)pos * a.scale_dim + i] = a.x_scales[(size_t)t * a.scale_dim + i];
-    }
+    if (is_carry(QUANT) && sl == 0)
+      copy_scale_row(a.em_scales, (size_t)pos, a.x_scales, t, a.scale_dim, lane);
   }
 }
 
 template <int QUANT>
 hipError_t launch_scatter(const SmArgs& a0, hipStream_t s) {
   SmArgs a = a0;
-  const int nu = QUANT != MEP_QUANT_NONE ? a.H / 16 : a.H / 8;
-  a.slices = (nu + kWave - 1) / kWave;
+  a.slices = (payload_units(QUANT, a.H) + kWave - 1) / kWave;
   const int blocks = (int)(((int64_t)a.T * a.slices + 3) / 4);
   if (a.k <= 8) sm_scatter_kernel<QUANT, 8><<<blocks, 256, 0, s>>>(a);
   else sm_scatter_kernel<QUANT, kMaxTopk><<<blocks, 256, 0, s>>>(a);
@@ -377,6 +363,8 @@ hipError_t launch_dispatch_standard_moe(const SmArgs& a, hipStream_t s) {
   switch (a.quant) {
     case MEP_QUANT_FP8_E4M3_BLOCK128: return launch_scatter<MEP_QUANT_FP8_E4M3_BLOCK128>(a, s);
     case MEP_QUANT_FP8_CARRY: return launch_scatter<MEP_QUANT_FP8_CARRY>(a, s);
+    case MEP_QUANT_FP4_CARRY: return launch_scatter<MEP_QUANT_FP4_CARRY>(a, s);
+    case MEP_QUANT_MXFP4: return launch_scatter<MEP_QUANT_MXFP4>(a, s);
     default: return launch_scatter<MEP_QUANT_NONE>(a, s);
   }
 }

@@ -62,6 +62,22 @@ extern "C" {
                                          ("Choosing an EP API and backend": the
                                          HIP backend carries already-quantized
                                          FP8 payloads)                           */
+#define MEP_QUANT_FP4_CARRY 3         /* as MEP_QUANT_FP8_CARRY for FP4 rows: H/2
+                                         bytes per row (two E2M1 codes a byte),
+                                         scale_dim 32-bit scale words per row,
+                                         both carried unchanged (same passage) */
+#define MEP_QUANT_MXFP4 4             /* dispatch payload: OCP MX FP4 -- per 32
+                                         columns an E8M0 scale byte, shared
+                                         exponent floor(log2(amax)) - 2 clamped
+                                         to [-127, 127]; codes E2M1(x / 2^exp),
+                                         round to nearest even, saturating at 6,
+                                         even column in the low nibble; all-zero
+                                         block: scale byte 0.  Rows of H/2
+                                         bytes; the H/32 scale bytes of a row
+                                         fill its H/128 scale words ("Choosing
+                                         an EP API and backend": FP4 conversion
+                                         kernels on gfx950; the block format is
+                                         this library's reading)                */
 #define MEP_RANK_MAJOR 0              /* combine input: [R, cap, H] bf16         */
 #define MEP_EXPERT_MAJOR 1            /* combine input: [cap_em, H] bf16         */
 
@@ -73,9 +89,9 @@ extern "C" {
  */
 typedef struct mep_config {
   int32_t hidden_dim;                 /* H: > 0, multiple of 8; of 128 when quantising, of
-                                         16 when carrying E4M3                           */
-  int32_t scale_dim;                  /* 0 for bf16; H/128 when quantising; any >= 0 scale
-                                         columns per row when carrying                   */
+                                         16 when carrying E4M3, of 32 when carrying FP4  */
+  int32_t scale_dim;                  /* 32-bit scale words per row: 0 for bf16; H/128
+                                         when quantising; any >= 0 when carrying         */
   int32_t num_experts_per_rank;       /* epr: 1..64                                       */
   int32_t num_experts_per_token;      /* k: 1..32, k <= R*epr                              */
   int32_t max_num_inp_token_per_rank; /* cap: receive rows per rank and the largest T, >= 1 */
@@ -135,10 +151,13 @@ int mep_plan(mep_handle *h, const int32_t *indices, int32_t T, int32_t *recv_cou
  *                         of x[T,H] copied;
  *   recv_scales[r, s, :]  the block scales ([R,cap,H/128] fp32), or the carried
  *                         scales[t, :] ([R,cap,scale_dim]); NULL for bf16;
+ * MEP_QUANT_MXFP4 writes [R,cap,H/2] packed E2M1 bytes and [R,cap,H/32] E8M0
+ * bytes (= H/128 words); MEP_QUANT_FP4_CARRY copies H/2 bytes of x and the
+ * scale_dim words of scales[t, :];
  *   recv_weights[r, s, :] the token's k weights (fp32 [R,cap,k]);
  *   recv_indices[r, s, :] the token's k expert ids (int32 [R,cap,k]).
- * scales is the caller's [T,scale_dim] fp32 input for MEP_QUANT_FP8_CARRY and
- * is ignored otherwise.  Rows past recv_counts[r] are not written.  Needs a
+ * scales is the caller's [T,scale_dim] 32-bit input for the carry modes and is
+ * ignored otherwise.  Rows past recv_counts[r] are not written.  Needs a
  * valid plan; x, weights, scales and indices hold the planned T tokens.
  */
 int mep_dispatch(mep_handle *h, const void *x, const float *weights, const float *scales,
@@ -168,8 +187,8 @@ int mep_plan_dispatch(mep_handle *h, const int32_t *indices, int32_t T, int32_t 
  *                       multiples of 128 rows (int32, E+1 entries,
  *                       em_offsets[E] = rows used);
  *   em_x[em_offsets[e] + i, :]      the i-th such receive row (ascending
- *                       receive slot), same element type as recv_x;
- *   em_scales[...]      its scales (FP8 only, else NULL);
+ *                       receive slot), in the row format of recv_x;
+ *   em_scales[...]      its scale words (scale_dim per row; NULL when 0);
  *   em_src_pos[...]     its src_token_pos.
  * Padding rows are not written.  cap_em is the row capacity of em_x /
  * em_scales / em_src_pos; T*k + 127*E always suffices.  Rows past cap_em are
@@ -217,6 +236,21 @@ int mep_dispatch_standard_moe(mep_handle *h, const int32_t *indices, int32_t T, 
  */
 int mep_combine(mep_handle *h, int32_t layout, const void *y, const float *weights, void *out,
                 void *stream);
+
+/*
+ * FP8 direct-cast combine payload (the intra-node tuning matrix of the MORI
+ * README / EPv2 guide pairs quant type fp8_direct_cast with a bf16 combine):
+ * mep_cast_fp8_direct writes y8 = OCP E4M3 of each bf16 value of the rows the
+ * current plan routes (round to nearest even, saturating at +-448, no scale;
+ * NaN inputs are not supported), y and y8 in the layout of mep_combine with 1
+ * byte per value (y8 is [R,cap,H] or [cap_em,H] bytes; other rows are not
+ * touched).  mep_combine_fp8 is mep_combine on such E4M3 rows: each value is
+ * decoded exactly to fp32 and accumulated as above.  Same state rules as
+ * mep_combine.
+ */
+int mep_cast_fp8_direct(mep_handle *h, int32_t layout, const void *y, void *y8, void *stream);
+int mep_combine_fp8(mep_handle *h, int32_t layout, const void *y8, const float *weights,
+                    void *out, void *stream);
 
 /*
  * Reset between iterations ("MORI-EP User Guide" section 3 reset()):

@@ -36,11 +36,13 @@ class Workload:
     experts_per_rank: int  # num_experts_per_rank
     topk: int              # num_experts_per_token
     cap: int               # max_num_inp_token_per_rank
-    quant: str             # "none" or "fp8"  (OCP E4M3, per-128-column fp32 scales)
+    quant: str             # "none", "fp8" (OCP E4M3, per-128-column fp32 scales) or
+                           # "mxfp4" (OCP MX FP4, per-32-column E8M0 scales)
     routing: str           # "uniform" or "zipf"
     expert: str            # expert stand-in: "identity", "dequant_half", "dequant"
     layout: str            # "rank_major" or "expert_major"
     zipf_s: float = 1.2
+    combine: str = "bf16"  # combine payload: "bf16", or "fp8_direct" (E4M3 cast, no scale)
 
     @property
     def experts(self) -> int:
@@ -48,7 +50,7 @@ class Workload:
 
     @property
     def scale_dim(self) -> int:
-        return self.hidden // 128 if self.quant == "fp8" else 0
+        return self.hidden // 128 if self.quant in ("fp8", "mxfp4") else 0
 
     @property
     def cap_em(self) -> int:
@@ -72,6 +74,12 @@ WORKLOADS = {
     "skew": Workload("skew", 4096, 7168, 16, 16, 8, 4096, "none", "zipf", "identity", "rank_major"),
     # standard-MoE layout: FP8 dispatch, expert-major conversion, combine from it
     "stdmoe": Workload("stdmoe", 4096, 7168, 32, 8, 8, 4096, "fp8", "uniform", "dequant", "expert_major"),
+    # the prefill shape with the tuning matrix's low-precision pairings: FP4
+    # dispatch with a bf16 combine, and an FP8 direct-cast combine payload
+    "prefill_mxfp4": Workload("prefill_mxfp4", 4096, 7168, 8, 32, 8, 4096, "mxfp4", "uniform",
+                              "dequant_half", "rank_major"),
+    "prefill_fp8direct": Workload("prefill_fp8direct", 4096, 7168, 8, 32, 8, 4096, "fp8",
+                                  "uniform", "dequant_half", "rank_major", combine="fp8_direct"),
 }
 
 
