@@ -267,6 +267,40 @@ def test_fp8_direct_cast_and_combine_expert_major(T, sample):
     _say(f"[fp8 direct] EM T={T}: {stats}")
 
 
+@pytest.mark.parametrize("R,epr,k", [(6, 4, 12), (4, 8, 32)])
+def test_fp8_direct_and_mxfp4_wide_topk(R, epr, k):
+    # top-k above 8: the cast walks a token's rows in groups of 8 and the combine
+    # takes its wide variant; ranks shared by several experts repeat rows
+    wl = dataclasses.replace(WORKLOADS["prefill"].with_tokens(150, cap=150), ranks=R,
+                             experts_per_rank=epr, topk=k, hidden=512)
+    _say(f"[wide] R={R} epr={epr} k={k}")
+    inp = make_inputs(wl, 61)
+    cap, H = wl.cap, wl.hidden
+    # MXFP4 dispatch
+    m4 = _mep(wl, M.MEP_QUANT_MXFP4)
+    got = _run_rank_major(wl, m4, dev(inp["x"]), dev(inp["weights"]), dev(inp["indices"]),
+                          None, True, H // 128)
+    pl = O.plan(inp["indices"], R, epr, cap)
+    d = O.dispatch(inp["x"], inp["weights"], inp["indices"], pl, R, epr, cap, 4, fill=SENT8)
+    _check_rank_major(wl, inp, pl, d, got, H // 128)
+    # direct cast and E4M3 combine
+    m = _mep(wl, M.MEP_QUANT_NONE, 0)
+    idx, w = dev(inp["indices"]), dev(inp["weights"])
+    M.mep_plan(m.h, idx, wl.tokens, torch.empty(R, dtype=torch.int32, device="cuda"),
+               torch.empty((R, cap), dtype=torch.int32, device="cuda"))
+    y = _expert_outputs((R * cap, H), 61)
+    y8 = torch.full((R, cap, H), SENT8, dtype=torch.uint8, device="cuda")
+    M.mep_cast_fp8_direct(m.h, M.MEP_RANK_MAJOR, dev(y), y8)
+    out = torch.empty((wl.tokens, H), dtype=torch.int16, device="cuda")
+    M.mep_combine_fp8(m.h, M.MEP_RANK_MAJOR, y8, w, out)
+    torch.cuda.synchronize()
+    used = (np.arange(cap)[None, :] < pl["recv_counts"][:, None]).reshape(-1)
+    tok_rows = (inp["indices"] // epr) * cap + pl["slot"]
+    ref_fn = lambda y8r: O.combine(y8r.reshape(R, cap, H), inp["weights"], inp["indices"],  # noqa: E731
+                                   pl, epr, cap)
+    _check_cast_combine(y, y8, out, used, tok_rows, ref_fn, wl.tokens, None)
+
+
 def test_fp8_direct_state_and_shape_rules():
     wl = WORKLOADS["tiny"]
     m = _mep(wl, M.MEP_QUANT_NONE, 0)

@@ -105,6 +105,19 @@ SMALL = [
                           "rank_major"), (0,)),
     ("wide64", Workload("wide64", 100, 256, 64, 2, 8, 100, "fp8", "uniform", "dequant_half",
                         "rank_major"), (0,)),
+    # top-k up to the maximum of 32, FP8 and expert-major with the wide variants
+    ("top20_fp8", Workload("top20_fp8", 300, 512, 16, 4, 20, 300, "fp8", "uniform",
+                           "dequant_half", "rank_major"), (0,)),
+    ("top32_em", Workload("top32_em", 200, 256, 8, 8, 32, 200, "fp8", "uniform", "dequant",
+                          "expert_major"), (0,)),
+    # the largest configuration: 64 ranks x 64 experts, top-32
+    ("max_cfg", Workload("max_cfg", 300, 256, 64, 64, 32, 300, "fp8", "uniform", "dequant",
+                         "expert_major"), (0,)),
+    # the narrowest rows: one 16-byte unit of bf16, one FP8 scale block
+    ("h8_bf16", Workload("h8_bf16", 200, 8, 4, 4, 4, 200, "none", "uniform", "identity",
+                         "rank_major"), (0,)),
+    ("h128_fp8", Workload("h128_fp8", 200, 128, 4, 4, 4, 200, "fp8", "uniform", "dequant_half",
+                          "expert_major"), (0,)),
 ]
 
 

@@ -175,7 +175,8 @@ def test_standard_moe_matches_oracle(label, name, T, mode, sd):
 
 
 @pytest.mark.parametrize("R,epr,k,T", [(64, 64, 8, 2000), (7, 13, 5, 3000), (4, 1, 1, 1500),
-                                        (2, 3, 6, 130)])
+                                        (2, 3, 6, 130), (64, 64, 32, 500), (3, 5, 9, 777),
+                                        (8, 8, 20, 300)])
 def test_standard_moe_expert_counts(R, epr, k, T):
     # expert counts that split the per-expert prefix work differently: 4096
     # experts (one work item each), 91 (eight items per expert), top-1, all
