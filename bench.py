@@ -425,7 +425,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path)", file=sys.stderr)
+              "(the library drives one device; the sharded design is not built)", file=sys.stderr)
         return 2
 
     import torch
