@@ -282,6 +282,8 @@ class Runner:
             self.step(self.sets[i % len(self.sets)])
         times = {"step": self.loop(self.step, steps)}
         assert self.M.mep_get_status(self.m.h, self.stream) == 0
+        # run-to-run spread: the same loop repeated (not part of `value`)
+        self.step_repeats = [round(self.loop(self.step, steps) * 1e3, 2) for _ in range(4)]
         times["plan_dispatch"] = self.loop(self.plan_dispatch, steps)
         if self.em:
             times["to_expert_major"] = self.loop(self.to_em, steps)
@@ -298,12 +300,21 @@ class Runner:
             times["dispatch_standard_moe"] = self.loop(self.standard_moe, steps)
         self.M.mep_reset(self.m.h, self.stream)
         nbytes = self.bytes()
+        # the pages' own bandwidth figure: payload bytes received (dispatch) or
+        # sent back (combine) per second; context, not the roofline
+        wl = self.wl
+        payload = {"dispatch": self.U * row_bytes(wl.hidden, self.quant),
+                   "combine": (self.Uem if self.em else self.U) * wl.hidden * 2}
+        payload["plan_dispatch"] = payload["dispatch"]
         ops = {}
         for name, ms in times.items():
             o = {"us": round(ms * 1e3, 2), "bytes": nbytes[name]}
             o["GBps"] = round(o["bytes"] / (ms * 1e-3) / 1e9, 1)
             o["frac"] = round(o["GBps"] / HBM_PEAK_GBS, 4)
+            if name in payload:
+                o["payload_GBps"] = round(payload[name] / (ms * 1e-3) / 1e9, 1)
             ops[name] = o
+        ops["step"]["repeats_us"] = self.step_repeats
         return ops
 
 
@@ -368,6 +379,13 @@ def time_decode(M, torch, wl, inp, reps, warmup):
     return out
 
 
+def env_info(torch):
+    p = torch.cuda.get_device_properties(0)
+    return {"device": p.name, "arch": getattr(p, "gcnArchName", ""),
+            "compute_units": p.multi_processor_count, "hip": torch.version.hip,
+            "torch": torch.__version__, "host_cpus": len(os.sched_getaffinity(0))}
+
+
 def copy_ceiling(torch, nbytes=512 << 20, reps=20):
     """Read+write rate of a plain device-to-device copy over rotating 512 MiB
     buffers (also the calibration kernel for the traffic counters)."""
@@ -417,7 +435,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--sets", type=int, default=4)
     ap.add_argument("--decode-reps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -504,6 +522,7 @@ def main():
         "roofline": roofline,
         "workloads": extra,
         "cpu_baseline": cpu,
+        "env": env_info(torch),
     }
     print(json.dumps(line), flush=True)
     return 0
