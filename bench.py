@@ -85,14 +85,17 @@ def combine_em_bytes(T, H, k):
 
 
 def src_digest(name):
-    """Digest of a kernel source file and every header beside it (a change to
-    a shared header changes the kernel too)."""
+    """Digest of the code of a kernel source file and of every header beside it
+    (a change to a shared header changes the kernel too).  Comments and blank
+    space are left out, so that a comment edit keeps the counters valid."""
     import glob
+    import re
     csrc = os.path.join(ROOT, "combine_mep_plan_amd", "csrc")
     h = hashlib.sha256()
     for p in [os.path.join(csrc, name)] + sorted(glob.glob(os.path.join(csrc, "*.h"))):
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p) as f:
+            code = re.sub(r"/\*.*?\*/|//[^\n]*", "", f.read(), flags=re.S)
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -440,6 +443,8 @@ def main():
     ap.add_argument("--decode-reps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="prefill and decode only")
+    ap.add_argument("--extra", default="skew,stdmoe,prefill_mxfp4,prefill_fp8direct",
+                    help="comma-separated extra workloads to measure after prefill and decode")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -483,8 +488,9 @@ def main():
 
     extra = {}
     if not args.no_extra:
-        for name, nsets in (("skew", 3), ("stdmoe", 2), ("prefill_mxfp4", 3),
-                            ("prefill_fp8direct", 3)):
+        nsets_of = {"skew": 3, "stdmoe": 2, "prefill_mxfp4": 3, "prefill_fp8direct": 3}
+        for name in [n for n in args.extra.split(",") if n]:
+            nsets = nsets_of.get(name, 2)
             xwl = WORKLOADS[name]
             say(f"{name}: T={xwl.tokens} R={xwl.ranks} epr={xwl.experts_per_rank}")
             r = Runner(M, torch, xwl, make_inputs(xwl, 0), nsets)

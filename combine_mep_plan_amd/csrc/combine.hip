@@ -101,9 +101,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Every top-k position loads its row, also when it shares a rank row with an
-// earlier position (the repeat is a cache hit): selecting among already
-// loaded registers, as the bf16 kernel does, here made the compiler wait on
-// each load in turn.
+// earlier position (about half of such repeats hit the caches): selecting
+// among already loaded registers, as the bf16 kernel does, here made the
+// compiler wait on each load in turn.
 template <int KMAX>
 __global__ __launch_bounds__(256) void combine_fp8_kernel(CombineArgs a) {
   const int lane = threadIdx.x & 63;
