@@ -57,11 +57,21 @@ __device__ __forceinline__ WaveRoute wave_route(const DispatchArgs& a, int t, in
   const int tok = c * kChunk + lane;
   w.base = 0;
   if (MODE == kCounts) {
+    // the chunk's in-block prefix and the first four earlier blocks' totals go
+    // out together with the mask load (a rolled loop would wait on each);
+    // blocks past the fourth (batches over 4096 tokens) are summed after
+    const int nb = c / 16;
+    int acc = 0, v[4] = {0, 0, 0, 0};
+    if (lane < a.R) {
+      acc = a.chunk_cnt[(size_t)c * a.R + lane];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (q < nb) v[q] = a.block_cnt[(size_t)q * a.R + lane];
+    }
     w.mask_l = tok < a.T ? a.mask[tok] : 0ull;
     if (lane < a.R) {
-      int acc = a.chunk_cnt[(size_t)c * a.R + lane];
-      for (int b = 0; b < c / 16; ++b) acc += a.block_cnt[(size_t)b * a.R + lane];
-      w.base = acc;
+      for (int b = 4; b < nb; ++b) acc += a.block_cnt[(size_t)b * a.R + lane];
+      w.base = acc + v[0] + v[1] + v[2] + v[3];
     }
   } else {
     int ids[KMAX];

@@ -325,6 +325,19 @@ def test_fused_plan_dispatch_64_ranks(T):
     assert M.mep_get_status(g.m.h) == 0
 
 
+@pytest.mark.parametrize("T,R", [(5200, 8), (9000, 8), (8193, 33)])
+def test_fused_plan_dispatch_long_batches(T, R):
+    # more than four 16-chunk count blocks before a token's chunk (the per-wave
+    # base sums the later blocks after the first four)
+    wl = Workload("long", T, 256, R, 4, 8, T, "fp8", "uniform", "dequant_half", "rank_major")
+    inp = make_inputs(wl, 2)
+    for fused in (True, False):
+        g = gpu_plan_dispatch(wl, inp, src_rank=1, fused=fused)
+        pl, d = oracle_plan_dispatch(wl, inp, src_rank=1)
+        check_plan_dispatch(wl, inp, g, pl, d)
+        assert M.mep_get_status(g.m.h) == 0
+
+
 @pytest.mark.parametrize("T", [128, 700])
 def test_hip_graph_capture_replay(T):
     # plan+dispatch and combine captured once in a HIP graph, replayed with new
