@@ -117,11 +117,26 @@ __device__ __forceinline__ void write_route(const DispatchArgs& a, const WaveRou
   }
 }
 
-__device__ __forceinline__ void store_meta(const DispatchArgs& a, int t, int row, int lane) {
-  if (lane < a.k) {
-    a.recv_w[(size_t)row * a.k + lane] = a.w[(size_t)t * a.k + lane];
-    a.recv_idx[(size_t)row * a.k + lane] = a.idx[(size_t)t * a.k + lane];
+// What slice 0 writes with every row of a token besides the payload: its k
+// weights and ids and, carrying, the caller's scale words.  Loaded once per
+// token, before the stores: on this architecture a wait for a load inside the
+// store loop also waits for every store issued before it.
+struct TokenMeta {
+  float w;     // lane < k: weight
+  int32_t id;  // lane < k: expert id
+  float sc;    // carrying, lane < scale_dim: scale word (the first 64)
+};
+
+template <int QUANT>
+__device__ __forceinline__ TokenMeta load_meta(const DispatchArgs& a, int t, int sl, int lane) {
+  TokenMeta m{0.0f, 0, 0.0f};
+  if (sl == 0 && lane < a.k) {
+    m.w = a.w[(size_t)t * a.k + lane];
+    m.id = a.idx[(size_t)t * a.k + lane];
   }
+  if (is_carry(QUANT) && sl == 0 && lane < a.scale_dim)
+    m.sc = a.x_scales[(size_t)t * a.scale_dim + lane];
+  return m;
 }
 
 // QUANT: a MEP_QUANT_* payload mode (see payload.h).
@@ -158,19 +173,33 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
   float scale = 0.0f;
   uint32_t e8 = 0;
   const u32x4 q = unit.convert(scale, e8);
+  const TokenMeta meta = load_meta<QUANT>(a, t, sl, lane);
   auto emit = [&](int row) {
     if (on) {
       store_nt(reinterpret_cast<u32x4*>(a.recv_x) + (size_t)row * nu + v, q);
       store_unit_scale<QUANT>(a.recv_scales, (size_t)row, a.H, v, scale, e8);
     }
     if (sl == 0) {
-      store_meta(a, t, row, lane);
-      if (is_carry(QUANT)) copy_scale_row(a.recv_scales, (size_t)row, a.x_scales, t, a.scale_dim, lane);
+      if (lane < a.k) {
+        a.recv_w[(size_t)row * a.k + lane] = meta.w;
+        a.recv_idx[(size_t)row * a.k + lane] = meta.id;
+      }
+      if (is_carry(QUANT)) {
+        if (lane < a.scale_dim) a.recv_scales[(size_t)row * a.scale_dim + lane] = meta.sc;
+        for (int i = lane + kWave; i < a.scale_dim; i += kWave)  // rows over 64 words
+          a.recv_scales[(size_t)row * a.scale_dim + i] = a.x_scales[(size_t)t * a.scale_dim + i];
+      }
     }
   };
   if (MODE == kRoute) {
+    // the token's rows, loaded before the first store
     const int32_t* rr = a.rrow + (size_t)t * a.k;
-    for (uint32_t m = first; m; m &= m - 1) emit(rr[__builtin_ctz(m)]);
+    int rows[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) rows[j] = j < a.k && (first >> j & 1u) ? rr[j] : -1;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (rows[j] >= 0) emit(rows[j]);
   } else {
     for (uint64_t m = w.tok_mask; m; m &= m - 1) {
       const int r = __builtin_ctzll(m);
