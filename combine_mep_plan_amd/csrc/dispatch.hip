@@ -73,6 +73,22 @@ __device__ __forceinline__ WaveRoute wave_route(const DispatchArgs& a, int t, in
       for (int b = 4; b < nb; ++b) acc += a.block_cnt[(size_t)b * a.R + lane];
       w.base = acc + v[0] + v[1] + v[2] + v[3];
     }
+  } else if (KMAX <= 8) {
+    // the token's chunk and the (at most three) earlier chunks: every id load
+    // goes out before any mask is formed
+    constexpr int kPrev = kInlinePlanTokens / kChunk - 1;
+    int ids[KMAX], prev[kPrev][KMAX];
+    if (tok < a.T) load_ids<KMAX>(a.idx, tok, a.k, ids);
+#pragma unroll
+    for (int q = 0; q < kPrev; ++q)
+      if (q < c) load_ids<KMAX>(a.idx, q * kChunk + lane, a.k, prev[q]);
+#pragma unroll
+    for (int q = 0; q < kPrev; ++q) {
+      if (q >= c) continue;  // uniform
+      uint32_t ignore = 0;
+      w.base += ranks_popcount(token_mask<KMAX>(prev[q], a.k, a.E, a.rdiv, ignore), a.R, lane);
+    }
+    w.mask_l = tok < a.T ? token_mask<KMAX>(ids, a.k, a.E, a.rdiv, st) : 0ull;
   } else {
     int ids[KMAX];
     for (int cc = 0; cc < c; ++cc) {

@@ -11,11 +11,9 @@
 
 namespace mep {
 
-// Load token t's top-k ids (k <= KMAX) and build its destination-rank mask.
-// Returns 0 for a token with a bad id; sets MEP_DEV_* bits in st.
+// Load token t's top-k ids (k <= KMAX).
 template <int KMAX>
-__device__ __forceinline__ uint64_t load_token(const int32_t* indices, int t, int k, int E,
-                                               RankDiv rdiv, int (&ids)[KMAX], uint32_t& st) {
+__device__ __forceinline__ void load_ids(const int32_t* indices, int t, int k, int (&ids)[KMAX]) {
   const int32_t* p = indices + (size_t)t * k;
   if (KMAX == 8 && k == 8) {
     const int4 v0 = reinterpret_cast<const int4*>(p)[0];
@@ -26,6 +24,13 @@ __device__ __forceinline__ uint64_t load_token(const int32_t* indices, int t, in
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) ids[j] = j < k ? p[j] : 0;
   }
+}
+
+// A token's destination-rank mask from its ids; 0 for a token with a bad id.
+// Sets MEP_DEV_* bits in st.
+template <int KMAX>
+__device__ __forceinline__ uint64_t token_mask(const int (&ids)[KMAX], int k, int E, RankDiv rdiv,
+                                               uint32_t& st) {
   uint64_t mask = 0;
   bool bad = false, dup = false;
 #pragma unroll
@@ -44,6 +49,14 @@ __device__ __forceinline__ uint64_t load_token(const int32_t* indices, int t, in
   if (bad) { st |= MEP_DEV_BAD_INDEX; return 0; }
   if (dup) st |= MEP_DEV_DUP_EXPERT;
   return mask;
+}
+
+// Both: token t's ids and destination-rank mask.
+template <int KMAX>
+__device__ __forceinline__ uint64_t load_token(const int32_t* indices, int t, int k, int E,
+                                               RankDiv rdiv, int (&ids)[KMAX], uint32_t& st) {
+  load_ids<KMAX>(indices, t, k, ids);
+  return token_mask<KMAX>(ids, k, E, rdiv, st);
 }
 
 // Lane r receives the number of lanes whose mask has bit r (0 in lanes >= R).
