@@ -444,7 +444,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--sets", type=int, default=4)
     ap.add_argument("--decode-reps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
