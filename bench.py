@@ -12,13 +12,15 @@ ways), the skewed-routing workload (Zipf 1.2, 16 ranks) and the standard-MoE
 workload (FP8 dispatch, expert-major conversion, combine from it; and the
 single-call standard-MoE dispatch followed by the same combine), and the
 prefill shape with an MXFP4 dispatch payload and with the FP8 direct-cast
-combine payload.  Inputs are
-synthetic and resident in HBM; expert outputs are produced once, before
-timing, by the stand-in expert.  Buffer sets rotate so no step finds its data
-in the 256 MB Infinity Cache.  Kernel durations come from back-to-back loops
-of one call each between two HIP events on the library's stream.
+combine payload.  Inputs are synthetic and resident in HBM; expert outputs are
+produced once, before timing, by the stand-in expert.  Buffer sets rotate so
+no step finds its data in the 256 MB Infinity Cache.  Kernel durations come
+from back-to-back loops of one call each between two HIP events on the
+library's stream.  The oracle's own rate on a token sample of the prefill
+workload is reported beside the GPU's (cpu_baseline).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+                    [--no-extra | --extra skew,stdmoe,prefill_mxfp4,prefill_fp8direct]
 """
 
 from __future__ import annotations

@@ -11,9 +11,10 @@
 //
 // A row is cut into slices of 2 x 16 bytes per lane (2 KiB per wave); one wave
 // handles one (token, slice), so a 4096-token batch runs ~29k short waves.
-// Each distinct expert-output row is loaded once (positions that share a rank
-// row reuse its registers) with non-temporal loads -- the rows are read
-// exactly once -- and all of a slice's loads are issued before the FMAs.
+// Each distinct expert-output row is loaded once (for top-k up to 8, positions
+// that share a rank row reuse its registers; wider top-k loads each position's
+// row) with non-temporal loads -- the rows are read exactly once -- and all of
+// a slice's loads are issued before the FMAs.
 //
 // FP8 direct-cast payload (the intra-node tuning matrix pairs quant type
 // fp8_direct_cast with a bf16 combine; the cast rule -- OCP E4M3, no scale,

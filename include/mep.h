@@ -9,8 +9,8 @@
  * rank e / num_experts_per_rank.
  *
  * Conventions (every entry point):
- *   - Pointers named x, recv_*, y, out, em_*, indices, weights, recv_counts,
- *     src_token_pos and workspace are DEVICE pointers, caller-owned, borrowed
+ *   - Pointers named x, scales, recv_*, y, y8, out, em_*, indices, weights,
+ *     recv_counts, src_token_pos and workspace are DEVICE pointers, caller-owned, borrowed
  *     only for the duration of the asynchronous call on `stream`
  *     (a hipStream_t passed as void*; NULL = the null stream).  The library
  *     never allocates or frees device memory and never synchronises, except
@@ -24,6 +24,10 @@
  *   - A handle is not thread-safe; use one handle per stream.  Calls on one
  *     handle must be issued on one stream (or externally ordered).
  *   - Layouts are row-major and dense: [T,H] means row t at offset t*H.
+ *   - Apart from mep_get_status, the calls launch kernels only (no memset,
+ *     copy or host wait), so a sequence of them can be captured into a HIP
+ *     graph; a replay reuses the handle state of the capture (its plan and its
+ *     status word).
  */
 #ifndef MEP_H
 #define MEP_H
