@@ -22,7 +22,8 @@ from oracle import oracle as O
 from synthetic import WORKLOADS, Workload, make_inputs
 
 from _gpu_harness import (SENT32, bf16_ulp_diff, check_combine, check_plan_dispatch, dev,
-                          gpu_plan_dispatch, host, oracle_plan_dispatch, run_full)
+                          gpu_plan_dispatch, host, oracle_plan_dispatch, run_full,
+                          stand_in_oracle)
 
 pytestmark = pytest.mark.gpu
 
@@ -377,3 +378,38 @@ def test_hip_graph_capture_replay(T):
         ref = O.combine(yo, new["weights"], new["indices"], pl, epr, cap)
         check_combine(host(out, np.uint16), ref)
     assert M.mep_get_status(g.m.h) == 0
+
+
+def test_two_handles_on_two_streams():
+    # two handles, each bound to its own (default-priority) stream, with their
+    # calls interleaved on the host: no state is shared between handles, and
+    # each stream's work matches the oracle
+    wls = [_variant("prefill", tokens=500, cap=512), _variant("skew", tokens=300, cap=300)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    runs = []
+    for i, wl in enumerate(wls):
+        inp = make_inputs(wl, 20 + i)
+        with torch.cuda.stream(streams[i]):
+            g = gpu_plan_dispatch(wl, inp, src_rank=i, fused=bool(i))
+        runs.append((wl, inp, g))
+    outs = []
+    for i, (wl, inp, g) in enumerate(runs):
+        with torch.cuda.stream(streams[i]):
+            y = g.recv_x if wl.quant == "none" else None
+            if y is None:
+                q = g.recv_x.view(torch.float8_e4m3fn).float()
+                y = ((q * g.recv_s.repeat_interleave(128, dim=-1)) * 0.5).to(torch.bfloat16) \
+                    .view(torch.int16)
+            out = torch.empty((wl.tokens, wl.hidden), dtype=torch.int16, device="cuda")
+            M.mep_combine(g.m.h, M.MEP_RANK_MAJOR, y, g.w, out)
+            outs.append((y, out))
+    torch.cuda.synchronize()
+    for i, (wl, inp, g) in enumerate(runs):
+        pl, d = oracle_plan_dispatch(wl, inp, src_rank=i)
+        check_plan_dispatch(wl, inp, g, pl, d)
+        y, out = outs[i]
+        # expert outputs on the oracle side come from the oracle's own dispatch
+        ref = O.combine(stand_in_oracle(wl, d["recv_x"], d["recv_scales"]), inp["weights"],
+                        inp["indices"], pl, wl.experts_per_rank, wl.cap)
+        check_combine(host(out, np.uint16), ref)
+        assert M.mep_get_status(g.m.h, streams[i]) == 0
