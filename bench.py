@@ -21,6 +21,7 @@ workload is reported beside the GPU's (cpu_baseline).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
                     [--no-extra | --extra skew,stdmoe,prefill_mxfp4,prefill_fp8direct]
+                    [--sweep 256,1024,8192]
 """
 
 from __future__ import annotations
@@ -453,6 +454,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="prefill and decode only")
     ap.add_argument("--extra", default="skew,stdmoe,prefill_mxfp4,prefill_fp8direct",
                     help="comma-separated extra workloads to measure after prefill and decode")
+    ap.add_argument("--sweep", default="",
+                    help="comma-separated token counts: the prefill configuration at each "
+                         "(step, fused plan+dispatch, combine), reported under 'sweep'")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -506,6 +510,17 @@ def main():
             del r
             torch.cuda.empty_cache()
 
+    sweep = {}
+    for T in [int(v) for v in args.sweep.split(",") if v]:
+        swl = wl.with_tokens(T, cap=max(T, wl.cap))
+        say(f"sweep: T={T}")
+        r = Runner(M, torch, swl, make_inputs(swl, 0), 3)
+        o = r.measure(max(args.steps // 2, 10), 10)
+        sweep[T] = {"U": r.U, **{n: {"us": o[n]["us"], "GBps": o[n]["GBps"]}
+                                 for n in ("step", "plan_dispatch", "combine")}}
+        del r
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         say("cpu baseline (oracle)")
@@ -535,6 +550,7 @@ def main():
         "decode_128": decode,
         "roofline": roofline,
         "workloads": extra,
+        **({"sweep": sweep} if sweep else {}),
         "cpu_baseline": cpu,
         "env": env_info(torch),
     }
