@@ -243,6 +243,15 @@ class Runner:
     def cast(self, s):
         self.M.mep_cast_fp8_direct(self.m.h, self.layout(), s["y"], s["y8"], self.stream)
 
+    def combine_in_flight(self, s):
+        self.M.mep_combine_fp8_direct(self.m.h, self.layout(), s["y"], s["w"], s["out"],
+                                      self.stream)
+
+    def step_in_flight(self, s):
+        self.plan_dispatch(s)
+        self.combine_in_flight(s)
+        self.M.mep_reset(self.m.h, self.stream)
+
     def combine(self, s):
         if self.fp8c:
             self.M.mep_combine_fp8(self.m.h, self.layout(), s["y8"], s["w"], s["out"], self.stream)
@@ -281,6 +290,8 @@ class Runner:
         elif self.fp8c:
             b["cast_fp8_direct"] = cast_fp8_bytes(H, U)
             b["combine"] = combine_fp8_bytes(T, H, k, U)
+            b["combine_in_flight"] = combine_bytes(T, H, k, U)
+            b["step_in_flight"] = b["plan_dispatch"] + b["combine_in_flight"]
         else:
             b["combine"] = combine_bytes(T, H, k, U)
         b["step"] = (b["plan_dispatch"] + b["combine"] + b.get("to_expert_major", 0)
@@ -301,9 +312,13 @@ class Runner:
             times["to_expert_major"] = self.loop(self.to_em, steps)
         if self.fp8c:
             times["cast_fp8_direct"] = self.loop(self.cast, steps)
+            # the same rounding applied in registers by the combine (one device)
+            times["combine_in_flight"] = self.loop(self.combine_in_flight, steps)
         times["combine"] = self.loop(self.combine, steps)
         times["plan"] = self.loop(self.plan, steps)
         times["dispatch"] = self.loop(self.dispatch, steps)
+        if self.fp8c:
+            times["step_in_flight"] = self.loop(self.step_in_flight, steps)
         if self.em:
             # standard-MoE dispatch straight into the expert-major layout, then
             # the same expert-major combine

@@ -77,6 +77,7 @@ def lib() -> C.CDLL:
             "mep_to_expert_major": ([p, p, p, p, p, p, p, p, p, p, p, i64, p], C.c_int),
             "mep_combine": ([p, i32, p, p, p, p], C.c_int),
             "mep_combine_fp8": ([p, i32, p, p, p, p], C.c_int),
+            "mep_combine_fp8_direct": ([p, i32, p, p, p, p], C.c_int),
             "mep_cast_fp8_direct": ([p, i32, p, p, p], C.c_int),
             "mep_reset": ([p, p], C.c_int),
             "mep_get_status": ([p, p, C.POINTER(i32)], C.c_int),
@@ -185,6 +186,12 @@ def mep_combine_fp8(h, layout, y8, weights, out, stream=None) -> None:
     s = _stream(stream, out)
     _check("mep_combine_fp8", lib().mep_combine_fp8(h, layout, _ptr(y8), _ptr(weights), _ptr(out),
                                                     s))
+
+
+def mep_combine_fp8_direct(h, layout, y, weights, out, stream=None) -> None:
+    s = _stream(stream, out)
+    _check("mep_combine_fp8_direct", lib().mep_combine_fp8_direct(
+        h, layout, _ptr(y), _ptr(weights), _ptr(out), s))
 
 
 def mep_cast_fp8_direct(h, layout, y, y8, stream=None) -> None:

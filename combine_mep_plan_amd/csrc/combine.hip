@@ -22,6 +22,10 @@
 // cast launch turns the routed bf16 expert-output rows into E4M3 rows, and the
 // E4M3 combine decodes each value exactly to fp32 and accumulates as above.
 // A lane owns 16 columns there: one 16-byte E4M3 unit in, two bf16 units out.
+// On one device the cast and the combine can also meet in registers: the bf16
+// combine with ROUND takes each value through the same E4M3 encode and decode
+// before its multiply-add -- bit for bit the two-launch result, with the bf16
+// rows read once and no E4M3 rows written.
 #include "dev.h"
 #include "mep_internal.h"
 
@@ -31,7 +35,21 @@ namespace {
 
 constexpr int kUnitsPerLane = 2;
 
-template <int KMAX, bool DEDUPE>
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// E4M3 of a bf16 pair's values, clamped to +-448 first so that the convert
+// saturates.
+__device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
+
+// Two values after the E4M3 direct cast and back (exact decode).
+__device__ __forceinline__ void round_e4m3_pair(float& a, float& b) {
+  const int p = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
+  const f32x2 r = __builtin_amdgcn_cvt_pk_f32_fp8(p, false);
+  a = r.x;
+  b = r.y;
+}
+
+template <int KMAX, bool DEDUPE, bool ROUND>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int lane = threadIdx.x & 63;
   const int g = first_lane(blockIdx.x * 4 + (threadIdx.x >> 6));
@@ -88,8 +106,10 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = __builtin_fmaf(w[j], bf16_lo(x[i]), acc[2 * i]);
-        acc[2 * i + 1] = __builtin_fmaf(w[j], bf16_hi(x[i]), acc[2 * i + 1]);
+        float lo = bf16_lo(x[i]), hi = bf16_hi(x[i]);
+        if (ROUND) round_e4m3_pair(lo, hi);
+        acc[2 * i] = __builtin_fmaf(w[j], lo, acc[2 * i]);
+        acc[2 * i + 1] = __builtin_fmaf(w[j], hi, acc[2 * i + 1]);
       }
     }
     u32x4 o;
@@ -98,8 +118,6 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     store_nt(out + v, o);
   }
 }
-
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Every top-k position loads its row, also when it shares a rank row with an
 // earlier position (about half of such repeats hit the caches): selecting
@@ -156,10 +174,6 @@ __global__ __launch_bounds__(256) void combine_fp8_kernel(CombineArgs a) {
   store_nt(out + 1, o1);
 }
 
-// E4M3 of a bf16 pair's values, clamped to +-448 first so that the convert
-// saturates.
-__device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
-
 // One wave per (token, slice); the token's distinct rows in groups of 8, all
 // loads of a group issued before its converts.
 template <bool RANK_MAJOR>
@@ -212,11 +226,14 @@ hipError_t launch_combine(const CombineArgs& a0, hipStream_t s) {
   a.slice_units = per;
   a.slices = (a.H / 8 + per - 1) / per;
   const int blocks = (int)(((int64_t)a.T * a.slices + 3) / 4);
-  if (a.k <= 8) {
-    if (a.distinct_rows) combine_kernel<8, false><<<blocks, 256, 0, s>>>(a);
-    else combine_kernel<8, true><<<blocks, 256, 0, s>>>(a);
+  if (a.round_e4m3) {
+    if (a.k > 8) combine_kernel<kMaxTopk, false, true><<<blocks, 256, 0, s>>>(a);
+    else if (a.distinct_rows) combine_kernel<8, false, true><<<blocks, 256, 0, s>>>(a);
+    else combine_kernel<8, true, true><<<blocks, 256, 0, s>>>(a);
   } else {
-    combine_kernel<kMaxTopk, false><<<blocks, 256, 0, s>>>(a);
+    if (a.k > 8) combine_kernel<kMaxTopk, false, false><<<blocks, 256, 0, s>>>(a);
+    else if (a.distinct_rows) combine_kernel<8, false, false><<<blocks, 256, 0, s>>>(a);
+    else combine_kernel<8, true, false><<<blocks, 256, 0, s>>>(a);
   }
   return hipGetLastError();
 }

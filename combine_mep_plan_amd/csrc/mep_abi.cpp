@@ -404,8 +404,10 @@ static int check_combine_layout(mep_handle* h, int32_t layout) {
   return MEP_OK;
 }
 
+// kind: 0 bf16 rows, 1 E4M3 rows, 2 bf16 rows rounded through E4M3 in flight
 static int combine_common(mep_handle* h, int32_t layout, const void* y, const float* weights,
-                          void* out, void* stream, bool fp8) {
+                          void* out, void* stream, int kind) {
+  const bool fp8 = kind == 1;
   if (!h) return MEP_ERR_NULL;
   int rc = check_combine_layout(h, layout);
   if (rc != MEP_OK) return rc;
@@ -424,18 +426,24 @@ static int combine_common(mep_handle* h, int32_t layout, const void* y, const fl
   a.T = T;
   a.H = h->cfg.hidden_dim;
   a.k = h->cfg.num_experts_per_token;
+  a.round_e4m3 = kind == 2 ? 1 : 0;
   return hip_rc(fp8 ? mep::launch_combine_fp8(a, (hipStream_t)stream)
                     : mep::launch_combine(a, (hipStream_t)stream));
 }
 
 int mep_combine(mep_handle* h, int32_t layout, const void* y, const float* weights, void* out,
                 void* stream) {
-  return combine_common(h, layout, y, weights, out, stream, false);
+  return combine_common(h, layout, y, weights, out, stream, 0);
 }
 
 int mep_combine_fp8(mep_handle* h, int32_t layout, const void* y8, const float* weights,
                     void* out, void* stream) {
-  return combine_common(h, layout, y8, weights, out, stream, true);
+  return combine_common(h, layout, y8, weights, out, stream, 1);
+}
+
+int mep_combine_fp8_direct(mep_handle* h, int32_t layout, const void* y, const float* weights,
+                           void* out, void* stream) {
+  return combine_common(h, layout, y, weights, out, stream, 2);
 }
 
 int mep_cast_fp8_direct(mep_handle* h, int32_t layout, const void* y, void* y8, void* stream) {

@@ -104,6 +104,7 @@ struct CombineArgs {
   void* out;               // [T,H] bf16
   int32_t T, H, k;
   int32_t distinct_rows;   // 1: the k rows of a token are distinct (no dedupe needed)
+  int32_t round_e4m3;      // 1: each value rounded through E4M3 (direct cast) before use
   int32_t slices, slice_units;  // waves per token and 16-byte lane units per wave
 };
 

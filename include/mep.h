@@ -257,6 +257,16 @@ int mep_combine_fp8(mep_handle *h, int32_t layout, const void *y8, const float *
                     void *out, void *stream);
 
 /*
+ * The same payload rounding without the E4M3 rows (one device: source and
+ * destination of the cast are the same): mep_combine on the bf16 rows y with
+ * each value cast to E4M3 and decoded back before its multiply-add.  out is
+ * bit for bit what mep_cast_fp8_direct followed by mep_combine_fp8 gives, the
+ * bf16 rows being read once.  Same state rules and layouts as mep_combine.
+ */
+int mep_combine_fp8_direct(mep_handle *h, int32_t layout, const void *y, const float *weights,
+                           void *out, void *stream);
+
+/*
  * Reset between iterations ("MORI-EP User Guide" section 3 reset()):
  * invalidates the plan (and the expert-major maps) and starts a new status
  * epoch, whose status word the last plan already cleared on the device, so no

@@ -188,6 +188,15 @@ def _expert_outputs(shape, seed):
     return _bf16_bits(v)
 
 
+def _check_in_flight(m, layout, y_dev, w_dev, out_two_step):
+    """mep_combine_fp8_direct (the rounding in registers) equals the cast +
+    E4M3 combine bit for bit."""
+    out = torch.empty_like(out_two_step)
+    M.mep_combine_fp8_direct(m.h, layout, y_dev, w_dev, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_two_step), "in-flight rounding differs from cast + combine"
+
+
 def _check_cast_combine(y, y8_gpu, out_gpu, used, tok_rows, combine_ref, T, sample):
     """y: bf16 bits [rows, H]; used: routed rows; tok_rows[t]: rows token t reads.
     Checks the cast of the routed rows (all of them, or those of `sample`
@@ -221,11 +230,13 @@ def test_fp8_direct_cast_and_combine_rank_major(T, sample):
     idx, w = dev(inp["indices"]), dev(inp["weights"])
     M.mep_plan(m.h, idx, T, counts, spos)
     y = _expert_outputs((R * cap, H), 53)
+    y_dev = dev(y)
     y8 = torch.full((R, cap, H), SENT8, dtype=torch.uint8, device="cuda")
-    M.mep_cast_fp8_direct(m.h, M.MEP_RANK_MAJOR, dev(y), y8)
+    M.mep_cast_fp8_direct(m.h, M.MEP_RANK_MAJOR, y_dev, y8)
     out = torch.empty((T, H), dtype=torch.int16, device="cuda")
     M.mep_combine_fp8(m.h, M.MEP_RANK_MAJOR, y8, w, out)
     torch.cuda.synchronize()
+    _check_in_flight(m, M.MEP_RANK_MAJOR, y_dev, w, out)
     pl = O.plan(inp["indices"], R, epr, cap)
     used = (np.arange(cap)[None, :] < pl["recv_counts"][:, None]).reshape(-1)
     tok_rows = (inp["indices"] // epr) * cap + pl["slot"]
@@ -250,11 +261,13 @@ def test_fp8_direct_cast_and_combine_expert_major(T, sample):
     M.mep_dispatch_standard_moe(m.h, dev(inp["indices"]), T, dev(inp["x"]), None, emx, None,
                                 emc, emo, emp, ce)
     y = _expert_outputs((ce, H), 59)
+    y_dev, w_dev = dev(y), dev(inp["weights"])
     y8 = torch.full((ce, H), SENT8, dtype=torch.uint8, device="cuda")
-    M.mep_cast_fp8_direct(m.h, M.MEP_EXPERT_MAJOR, dev(y), y8)
+    M.mep_cast_fp8_direct(m.h, M.MEP_EXPERT_MAJOR, y_dev, y8)
     out = torch.empty((T, H), dtype=torch.int16, device="cuda")
-    M.mep_combine_fp8(m.h, M.MEP_EXPERT_MAJOR, y8, dev(inp["weights"]), out)
+    M.mep_combine_fp8(m.h, M.MEP_EXPERT_MAJOR, y8, w_dev, out)
     torch.cuda.synchronize()
+    _check_in_flight(m, M.MEP_EXPERT_MAJOR, y_dev, w_dev, out)
     # the layout, from the routing alone (no payload needed)
     em = O.dispatch_standard_moe(np.zeros((T, 16), np.uint16), inp["weights"], inp["indices"],
                                  wl.ranks, wl.experts_per_rank, wl.cap, 0, ce)
@@ -289,11 +302,13 @@ def test_fp8_direct_and_mxfp4_wide_topk(R, epr, k):
     M.mep_plan(m.h, idx, wl.tokens, torch.empty(R, dtype=torch.int32, device="cuda"),
                torch.empty((R, cap), dtype=torch.int32, device="cuda"))
     y = _expert_outputs((R * cap, H), 61)
+    y_dev = dev(y)
     y8 = torch.full((R, cap, H), SENT8, dtype=torch.uint8, device="cuda")
-    M.mep_cast_fp8_direct(m.h, M.MEP_RANK_MAJOR, dev(y), y8)
+    M.mep_cast_fp8_direct(m.h, M.MEP_RANK_MAJOR, y_dev, y8)
     out = torch.empty((wl.tokens, H), dtype=torch.int16, device="cuda")
     M.mep_combine_fp8(m.h, M.MEP_RANK_MAJOR, y8, w, out)
     torch.cuda.synchronize()
+    _check_in_flight(m, M.MEP_RANK_MAJOR, y_dev, w, out)
     used = (np.arange(cap)[None, :] < pl["recv_counts"][:, None]).reshape(-1)
     tok_rows = (inp["indices"] // epr) * cap + pl["slot"]
     ref_fn = lambda y8r: O.combine(y8r.reshape(R, cap, H), inp["weights"], inp["indices"],  # noqa: E731
@@ -307,7 +322,8 @@ def test_fp8_direct_state_and_shape_rules():
     y = torch.zeros((wl.ranks, wl.cap, wl.hidden), dtype=torch.int16, device="cuda")
     y8 = torch.zeros((wl.ranks, wl.cap, wl.hidden), dtype=torch.uint8, device="cuda")
     for fn in (lambda: M.mep_cast_fp8_direct(m.h, M.MEP_RANK_MAJOR, y, y8),
-               lambda: M.mep_combine_fp8(m.h, M.MEP_EXPERT_MAJOR, y8, None, y)):
+               lambda: M.mep_combine_fp8(m.h, M.MEP_EXPERT_MAJOR, y8, None, y),
+               lambda: M.mep_combine_fp8_direct(m.h, M.MEP_RANK_MAJOR, y, None, y)):
         with pytest.raises(M.MepError) as e:
             fn()
         assert e.value.code == M.MEP_ERR_STATE
