@@ -105,10 +105,10 @@ __device__ __forceinline__ WaveRoute wave_route(const DispatchArgs& a, int t, in
 
 // Plan outputs for token t (fused modes; one wave per token does this):
 // receive row of each top-k position, first-occurrence bits, src_token_pos,
-// and -- from the last token's wave -- recv_counts.
+// and -- from the last token's wave -- recv_counts.  e: lane < k holds the
+// token's expert id of top-k position lane.
 __device__ __forceinline__ void write_route(const DispatchArgs& a, const WaveRoute& w, int t,
-                                            int lane) {
-  const int e = lane < a.k ? a.idx[(size_t)t * a.k + lane] : 0;
+                                            int lane, int e) {
   if (w.tok_mask == 0) {
     if (lane < a.k) a.rrow[(size_t)t * a.k + lane] = -1;
     if (lane == 0) a.ufirst[t] = 0u;
@@ -135,8 +135,8 @@ __device__ __forceinline__ void write_route(const DispatchArgs& a, const WaveRou
 
 // What slice 0 writes with every row of a token besides the payload: its k
 // weights and ids and, carrying, the caller's scale words.  Loaded once per
-// token, before the stores: on this architecture a wait for a load inside the
-// store loop also waits for every store issued before it.
+// token, before the stores: on this architecture a wait for a load issued
+// after stores also waits for those stores.
 struct TokenMeta {
   float w;     // lane < k: weight
   int32_t id;  // lane < k: expert id
@@ -170,6 +170,10 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
   const bool on = v < nu;
   Unit<QUANT> unit;
   unit.load(a.x, t, a.H, v, on);
+  // fused modes: the plan outputs need the ids, so the token's metadata goes
+  // out with the payload unit
+  TokenMeta meta{0.0f, 0, 0.0f};
+  if (MODE != kRoute) meta = load_meta<QUANT>(a, t, sl, lane);
 
   uint32_t first = 0;
   WaveRoute w{};
@@ -181,7 +185,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
     w = wave_route<MODE, KMAX>(a, t, lane, st);
     if (sl == 0) {
       if (MODE == kInline) or_status(a.status, lane == w.tl ? st : 0u);
-      write_route(a, w, t, lane);
+      write_route(a, w, t, lane, meta.id);
     }
     if (w.tok_mask == 0) return;
   }
@@ -189,7 +193,10 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
   float scale = 0.0f;
   uint32_t e8 = 0;
   const u32x4 q = unit.convert(scale, e8);
-  const TokenMeta meta = load_meta<QUANT>(a, t, sl, lane);
+  // after a prior plan, loading the metadata and the rows only once the
+  // token is known to be dispatched measured faster at large batches than
+  // issuing them with the payload unit
+  if (MODE == kRoute) meta = load_meta<QUANT>(a, t, sl, lane);
   auto emit = [&](int row) {
     if (on) {
       store_nt(reinterpret_cast<u32x4*>(a.recv_x) + (size_t)row * nu + v, q);
