@@ -135,6 +135,23 @@ def _loop_ms(torch, stream, fn, n):
     return a.elapsed_time(b) / n
 
 
+def _per_call_us(torch, stream, fn, n):
+    """Median, p10 and p90 of n calls of fn(i), each bracketed by its own pair
+    of HIP events on `stream`; the calls still run back to back on the GPU."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        fn(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    d = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    q = statistics.quantiles(d, n=10)
+    return {"median": round(statistics.median(d), 2), "p10": round(q[0], 2),
+            "p90": round(q[8], 2), "calls": n}
+
+
 # --------------------------------------------------------------------------
 # one workload: buffers, stand-in expert outputs, timed loops
 # --------------------------------------------------------------------------
@@ -276,6 +293,10 @@ class Runner:
                 fn(s)
         return _loop_ms(self.torch, self.stream, lambda i: fn(self.sets[i % len(self.sets)]), n)
 
+    def per_call(self, fn, n=100):
+        return _per_call_us(self.torch, self.stream, lambda i: fn(self.sets[i % len(self.sets)]),
+                            n)
+
     def bytes(self):
         wl, U = self.wl, self.U
         T, H, k, R = wl.tokens, wl.hidden, wl.topk, wl.ranks
@@ -342,6 +363,17 @@ class Runner:
                 o["payload_GBps"] = round(payload[name] / (ms * 1e-3) / 1e9, 1)
             ops[name] = o
         ops["step"]["repeats_us"] = self.step_repeats
+        # per-call spread of the main operations (context; the figures above
+        # are loop averages).  The step ends with a reset; the plan+dispatch
+        # calls leave a plan for the combine calls.
+        per = {"step": self.per_call(self.step),
+               "plan_dispatch": self.per_call(self.plan_dispatch)}
+        if self.em:
+            self.to_em(self.sets[0])
+        per["combine"] = self.per_call(self.combine)
+        self.M.mep_reset(self.m.h, self.stream)
+        for name, v in per.items():
+            ops[name]["per_call_us"] = v
         return ops
 
 
@@ -380,26 +412,40 @@ def time_decode(M, torch, wl, inp, reps, warmup):
                     res.setdefault(f"{name}{'' if queued else '_host'}_us", []).append(t)
         M.mep_reset(r.m.h, stream)
     out = {k: round(statistics.median(v), 2) for k, v in res.items()}
+    for k, v in res.items():
+        if not k.endswith("_host_us"):
+            q = statistics.quantiles(v, n=10)
+            out[k.replace("_us", "_p10_p90_us")] = [round(q[0], 2), round(q[8], 2)]
     s = r.sets[0]
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        r.stream = torch.cuda.current_stream()  # capture stream
-        r.plan_dispatch(s)
-        r.combine(s)
-    r.stream = stream
-    g_us = []
-    for i in range(warmup + reps):
-        a, b = ev(), ev()
-        torch.cuda.synchronize()
-        torch.cuda._sleep(200_000)
-        a.record(stream)
-        graph.replay()
-        b.record(stream)
-        torch.cuda.synchronize()
-        if i >= warmup:
-            g_us.append(a.elapsed_time(b) * 1e3)
-    out["graph_plan_dispatch_combine_us"] = round(statistics.median(g_us), 2)
-    del graph
+
+    def graph_us(fns):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            r.stream = torch.cuda.current_stream()  # capture stream
+            for fn in fns:
+                fn(s)
+        r.stream = stream
+        g_us = []
+        for i in range(warmup + reps):
+            a, b = ev(), ev()
+            torch.cuda.synchronize()
+            torch.cuda._sleep(200_000)
+            a.record(stream)
+            graph.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            if i >= warmup:
+                g_us.append(a.elapsed_time(b) * 1e3)
+        del graph
+        return round(statistics.median(g_us), 2)
+
+    # a plan+dispatch starts a round: a reset precedes each capture holding one
+    M.mep_reset(r.m.h, stream)
+    out["graph_plan_dispatch_us"] = graph_us([r.plan_dispatch])
+    out["graph_combine_us"] = graph_us([r.combine])
+    M.mep_reset(r.m.h, stream)
+    out["graph_plan_dispatch_combine_us"] = graph_us([r.plan_dispatch, r.combine])
+    M.mep_reset(r.m.h, stream)
     nb = r.bytes()
     out.update({"tokens": wl.tokens, "U": r.U, "dispatch_bytes": nb["plan_dispatch"],
                 "combine_bytes": nb["combine"]})
@@ -441,21 +487,27 @@ def cpu_baseline(wl, inp, budget_s=20.0):
     U = int(pl["recv_counts"].sum())
     nbytes = (plan_bytes(ts, k, R, U) + dispatch_bytes(ts, H, k, U, "fp8")
               + combine_bytes(ts, H, k, U))
-    times = []
+    times, t_pd, t_c = [], [], []
     t_end = time.perf_counter() + budget_s
     while time.perf_counter() < t_end or len(times) < 2:
         t0 = time.perf_counter()
         pl = O.plan(sub["indices"], R, epr, cap)
         d = O.dispatch(sub["x"], sub["weights"], sub["indices"], pl, R, epr, cap, True)
+        t1 = time.perf_counter()
         O.combine(y, sub["weights"], sub["indices"], pl, epr, cap)
-        times.append(time.perf_counter() - t0)
+        t2 = time.perf_counter()
+        times.append(t2 - t0)
+        t_pd.append(t1 - t0)
+        t_c.append(t2 - t1)
         if len(times) >= 20:
             break
     t = statistics.median(times)
     return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"first {ts} of {wl.tokens} tokens of the prefill workload, plan + FP8 "
                       f"dispatch + combine, single thread, median of {len(times)} runs "
-                      f"({t * 1e3:.0f} ms each; expert outputs prepared untimed)"}
+                      f"({t * 1e3:.0f} ms each; expert outputs prepared untimed)",
+            "phases_ms": {"plan_dispatch": round(statistics.median(t_pd) * 1e3, 1),
+                          "combine": round(statistics.median(t_c) * 1e3, 1)}}
 
 
 def main():
