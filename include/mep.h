@@ -242,8 +242,9 @@ int mep_combine(mep_handle *h, int32_t layout, const void *y, const float *weigh
                 void *stream);
 
 /*
- * FP8 direct-cast combine payload (the intra-node tuning matrix of the MORI
- * README / EPv2 guide pairs quant type fp8_direct_cast with a bf16 combine):
+ * FP8 direct-cast combine payload ("MORI-EP User Guide", section 10 Tuning:
+ * the intra-node tuning matrix pairs quant type fp8_direct_cast with a bf16
+ * combine):
  * mep_cast_fp8_direct writes y8 = OCP E4M3 of each bf16 value of the rows the
  * current plan routes (round to nearest even, saturating at +-448, no scale;
  * NaN inputs are not supported), y and y8 in the layout of mep_combine with 1

@@ -62,8 +62,9 @@
  *      Two elements per byte, the even column in the low nibble; the H/32
  *      scale bytes of a row fill H/128 32-bit scale words.  A carried FP4
  *      payload is H/2 bytes per row with the caller's scale words.
- *   R12 FP8 direct-cast combine payload ([Backends]/tuning matrix: quant type
- *      fp8_direct_cast with a bf16 combine): each expert-output value is cast
+ *   R12 FP8 direct-cast combine payload ("MORI-EP User Guide", section 10
+ *      Tuning, intra-node tuning matrix: quant type fp8_direct_cast with a bf16
+ *      combine): each expert-output value is cast
  *      to OCP E4M3 with no scale (round to nearest even, saturating at 448);
  *      the combine accumulates the decoded values exactly as R6.
  */
