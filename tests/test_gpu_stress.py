@@ -1,7 +1,8 @@
 """GPU stress: many rounds of the whole path compared with verified results.
 
-Like the pages' tuned-configuration check (many rounds against expected
-values; MORI README / EP guide tuning section), 500 rounds of fused plan +
+Like the pages' check of tuned configurations (many rounds of dispatch and
+combine output against expected values; "MORI-EP User Guide", section 10
+Tuning), 500 rounds of fused plan +
 FP8 dispatch + combine + reset run back to back over four input sets with
 different routings and token counts.  The first round of each set is checked
 against the oracle; every later round must reproduce it bit for bit (the
