@@ -20,6 +20,7 @@ MEP_ERR_ALIGN = -4
 MEP_ERR_STATE = -5
 MEP_ERR_HIP = -6
 MEP_ERR_DEVICE = -7
+MEP_ERR_NOMEM = -8
 
 MEP_DEV_BAD_INDEX = 1
 MEP_DEV_DUP_EXPERT = 2

@@ -109,6 +109,7 @@ const char* mep_error_string(int code) {
     case MEP_ERR_STATE: return "call order violated";
     case MEP_ERR_HIP: return "HIP runtime error";
     case MEP_ERR_DEVICE: return "device status set";
+    case MEP_ERR_NOMEM: return "out of host memory";
     default: return "unknown";
   }
 }
@@ -132,7 +133,7 @@ int mep_create(const mep_config* cfg, void* workspace, size_t workspace_bytes, m
   for (uint32_t e = 0; e < E; ++e)
     if (rd(e) != e / (uint32_t)cfg->num_experts_per_rank) return MEP_ERR_CONFIG;
   mep_handle* h = (mep_handle*)calloc(1, sizeof(mep_handle));
-  if (!h) return MEP_ERR_CONFIG;
+  if (!h) return MEP_ERR_NOMEM;
   h->cfg = *cfg;
   h->ws = (unsigned char*)workspace;
   h->ws_bytes = workspace_bytes;

@@ -48,6 +48,7 @@ extern "C" {
 #define MEP_ERR_STATE (-5)   /* call order violated (e.g. dispatch before plan) */
 #define MEP_ERR_HIP (-6)     /* the HIP runtime reported an error               */
 #define MEP_ERR_DEVICE (-7)  /* mep_get_status: device status word is non-zero  */
+#define MEP_ERR_NOMEM (-8)   /* mep_create: the host heap could not hold a handle */
 
 /* ---- device status bits (sticky until mep_reset) ------------------------- */
 #define MEP_DEV_BAD_INDEX 1   /* an expert id outside [0, E): that token is not

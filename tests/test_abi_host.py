@@ -155,6 +155,6 @@ def test_standard_moe_and_carry_argument_checks():
 
 
 def test_error_strings():
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         assert M.mep_error_string(code) not in ("", "unknown")
     assert M.mep_error_string(-99) == "unknown"
