@@ -18,10 +18,10 @@
 //
 // FP8 direct-cast payload ("MORI-EP User Guide", section 10 Tuning: the
 // intra-node tuning matrix pairs quant type fp8_direct_cast with a bf16
-// combine; the cast rule -- OCP E4M3, no scale,
-// round to nearest even, saturating at 448 -- is this library's reading): a
-// cast launch turns the routed bf16 expert-output rows into E4M3 rows, and the
-// E4M3 combine decodes each value exactly to fp32 and accumulates as above.
+// combine; the cast rule -- OCP E4M3, no scale, round to nearest even,
+// saturating at 448 -- is this library's reading): a cast launch turns the
+// routed bf16 expert-output rows into E4M3 rows, and the E4M3 combine decodes
+// each value exactly to fp32 and accumulates as above.
 // A lane owns 16 columns there: one 16-byte E4M3 unit in, two bf16 units out.
 // On one device the cast and the combine can also meet in registers: the bf16
 // combine with ROUND takes each value through the same E4M3 encode and decode
