@@ -391,15 +391,18 @@ def test_fp8_path_combine_bound(oracle):
 # ----------------------------------------------------------------------------
 
 def test_expert_major_layout(oracle):
+    # a source rank other than 0, so that source positions carry its offset
     wl = WORKLOADS["stdmoe"].with_tokens(300)
     inp = make_inputs(wl, 4)
-    pl = oracle.plan(inp["indices"], wl.ranks, wl.experts_per_rank, wl.cap)
+    src = 3
+    pl = oracle.plan(inp["indices"], wl.ranks, wl.experts_per_rank, wl.cap, src)
     d = oracle.dispatch(inp["x"], inp["weights"], inp["indices"], pl, wl.ranks,
                         wl.experts_per_rank, wl.cap, True)
     em = oracle.to_expert_major(d, pl, wl.ranks, wl.experts_per_rank, wl.cap, wl.tokens,
-                                wl.cap_em, fill=0x5A)
+                                wl.cap_em, src, fill=0x5A)
     idx = inp["indices"]
     T, k, E = wl.tokens, wl.topk, wl.experts
+    q_all = np.stack([oracle.quant_row(inp["x"][t])[0] for t in range(T)])
     assert em["status"] == 0
     cnt = np.bincount(idx.ravel(), minlength=E)
     assert np.array_equal(em["em_counts"], cnt)
@@ -415,10 +418,10 @@ def test_expert_major_layout(oracle):
     for e in range(E):
         toks = flat_t[order][starts[e]:starts[e + 1]]
         o = em["em_offsets"][e]
-        assert np.array_equal(em["em_src_pos"][o:o + cnt[e]], toks)
-        q = np.stack([oracle.quant_row(inp["x"][t])[0] for t in toks]) if len(toks) else None
-        if q is not None:
-            assert np.array_equal(em["em_x"][o:o + cnt[e]], q)
+        # source position: the plan's encoding, src_rank * (R * cap) + token
+        assert np.array_equal(em["em_src_pos"][o:o + cnt[e]],
+                              src * wl.ranks * wl.cap + toks)
+        assert np.array_equal(em["em_x"][o:o + cnt[e]], q_all[toks])
         # padding rows untouched
         assert np.all(em["em_x"][o + cnt[e]:em["em_offsets"][e + 1]] == 0x5A)
         for i, t in enumerate(toks):
@@ -477,6 +480,36 @@ def test_combine_is_fused_chain_in_top_k_order(oracle):
     assert np.array_equal(out, ref)
     # the data does tell a fused chain from a multiply-then-add chain
     assert np.count_nonzero(torch_bf16(unfused) != ref) > 0
+
+
+def test_expert_major_combine_is_fused_chain_in_top_k_order(oracle):
+    # As for the rank-major combine: each (t, j) reads its own expert-major row
+    # (here an arbitrary distinct row), and the chain of exact fp32 fmas in
+    # top-k order is computed in float64 with one rounding per step.
+    rng = np.random.default_rng(17)
+    T, H, k = 256, 1024, 8
+    tok = rng.permutation(T * k).reshape(T, k).astype(np.int32)
+    mag = rng.uniform(0.5, 2.0, size=(T * k, H)) * rng.choice([-1.0, 1.0], size=(T * k, H))
+    y = torch_bf16(mag.astype(np.float32))
+    w = rng.uniform(0.1, 1.0, size=(T, k)).astype(np.float32)
+    out = oracle.combine_em(y, w, tok)
+    rows = bf16_f32(y)[tok]                               # [T, k, H] fp32 values
+
+    def chain(order, fused=True):
+        acc = np.zeros((T, H), np.float32)
+        for j in order:
+            p = w[:, j, None].astype(np.float64) * rows[:, j].astype(np.float64)
+            if fused:
+                acc = (p + acc.astype(np.float64)).astype(np.float32)
+            else:
+                acc = (acc + p.astype(np.float32)).astype(np.float32)
+        return torch_bf16(acc)
+
+    ref = chain(range(k))
+    assert np.array_equal(out, ref)
+    # the data tells the top-k order and the fused chain from the alternatives
+    assert np.count_nonzero(chain(range(k - 1, -1, -1)) != ref) > 0
+    assert np.count_nonzero(chain(range(k), fused=False) != ref) > 0
 
 
 # ----------------------------------------------------------------------------
