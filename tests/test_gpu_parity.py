@@ -413,3 +413,92 @@ def test_two_handles_on_two_streams():
                         inp["indices"], pl, wl.experts_per_rank, wl.cap)
         check_combine(host(out, np.uint16), ref)
         assert M.mep_get_status(g.m.h, streams[i]) == 0
+
+
+def test_buffers_past_4_gib():
+    # 45000 bf16 tokens of 7168 columns: the receive buffers (5.2 GB) and the
+    # expert-major rows (5.6 GB) reach byte offsets past 2^32, so every row
+    # address needs 64-bit arithmetic.  Checked: plan outputs in full; the rows
+    # at the top of every rank's buffer, of the last experts' segments and a
+    # random sample; the combine of the last and of sampled tokens (identity
+    # expert, so the oracle runs the same tokens as a small batch of their own).
+    wl = dataclasses.replace(WORKLOADS["decode"], tokens=45000, cap=45000)
+    T, R, cap, H, k, epr, E = wl.tokens, wl.ranks, wl.cap, wl.hidden, wl.topk, \
+        wl.experts_per_rank, wl.experts
+    assert R * cap * H * 2 > 2**32
+    inp = make_inputs(wl, 11)
+    idx_h, w_h, x_h = inp["indices"], inp["weights"], inp["x"]
+    pl = O.plan(idx_h, R, epr, cap)
+    m = M.Mep(H, epr, k, cap, R)
+    x, w, idx = dev(x_h), dev(w_h), dev(idx_h)
+    counts = torch.empty(R, dtype=torch.int32, device="cuda")
+    spos = torch.empty((R, cap), dtype=torch.int32, device="cuda")
+    recv_x = torch.empty((R, cap, H), dtype=torch.int16, device="cuda")
+    recv_w = torch.empty((R, cap, k), dtype=torch.float32, device="cuda")
+    recv_i = torch.empty((R, cap, k), dtype=torch.int32, device="cuda")
+    route = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    _say(f"[big] T={T} H={H} R={R} fused plan+dispatch, combine")
+    M.mep_plan_dispatch(m.h, idx, T, counts, spos, x, w, None, recv_x, None, recv_w, recv_i)
+    M.mep_get_route(m.h, route)
+    M.mep_combine(m.h, M.MEP_RANK_MAJOR, recv_x, w, out)
+    torch.cuda.synchronize()
+    assert M.mep_get_status(m.h) == 0
+    n = pl["recv_counts"]
+    assert np.array_equal(host(counts), n)
+    sp = host(spos)
+    for r in range(R):
+        assert np.array_equal(sp[r, :n[r]], pl["src_token_pos"][r, :n[r]])
+    rt = host(route)
+    assert np.array_equal(rt, np.where(pl["slot"] >= 0, (idx_h // epr) * cap + pl["slot"], -1))
+    rng = np.random.default_rng(5)
+    rr = np.concatenate([np.repeat(np.arange(R), 16), rng.integers(0, R, 64)])
+    ss = np.concatenate([np.concatenate([np.arange(n[r] - 16, n[r]) for r in range(R)]),
+                         rng.integers(0, n.min(), 64)])
+    tt = pl["src_token_pos"][rr, ss]
+    ri_t, si_t = torch.from_numpy(rr).cuda(), torch.from_numpy(ss).cuda()
+    assert np.array_equal(host(recv_x[ri_t, si_t], np.uint16), x_h[tt])
+    assert np.array_equal(host(recv_w[ri_t, si_t]), w_h[tt])
+    assert np.array_equal(host(recv_i[ri_t, si_t]), idx_h[tt])
+    toks = np.unique(np.concatenate([np.arange(T - 32, T), rng.choice(T, 32, replace=False)]))
+    pl_s = O.plan(idx_h[toks], R, epr, len(toks))
+    d_s = O.dispatch(x_h[toks], w_h[toks], idx_h[toks], pl_s, R, epr, len(toks), False)
+    ref = O.combine(d_s["recv_x"], w_h[toks], idx_h[toks], pl_s, epr, len(toks))
+    tk = torch.from_numpy(toks).cuda()
+    check_combine(host(out[tk], np.uint16), ref)
+    del recv_x, recv_w, recv_i
+    torch.cuda.empty_cache()
+
+    # the same tokens straight into the expert-major layout, and its combine
+    M.mep_reset(m.h)
+    cap_em = wl.cap_em
+    assert cap_em * H * 2 > 2**32
+    em_x = torch.empty((cap_em, H), dtype=torch.int16, device="cuda")
+    emc = torch.empty(E, dtype=torch.int32, device="cuda")
+    emo = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    emp = torch.empty(cap_em, dtype=torch.int32, device="cuda")
+    em_route = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    out2 = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    _say(f"[big] standard-MoE dispatch, cap_em={cap_em}, expert-major combine")
+    M.mep_dispatch_standard_moe(m.h, idx, T, x, None, em_x, None, emc, emo, emp, cap_em)
+    M.mep_get_route(m.h, None, em_route)
+    M.mep_combine(m.h, M.MEP_EXPERT_MAJOR, em_x, w, out2)
+    torch.cuda.synchronize()
+    assert M.mep_get_status(m.h) == 0
+    cnt = np.bincount(idx_h.ravel(), minlength=E)
+    assert np.array_equal(host(emc), cnt)
+    offs = np.concatenate([[0], np.cumsum((cnt + 127) // 128 * 128)])
+    assert np.array_equal(host(emo), offs)
+    pos = host(emp)
+    for e in (E - 2, E - 1):  # the highest segments
+        toks_e = np.nonzero((idx_h == e).any(axis=1))[0]
+        o = offs[e]
+        assert np.array_equal(pos[o:o + cnt[e]], toks_e)
+        rows = host(em_x[o:o + cnt[e]], np.uint16)
+        assert np.array_equal(rows, x_h[toks_e])
+    er = host(em_route)
+    for t in toks:
+        for j in range(k):
+            e = idx_h[t, j]
+            assert offs[e] <= er[t, j] < offs[e] + cnt[e]
+    check_combine(host(out2[tk], np.uint16), ref)
