@@ -473,9 +473,12 @@ def copy_ceiling(torch, nbytes=512 << 20, reps=20):
     return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
 
 
-def cpu_baseline(wl, inp, budget_s=20.0):
+def cpu_baseline(wl, inp, gpu_out=None, budget_s=20.0):
     """The CPU oracle, single-threaded, on a bounded token sample of the same
-    workload: plan + FP8 dispatch + combine of the first `ts` tokens."""
+    workload: plan + FP8 dispatch + combine of the first `ts` tokens.  A
+    token's combined row does not depend on the other tokens, so the sample's
+    rows are also compared with the timed GPU run's (`gpu_out`, bf16 bits of
+    its first `ts` output rows)."""
     from oracle import oracle as O
     ts = 512
     sub = {"x": inp["x"][:ts], "indices": inp["indices"][:ts], "weights": inp["weights"][:ts]}
@@ -494,7 +497,7 @@ def cpu_baseline(wl, inp, budget_s=20.0):
         pl = O.plan(sub["indices"], R, epr, cap)
         d = O.dispatch(sub["x"], sub["weights"], sub["indices"], pl, R, epr, cap, True)
         t1 = time.perf_counter()
-        O.combine(y, sub["weights"], sub["indices"], pl, epr, cap)
+        out = O.combine(y, sub["weights"], sub["indices"], pl, epr, cap)
         t2 = time.perf_counter()
         times.append(t2 - t0)
         t_pd.append(t1 - t0)
@@ -507,7 +510,9 @@ def cpu_baseline(wl, inp, budget_s=20.0):
                       f"dispatch + combine, single thread, median of {len(times)} runs "
                       f"({t * 1e3:.0f} ms each; expert outputs prepared untimed)",
             "phases_ms": {"plan_dispatch": round(statistics.median(t_pd) * 1e3, 1),
-                          "combine": round(statistics.median(t_c) * 1e3, 1)}}
+                          "combine": round(statistics.median(t_c) * 1e3, 1)},
+            "sample_matches_gpu": (None if gpu_out is None else
+                                   bool(np.array_equal(out, gpu_out[:ts])))}
 
 
 def main():
@@ -542,6 +547,7 @@ def main():
     run = Runner(M, torch, wl, inp, args.sets)
     ops = run.measure(args.steps, args.warmup)
     U = run.U
+    gpu_out = run.sets[0]["out"][:512].cpu().numpy().view(np.uint16)
     del run
     torch.cuda.empty_cache()
     ms_step = ops["step"]["us"] * 1e-3
@@ -591,7 +597,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         say("cpu baseline (oracle)")
-        cpu = cpu_baseline(wl, inp)
+        cpu = cpu_baseline(wl, inp, gpu_out)
 
     line = {
         "metric": METRIC,
