@@ -502,3 +502,40 @@ def test_buffers_past_4_gib():
             e = idx_h[t, j]
             assert offs[e] <= er[t, j] < offs[e] + cnt[e]
     check_combine(host(out2[tk], np.uint16), ref)
+
+
+@pytest.mark.parametrize("R,epr,k,layout", [(8, 32, 16, "rank_major"), (8, 32, 32, "rank_major"),
+                                           (5, 8, 12, "rank_major"), (16, 16, 16, "rank_major"),
+                                           (8, 32, 32, "expert_major")])
+def test_wide_top_k_combine(R, epr, k, layout):
+    # top-k above 8: up to 8 ranks, each distinct rank row is held once and the
+    # positions pick it in j order; more ranks or the expert-major layout go
+    # through groups of 8 positions.  Whole path against the oracle.
+    wl = Workload("wide_k", 700, 1024, R, epr, k, 700, "fp8", "uniform", "dequant_half", layout)
+    stats = run_full(wl, 21, src_rank=R - 1, fused=True)
+    _say(f"[wide] R={R} k={k} {layout}: {stats}")
+
+
+@pytest.mark.parametrize("R,epr,k", [(8, 32, 16), (7, 4, 28), (16, 16, 16)])
+def test_wide_top_k_in_flight_rounding(R, epr, k):
+    # the E4M3 rounding in flight at top-k above 8 equals cast + E4M3 combine
+    wl = Workload("wide_r", 300, 512, R, epr, k, 300, "none", "uniform", "identity",
+                  "rank_major")
+    inp = make_inputs(wl, 22)
+    g = gpu_plan_dispatch(wl, inp, fused=True)
+    pl, d = oracle_plan_dispatch(wl, inp)
+    y8 = torch.zeros(g.recv_x.shape, dtype=torch.uint8, device="cuda")
+    M.mep_cast_fp8_direct(g.m.h, M.MEP_RANK_MAJOR, g.recv_x, y8)
+    two = torch.empty((wl.tokens, wl.hidden), dtype=torch.int16, device="cuda")
+    M.mep_combine_fp8(g.m.h, M.MEP_RANK_MAJOR, y8, g.w, two)
+    one = torch.empty_like(two)
+    M.mep_combine_fp8_direct(g.m.h, M.MEP_RANK_MAJOR, g.recv_x, g.w, one)
+    torch.cuda.synchronize()
+    assert torch.equal(one, two)
+    n = pl["recv_counts"]
+    used = np.arange(wl.cap)[None, :] < n[:, None]
+    ref8 = np.zeros(d["recv_x"].shape, dtype=np.uint8)
+    ref8[used] = O.cast_fp8_direct(d["recv_x"][used])
+    ref = O.combine(O.e4m3_to_bf16(ref8), inp["weights"], inp["indices"], pl, epr, wl.cap)
+    check_combine(host(one, np.uint16), ref)
+    assert M.mep_get_status(g.m.h) == 0
