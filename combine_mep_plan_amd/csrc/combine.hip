@@ -24,9 +24,9 @@
 // each value exactly to fp32 and accumulates as above.
 // A lane owns 16 columns there: one 16-byte E4M3 unit in, two bf16 units out.
 // On one device the cast and the combine can also meet in registers: the bf16
-// combine with ROUND takes each value through the same E4M3 encode and decode
-// before its multiply-add -- bit for bit the two-launch result, with the bf16
-// rows read once and no E4M3 rows written.
+// combine with ROUND takes every value of each loaded row through the same
+// E4M3 encode and decode before the multiply-adds -- bit for bit the
+// two-launch result, with the bf16 rows read once and no E4M3 rows written.
 #include "dev.h"
 #include "mep_internal.h"
 
@@ -48,6 +48,18 @@ __device__ __forceinline__ void round_e4m3_pair(float& a, float& b) {
   const f32x2 r = __builtin_amdgcn_cvt_pk_f32_fp8(p, false);
   a = r.x;
   b = r.y;
+}
+
+// A unit of 8 bf16 values after the E4M3 direct cast and back, packed again as
+// bf16: every E4M3 value is a bf16 value, so the repacking is exact.  Applied
+// once to each loaded row, not once per top-k position using it.
+__device__ __forceinline__ void round_e4m3_unit(u32x4& x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float lo = bf16_lo(x[i]), hi = bf16_hi(x[i]);
+    round_e4m3_pair(lo, hi);
+    x[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+  }
 }
 
 template <int KMAX, bool DEDUPE, bool ROUND>
@@ -89,6 +101,13 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
         in[u][j] = __builtin_nontemporal_load(y + (size_t)row[j] * nv + v);
     }
   }
+  if (ROUND) {
+#pragma unroll
+    for (int u = 0; u < kUnitsPerLane; ++u)
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j)
+        if (row[j] >= 0 && src[j] == j) round_e4m3_unit(in[u][j]);
+  }
 #pragma unroll
   for (int u = 0; u < kUnitsPerLane; ++u) {
     const int v = v0 + u * kWave;
@@ -107,8 +126,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float lo = bf16_lo(x[i]), hi = bf16_hi(x[i]);
-        if (ROUND) round_e4m3_pair(lo, hi);
+        const float lo = bf16_lo(x[i]), hi = bf16_hi(x[i]);
         acc[2 * i] = __builtin_fmaf(w[j], lo, acc[2 * i]);
         acc[2 * i + 1] = __builtin_fmaf(w[j], hi, acc[2 * i + 1]);
       }
@@ -172,6 +190,13 @@ __global__ __launch_bounds__(256) void combine_wide_kernel(CombineArgs a) {
           in[u][q] = y[(size_t)row[q] * nv + v];
       }
     }
+    if (ROUND) {
+#pragma unroll
+      for (int u = 0; u < kUnitsPerLane; ++u)
+#pragma unroll
+        for (int q = 0; q < G; ++q)
+          if (row[q] >= 0 && src[q] == q) round_e4m3_unit(in[u][q]);
+    }
 #pragma unroll
     for (int u = 0; u < kUnitsPerLane; ++u) {
 #pragma unroll
@@ -185,8 +210,7 @@ __global__ __launch_bounds__(256) void combine_wide_kernel(CombineArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float lo = bf16_lo(x[i]), hi = bf16_hi(x[i]);
-          if (ROUND) round_e4m3_pair(lo, hi);
+          const float lo = bf16_lo(x[i]), hi = bf16_hi(x[i]);
           acc[u][2 * i] = __builtin_fmaf(w[q], lo, acc[u][2 * i]);
           acc[u][2 * i + 1] = __builtin_fmaf(w[q], hi, acc[u][2 * i + 1]);
         }
@@ -249,6 +273,62 @@ __global__ __launch_bounds__(256) void combine_fp8_kernel(CombineArgs a) {
       acc[4 * i + 3] = __builtin_fmaf(w[j], hi.y, acc[4 * i + 3]);
     }
   }
+  u32x4 o0, o1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o0[i] = pack_bf16_rne(acc[2 * i], acc[2 * i + 1]);
+    o1[i] = pack_bf16_rne(acc[8 + 2 * i], acc[8 + 2 * i + 1]);
+  }
+  u32x4* out = reinterpret_cast<u32x4*>(a.out) + (size_t)t * (a.H / 8) + 2 * v;
+  store_nt(out, o0);
+  store_nt(out + 1, o1);
+}
+
+// The E4M3 combine beyond top-8: positions in groups of 8, in order, each
+// group's loads issued before its multiply-adds (cached loads, so that rank
+// rows named again can come from the caches); acc carries the chain.
+__global__ __launch_bounds__(256) void combine_fp8_wide_kernel(CombineArgs a) {
+  constexpr int G = 8;
+  const int lane = threadIdx.x & 63;
+  const int g = first_lane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  const int t = g / a.slices, sl = g - t * a.slices;
+  if (t >= a.T) return;
+  const int nv8 = a.H / 16;  // 16-byte E4M3 units per row
+  const u32x4* y = reinterpret_cast<const u32x4*>(a.y);
+  const int v = sl * kWave + lane;
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+  for (int j0 = 0; j0 < a.k; j0 += G) {  // uniform
+    int row[G];
+    float w[G];
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+      const int j = j0 + q;
+      row[q] = j < a.k ? a.rows[(size_t)t * a.k + j] : -1;
+      w[q] = j < a.k ? a.w[(size_t)t * a.k + j] : 0.0f;
+    }
+    u32x4 in[G];
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+      in[q] = u32x4{0, 0, 0, 0};
+      if (row[q] >= 0 && v < nv8) in[q] = y[(size_t)row[q] * nv8 + v];
+    }
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+      if (row[q] < 0) continue;  // uniform
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)in[q][i], false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)in[q][i], true);
+        acc[4 * i] = __builtin_fmaf(w[q], lo.x, acc[4 * i]);
+        acc[4 * i + 1] = __builtin_fmaf(w[q], lo.y, acc[4 * i + 1]);
+        acc[4 * i + 2] = __builtin_fmaf(w[q], hi.x, acc[4 * i + 2]);
+        acc[4 * i + 3] = __builtin_fmaf(w[q], hi.y, acc[4 * i + 3]);
+      }
+    }
+  }
+  if (v >= nv8) return;
   u32x4 o0, o1;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -338,7 +418,7 @@ hipError_t launch_combine_fp8(const CombineArgs& a0, hipStream_t s) {
   a.slices = (a.H / 16 + kWave - 1) / kWave;
   const int blocks = (int)(((int64_t)a.T * a.slices + 3) / 4);
   if (a.k <= 8) combine_fp8_kernel<8><<<blocks, 256, 0, s>>>(a);
-  else combine_fp8_kernel<kMaxTopk><<<blocks, 256, 0, s>>>(a);
+  else combine_fp8_wide_kernel<<<blocks, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
