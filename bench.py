@@ -3,9 +3,9 @@
 Headline step (`value`): the whole path on one batch of the prefill workload
 -- routing plan + FP8 dispatch through the fused mep_plan_dispatch (OCP E4M3,
 one fp32 scale per 128 columns), bf16 combine, reset -- for 4096 tokens x
-7168 hidden, top-8 of 256 experts on 8 virtual ranks: the shape of the MORI
-README bandwidth table ("4096 tokens, 7168 hidden, top-8, FP8 dispatch + BF16
-combine").  value = the step's algorithmic HBM bytes / step time.
+7168 hidden, top-8 of 256 experts on 8 virtual ranks: the shape and dtypes of
+the MORI README's bandwidth table.  value = the step's algorithmic HBM bytes /
+step time.
 
 Also measured, each on its own buffers: decode latency (128 tokens, bf16 both
 ways), the skewed-routing workload (Zipf 1.2, 16 ranks) and the standard-MoE

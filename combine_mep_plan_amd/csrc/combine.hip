@@ -1,11 +1,11 @@
 // Combine: gather each token's k expert-output rows back to token order as a
 // weighted sum.
 //
-// Source: "MORI-EP User Guide", section 3 combine() (expert outputs, weights
-// "for weighted combination", indices as for dispatch; output rows at the
-// tokens' original positions) and section 4 combine_standard_moe() for the
-// expert-major input; "Choosing an EP API and backend": gather combine in
-// BF16/FP32.  Arithmetic: fp32 accumulator starting at +0, one fused
+// Source: "MORI-EP User Guide", section 3 combine() (expert outputs, the
+// weights that scale each expert's contribution, indices as for dispatch;
+// output rows at the tokens' original positions) and section 4
+// combine_standard_moe() for the expert-major input; "Choosing an EP API and
+// backend": the HIP backend's combine gathers in BF16 or FP32.  Arithmetic: fp32 accumulator starting at +0, one fused
 // multiply-add per top-k position in order j = 0..k-1, then bf16 round to
 // nearest even -- a fixed order, so the result does not depend on timing.
 //

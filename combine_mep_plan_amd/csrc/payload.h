@@ -4,8 +4,8 @@
 //
 // Sources: "MORI-EP User Guide" section 3 dispatch() (rows with their scales);
 // "Choosing an EP API and backend": OCP E4M3 is the gfx950 FP8 flavour, the
-// HIP backend carries already-quantized FP8/FP4 payloads, gfx950 has FP4
-// conversion.  The block formats (E4M3 with an fp32 scale per 128 columns;
+// HIP backend's dispatch can move FP8/FP4 rows that arrive quantized, gfx950
+// has FP4 conversion.  The block formats (E4M3 with an fp32 scale per 128 columns;
 // OCP MX FP4 with an E8M0 scale per 32 columns) are this library's readings.
 #pragma once
 

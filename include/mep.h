@@ -65,8 +65,8 @@ extern "C" {
                                          E4M3 bytes with scale_dim fp32 scales
                                          per row; both are carried unchanged
                                          ("Choosing an EP API and backend": the
-                                         HIP backend carries already-quantized
-                                         FP8 payloads)                           */
+                                         HIP backend's dispatch can move FP8
+                                         rows that arrive quantized)             */
 #define MEP_QUANT_FP4_CARRY 3         /* as MEP_QUANT_FP8_CARRY for FP4 rows: H/2
                                          bytes per row (two E2M1 codes a byte),
                                          scale_dim 32-bit scale words per row,
@@ -227,7 +227,8 @@ int mep_dispatch_standard_moe(mep_handle *h, const int32_t *indices, int32_t T, 
  * Combine ("MORI-EP User Guide" section 3 combine(): expert outputs gathered
  * back to token order as a weighted combination; section 4
  * combine_standard_moe() for the expert-major input; "Choosing an EP API and
- * backend": gather combine in BF16/FP32).  For every planned token t:
+ * backend": the HIP backend's combine gathers in BF16 or FP32).  For every
+ * planned token t:
  *   out[t, h] = bf16_rne(acc),  acc = +0.0f, then for j = 0..k-1 in order
  *               acc = fmaf(weights[t, j], y_j[h], acc)
  * where y_j is the bf16 expert-output row holding (t, expert j):

@@ -20,7 +20,8 @@
  * Readings taken where the pages leave a step open (each is repeated at the
  * function that applies it):
  *   R1 expert e lives on rank e / num_experts_per_rank (contiguous blocks:
- *      [Guide] section 2, "256 experts / 8 GPUs").
+ *      [Guide] section 2, whose DeepSeek-V3 example gives each of 8 GPUs 32
+ *      of the 256 experts).
  *   R2 a token is sent once per destination rank; the first j (in top-k
  *      order) naming that rank owns the row, later j on the same rank share it
  *      ([Issue57]: the design removes redundant transfer).
@@ -35,9 +36,9 @@
  *   R6 combine: out[t] = bf16_rne( fp32 sum over j = 0..k-1, in that order,
  *      acc = fmaf(w[t][j], y_j, acc), acc starting at +0 ), where y_j is the
  *      expert-output row holding (t, expert j) -- a rank row shared by two
- *      experts is used once per expert ([Guide] section 3 combine(): weights
- *      are for the weighted combination; [Backends]: gather combine in
- *      BF16/FP32).
+ *      experts is used once per expert ([Guide] section 3 combine(): the
+ *      weights scale each expert's output; [Backends]: the HIP backend's
+ *      combine gathers in BF16 or FP32).
  *   R7 expert-major layout: experts in global order; each expert's rows in
  *      ascending receive slot; each segment starts at a multiple of 128 rows;
  *      padding rows are not written ([Guide] section 4,
@@ -219,8 +220,8 @@ int32_t oracle_plan(const int32_t *idx, int32_t T, int32_t k, int32_t R, int32_t
 /*             recv_scales [R,cap,H/128] (reading R5).                       */
 /* quant == 2: x [T,H] E4M3 bytes with xs [T,sd] fp32 scales, both copied    */
 /*             into recv_x [R,cap,H] bytes and recv_scales [R,cap,sd]        */
-/*             ([Backends]: the HIP backend carries already-quantized FP8    */
-/*             payloads; reading R9).                                        */
+/*             ([Backends]: the HIP backend's dispatch can move FP8 rows     */
+/*             that arrive quantized; reading R9).                           */
 /* quant == 3: as 2 for FP4 rows of H/2 bytes (reading R11).                 */
 /* quant == 4: x [T,H] bf16 bits quantised to MXFP4: recv_x [R,cap,H/2]      */
 /*             bytes, recv_scales [R,cap,H/128] words of E8M0 bytes (R11).   */

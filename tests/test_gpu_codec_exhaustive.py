@@ -14,8 +14,8 @@ references are definitions that need no sampling:
   whose magnitude is at most 448 * (1 + 2^-23) -- the largest quotient a
   quantising dispatch can form (amax / (amax / 448)).
 
-Source: "Choosing an EP API and backend" (OCP E4M3 on gfx950; gather combine
-in BF16/FP32).
+Source: "Choosing an EP API and backend" (OCP E4M3 on gfx950; the HIP
+backend's combine gathers in BF16 or FP32).
 """
 
 import numpy as np

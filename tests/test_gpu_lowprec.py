@@ -2,8 +2,8 @@
 FP4 payloads, and the FP8 direct-cast combine payload.
 
 Sources: "Choosing an EP API and backend" (FP4 conversion kernels on gfx950;
-the HIP backend carries already-quantized FP8/FP4 payloads; OCP E4M3 on
-gfx950), and "MORI-EP User Guide" section 10 Tuning, whose intra-node tuning
+the HIP backend's dispatch can move FP8/FP4 rows that arrive quantized;
+OCP E4M3 on gfx950), and "MORI-EP User Guide" section 10 Tuning, whose intra-node tuning
 matrix pairs an FP4 dispatch with a bf16 combine and quant type
 fp8_direct_cast.  The block formats are the readings the
 oracle documents (OCP MX FP4: E2M1 codes, E8M0 scale per 32 columns; E4M3
