@@ -94,11 +94,15 @@ def lib() -> C.CDLL:
 
 
 def _ptr(t):
-    """Device pointer of a tensor (must be contiguous), an int, or None."""
+    """Device pointer of a tensor (must be contiguous and on a GPU), an int
+    (taken as a device address), or None."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_cuda:
+        raise ValueError("tensors passed to libmep must be on the GPU (a host pointer "
+                         "would make the kernels fault)")
     if not t.is_contiguous():
         raise ValueError("tensors passed to libmep must be contiguous")
     return t.data_ptr()

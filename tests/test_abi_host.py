@@ -158,3 +158,14 @@ def test_error_strings():
     for code in range(-8, 1):
         assert M.mep_error_string(code) not in ("", "unknown")
     assert M.mep_error_string(-99) == "unknown"
+
+
+def test_binding_refuses_host_tensors():
+    # a host tensor's address handed to a kernel would fault the GPU: the
+    # binding refuses it before any call reaches the library
+    import torch
+    t = torch.zeros(64, dtype=torch.int32)
+    with pytest.raises(ValueError, match="on the GPU"):
+        M.mep_probe_bf16(t, t, 0)
+    from combine_mep_plan_amd import _binding as B
+    assert B._ptr(None) is None and B._ptr(1 << 20) == 1 << 20
