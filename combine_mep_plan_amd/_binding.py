@@ -122,6 +122,103 @@ def _check(fn: str, rc: int) -> None:
         raise MepError(fn, rc)
 
 
+# ---------------------------------------------------------------------------
+# buffer sizes.  The C ABI trusts the caller's buffer sizes (a short buffer
+# would be written past its end on the GPU); for handles made here, the
+# binding checks every tensor against the sizes the call will touch, using the
+# handle's config and the token count of its last plan.
+# ---------------------------------------------------------------------------
+
+# handle -> {"cfg": MepConfig, "T": planned tokens, "cap_em": rows, "rm"/"em": whether
+# the rank-major plan / the expert-major layout is valid (the library's call
+# order, mirrored so that a call the library will refuse is not size-checked)
+_handles: dict = {}
+
+
+def _row_bytes_in(c) -> int:
+    """Bytes of one token row the dispatch reads."""
+    return {MEP_QUANT_FP8_CARRY: c.hidden_dim, MEP_QUANT_FP4_CARRY: c.hidden_dim // 2}.get(
+        c.quant, 2 * c.hidden_dim)
+
+
+def _row_bytes_out(c) -> int:
+    """Bytes of one received (or expert-major) row."""
+    if c.quant == MEP_QUANT_NONE:
+        return 2 * c.hidden_dim
+    if c.quant in (MEP_QUANT_MXFP4, MEP_QUANT_FP4_CARRY):
+        return c.hidden_dim // 2
+    return c.hidden_dim
+
+
+def _need(fn: str, name: str, t, nbytes: int) -> None:
+    if t is None or isinstance(t, int) or nbytes <= 0:
+        return
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{fn}: {name} holds {have} bytes, the call touches {nbytes}")
+
+
+def _state(h):
+    return _handles.get(h)
+
+
+def _check_plan_buffers(fn, st, indices, T, recv_counts, src_token_pos):
+    c = st["cfg"]
+    _need(fn, "indices", indices, 4 * T * c.num_experts_per_token)
+    _need(fn, "recv_counts", recv_counts, 4 * c.world_size)
+    _need(fn, "src_token_pos", src_token_pos, 4 * c.world_size * c.max_num_inp_token_per_rank)
+
+
+def _check_dispatch_buffers(fn, st, T, x, weights, scales, indices, recv_x, recv_scales,
+                            recv_weights, recv_indices):
+    c = st["cfg"]
+    k, rows = c.num_experts_per_token, c.world_size * c.max_num_inp_token_per_rank
+    sd = c.scale_dim if c.quant != MEP_QUANT_NONE else 0
+    _need(fn, "x", x, T * _row_bytes_in(c))
+    _need(fn, "weights", weights, 4 * T * k)
+    _need(fn, "indices", indices, 4 * T * k)
+    if c.quant in (MEP_QUANT_FP8_CARRY, MEP_QUANT_FP4_CARRY):
+        _need(fn, "scales", scales, 4 * T * sd)
+    _need(fn, "recv_x", recv_x, rows * _row_bytes_out(c))
+    _need(fn, "recv_scales", recv_scales, 4 * rows * sd)
+    _need(fn, "recv_weights", recv_weights, 4 * rows * k)
+    _need(fn, "recv_indices", recv_indices, 4 * rows * k)
+
+
+def _check_em_buffers(fn, st, cap_em, em_x, em_scales, em_counts, em_offsets, em_src_pos):
+    c = st["cfg"]
+    E = c.world_size * c.num_experts_per_rank
+    sd = c.scale_dim if c.quant != MEP_QUANT_NONE else 0
+    _need(fn, "em_x", em_x, cap_em * _row_bytes_out(c))
+    _need(fn, "em_scales", em_scales, 4 * cap_em * sd)
+    _need(fn, "em_counts", em_counts, 4 * E)
+    _need(fn, "em_offsets", em_offsets, 4 * (E + 1))
+    _need(fn, "em_src_pos", em_src_pos, 4 * cap_em)
+
+
+def _layout_ready(st, layout) -> bool:
+    return st is not None and st.get("rm" if layout == MEP_RANK_MAJOR else "em", False)
+
+
+def _combine_rows(st, layout) -> int:
+    """Rows of the layout's expert-output buffer (0 when no token is planned:
+    the call then reads nothing)."""
+    c = st["cfg"]
+    if not st.get("T"):
+        return 0
+    if layout == MEP_RANK_MAJOR:
+        return c.world_size * c.max_num_inp_token_per_rank
+    return st.get("cap_em") or 0
+
+
+def _check_combine_buffers(fn, st, layout, y, y_value_bytes, weights, out):
+    c = st["cfg"]
+    T = st.get("T") or 0
+    _need(fn, "y", y, _combine_rows(st, layout) * c.hidden_dim * y_value_bytes)
+    _need(fn, "weights", weights, 4 * T * c.num_experts_per_token)
+    _need(fn, "out", out, 2 * T * c.hidden_dim)
+
+
 def mep_error_string(code: int) -> str:
     return lib().mep_error_string(code).decode()
 
@@ -134,21 +231,34 @@ def mep_create(cfg: MepConfig, workspace, workspace_bytes: int) -> int:
     h = C.c_void_p()
     _check("mep_create", lib().mep_create(C.byref(cfg), _ptr(workspace), workspace_bytes,
                                           C.byref(h)))
+    c = MepConfig()
+    C.pointer(c)[0] = cfg  # a copy: later edits of cfg do not change the checks
+    _handles[h.value] = {"cfg": c, "T": None, "cap_em": None, "rm": False, "em": False}
     return h.value
 
 
 def mep_destroy(h: int) -> None:
     _check("mep_destroy", lib().mep_destroy(h))
+    _handles.pop(h, None)
 
 
 def mep_plan(h, indices, T, recv_counts, src_token_pos, stream=None) -> None:
+    st = _state(h)
+    if st is not None and 0 <= T <= st["cfg"].max_num_inp_token_per_rank:
+        _check_plan_buffers("mep_plan", st, indices, T, recv_counts, src_token_pos)
     s = _stream(stream, recv_counts)
     _check("mep_plan", lib().mep_plan(h, _ptr(indices), T, _ptr(recv_counts),
                                       _ptr(src_token_pos), s))
+    if st is not None:
+        st.update(T=T, rm=True, em=False)
 
 
 def mep_dispatch(h, x, weights, scales, indices, recv_x, recv_scales, recv_weights,
                  recv_indices, stream=None) -> None:
+    st = _state(h)
+    if _layout_ready(st, MEP_RANK_MAJOR):
+        _check_dispatch_buffers("mep_dispatch", st, st["T"], x, weights, scales, indices, recv_x,
+                                recv_scales, recv_weights, recv_indices)
     s = _stream(stream, recv_x)
     _check("mep_dispatch", lib().mep_dispatch(h, _ptr(x), _ptr(weights), _ptr(scales),
                                               _ptr(indices), _ptr(recv_x), _ptr(recv_scales),
@@ -157,55 +267,104 @@ def mep_dispatch(h, x, weights, scales, indices, recv_x, recv_scales, recv_weigh
 
 def mep_plan_dispatch(h, indices, T, recv_counts, src_token_pos, x, weights, scales, recv_x,
                       recv_scales, recv_weights, recv_indices, stream=None) -> None:
+    st = _state(h)
+    if st is not None and 0 <= T <= st["cfg"].max_num_inp_token_per_rank:
+        _check_plan_buffers("mep_plan_dispatch", st, indices, T, recv_counts, src_token_pos)
+        _check_dispatch_buffers("mep_plan_dispatch", st, T, x, weights, scales, indices, recv_x,
+                                recv_scales, recv_weights, recv_indices)
     s = _stream(stream, recv_x)
     _check("mep_plan_dispatch", lib().mep_plan_dispatch(
         h, _ptr(indices), T, _ptr(recv_counts), _ptr(src_token_pos), _ptr(x), _ptr(weights),
         _ptr(scales), _ptr(recv_x), _ptr(recv_scales), _ptr(recv_weights), _ptr(recv_indices),
         s))
+    if st is not None:
+        st.update(T=T, rm=True, em=False)
 
 
 def mep_dispatch_standard_moe(h, indices, T, x, scales, em_x, em_scales, em_counts, em_offsets,
                               em_src_pos, cap_em, stream=None) -> None:
+    st = _state(h)
+    fn = "mep_dispatch_standard_moe"
+    if st is not None and 0 <= T <= st["cfg"].max_num_inp_token_per_rank and cap_em >= 0:
+        c = st["cfg"]
+        _need(fn, "indices", indices, 4 * T * c.num_experts_per_token)
+        _need(fn, "x", x, T * _row_bytes_in(c))
+        if c.quant in (MEP_QUANT_FP8_CARRY, MEP_QUANT_FP4_CARRY):
+            _need(fn, "scales", scales, 4 * T * c.scale_dim)
+        _check_em_buffers(fn, st, cap_em, em_x, em_scales, em_counts, em_offsets, em_src_pos)
     s = _stream(stream, em_x)
-    _check("mep_dispatch_standard_moe", lib().mep_dispatch_standard_moe(
+    _check(fn, lib().mep_dispatch_standard_moe(
         h, _ptr(indices), T, _ptr(x), _ptr(scales), _ptr(em_x), _ptr(em_scales),
         _ptr(em_counts), _ptr(em_offsets), _ptr(em_src_pos), cap_em, s))
+    if st is not None:
+        st.update(T=T, cap_em=cap_em, rm=False, em=True)
 
 
 def mep_to_expert_major(h, recv_x, recv_scales, recv_indices, recv_counts, src_token_pos, em_x,
                         em_scales, em_counts, em_offsets, em_src_pos, cap_em,
                         stream=None) -> None:
+    st = _state(h)
+    fn = "mep_to_expert_major"
+    if _layout_ready(st, MEP_RANK_MAJOR) and cap_em >= 0:
+        c = st["cfg"]
+        rows = c.world_size * c.max_num_inp_token_per_rank
+        sd = c.scale_dim if c.quant != MEP_QUANT_NONE else 0
+        _need(fn, "recv_x", recv_x, rows * _row_bytes_out(c))
+        _need(fn, "recv_scales", recv_scales, 4 * rows * sd)
+        _need(fn, "recv_indices", recv_indices, 4 * rows * c.num_experts_per_token)
+        _need(fn, "recv_counts", recv_counts, 4 * c.world_size)
+        _need(fn, "src_token_pos", src_token_pos, 4 * rows)
+        _check_em_buffers(fn, st, cap_em, em_x, em_scales, em_counts, em_offsets, em_src_pos)
     s = _stream(stream, em_x)
-    _check("mep_to_expert_major", lib().mep_to_expert_major(
+    _check(fn, lib().mep_to_expert_major(
         h, _ptr(recv_x), _ptr(recv_scales), _ptr(recv_indices), _ptr(recv_counts),
         _ptr(src_token_pos), _ptr(em_x), _ptr(em_scales), _ptr(em_counts), _ptr(em_offsets),
         _ptr(em_src_pos), cap_em, s))
+    if st is not None:
+        st.update(cap_em=cap_em, em=True)
 
 
 def mep_combine(h, layout, y, weights, out, stream=None) -> None:
+    st = _state(h)
+    if _layout_ready(st, layout):
+        _check_combine_buffers("mep_combine", st, layout, y, 2, weights, out)
     s = _stream(stream, out)
     _check("mep_combine", lib().mep_combine(h, layout, _ptr(y), _ptr(weights), _ptr(out), s))
 
 
 def mep_combine_fp8(h, layout, y8, weights, out, stream=None) -> None:
+    st = _state(h)
+    if _layout_ready(st, layout):
+        _check_combine_buffers("mep_combine_fp8", st, layout, y8, 1, weights, out)
     s = _stream(stream, out)
     _check("mep_combine_fp8", lib().mep_combine_fp8(h, layout, _ptr(y8), _ptr(weights), _ptr(out),
                                                     s))
 
 
 def mep_combine_fp8_direct(h, layout, y, weights, out, stream=None) -> None:
+    st = _state(h)
+    if _layout_ready(st, layout):
+        _check_combine_buffers("mep_combine_fp8_direct", st, layout, y, 2, weights, out)
     s = _stream(stream, out)
     _check("mep_combine_fp8_direct", lib().mep_combine_fp8_direct(
         h, layout, _ptr(y), _ptr(weights), _ptr(out), s))
 
 
 def mep_cast_fp8_direct(h, layout, y, y8, stream=None) -> None:
+    st = _state(h)
+    if _layout_ready(st, layout):
+        rows, H = _combine_rows(st, layout), st["cfg"].hidden_dim
+        _need("mep_cast_fp8_direct", "y", y, rows * H * 2)
+        _need("mep_cast_fp8_direct", "y8", y8, rows * H)
     s = _stream(stream, y8)
     _check("mep_cast_fp8_direct", lib().mep_cast_fp8_direct(h, layout, _ptr(y), _ptr(y8), s))
 
 
 def mep_reset(h, stream=None) -> None:
     _check("mep_reset", lib().mep_reset(h, _stream(stream)))
+    st = _state(h)
+    if st is not None:
+        st.update(rm=False, em=False)
 
 
 def mep_get_status(h, stream=None) -> int:
@@ -217,6 +376,13 @@ def mep_get_status(h, stream=None) -> int:
 
 
 def mep_get_route(h, recv_row, em_row=None, stream=None) -> None:
+    st = _state(h)
+    if st is not None and st["T"] is not None:
+        n = 4 * st["T"] * st["cfg"].num_experts_per_token
+        if st["rm"]:
+            _need("mep_get_route", "recv_row", recv_row, n)
+        if st["em"]:
+            _need("mep_get_route", "em_row", em_row, n)
     s = _stream(stream, recv_row)
     _check("mep_get_route", lib().mep_get_route(h, _ptr(recv_row), _ptr(em_row), s))
 

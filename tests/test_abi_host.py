@@ -169,3 +169,36 @@ def test_binding_refuses_host_tensors():
         M.mep_probe_bf16(t, t, 0)
     from combine_mep_plan_amd import _binding as B
     assert B._ptr(None) is None and B._ptr(1 << 20) == 1 << 20
+
+
+def test_binding_checks_buffer_sizes():
+    # the binding knows each handle's config and last planned token count and
+    # refuses a buffer shorter than what the call would touch
+    import torch
+    c = cfg(quant=M.MEP_QUANT_FP8_E4M3_BLOCK128, scale_dim=56)
+    h = M.mep_create(c, FAKE, M.mep_workspace_bytes(c))
+    R, cap, H, k = c.world_size, c.max_num_inp_token_per_rank, c.hidden_dim, \
+        c.num_experts_per_token
+    i32 = lambda n: torch.zeros(n, dtype=torch.int32)  # noqa: E731
+    f32 = lambda n: torch.zeros(n, dtype=torch.float32)  # noqa: E731
+    T = 16
+    with pytest.raises(ValueError, match="indices holds"):
+        M.mep_plan(h, i32(T * k - 1), T, i32(R), i32(R * cap))
+    with pytest.raises(ValueError, match="src_token_pos holds"):
+        M.mep_plan(h, i32(T * k), T, i32(R), i32(R * cap - 1))
+    ok = dict(x=torch.zeros((T, H), dtype=torch.int16), w=f32(T * k),
+              rx=torch.zeros((R, cap, H), dtype=torch.uint8), rs=f32(R * cap * H // 128),
+              rw=f32(R * cap * k), ri=i32(R * cap * k))
+    for name, short in (("recv_x", torch.zeros(R * cap * H - 1, dtype=torch.uint8)),
+                        ("recv_scales", f32(R * cap * H // 128 - 1)),
+                        ("x", torch.zeros(T * H - 1, dtype=torch.int16))):
+        a = dict(ok)
+        a[{"recv_x": "rx", "recv_scales": "rs", "x": "x"}[name]] = short
+        with pytest.raises(ValueError, match=f"{name} holds"):
+            M.mep_plan_dispatch(h, i32(T * k), T, i32(R), i32(R * cap), a["x"], a["w"], None,
+                                a["rx"], a["rs"], a["rw"], a["ri"])
+    # every size right: the host tensors are then refused as host memory
+    with pytest.raises(ValueError, match="on the GPU"):
+        M.mep_plan_dispatch(h, i32(T * k), T, i32(R), i32(R * cap), ok["x"], ok["w"], None,
+                            ok["rx"], ok["rs"], ok["rw"], ok["ri"], stream=0)
+    M.mep_destroy(h)
