@@ -150,8 +150,19 @@ def _row_bytes_out(c) -> int:
     return c.hidden_dim
 
 
+_INT32 = {"indices", "recv_counts", "src_token_pos", "recv_indices", "em_counts",
+          "em_offsets", "em_src_pos", "recv_row", "em_row"}
+_FLOAT32 = {"weights", "recv_weights"}  # scale buffers hold opaque 32-bit words in some modes
+
+
 def _need(fn: str, name: str, t, nbytes: int) -> None:
-    if t is None or isinstance(t, int) or nbytes <= 0:
+    if t is None or isinstance(t, int):
+        return
+    import torch
+    want = torch.int32 if name in _INT32 else torch.float32 if name in _FLOAT32 else None
+    if want is not None and t.dtype != want:
+        raise ValueError(f"{fn}: {name} must be {want}, not {t.dtype}")
+    if nbytes <= 0:
         return
     have = t.numel() * t.element_size()
     if have < nbytes:

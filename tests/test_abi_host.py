@@ -197,6 +197,12 @@ def test_binding_checks_buffer_sizes():
         with pytest.raises(ValueError, match=f"{name} holds"):
             M.mep_plan_dispatch(h, i32(T * k), T, i32(R), i32(R * cap), a["x"], a["w"], None,
                                 a["rx"], a["rs"], a["rw"], a["ri"])
+    with pytest.raises(ValueError, match="indices must be torch.int32"):
+        M.mep_plan(h, torch.zeros(T * k, dtype=torch.int64), T, i32(R), i32(R * cap))
+    with pytest.raises(ValueError, match="weights must be torch.float32"):
+        M.mep_plan_dispatch(h, i32(T * k), T, i32(R), i32(R * cap), ok["x"],
+                            torch.zeros(T * k, dtype=torch.float64), None, ok["rx"], ok["rs"],
+                            ok["rw"], ok["ri"])
     # every size right: the host tensors are then refused as host memory
     with pytest.raises(ValueError, match="on the GPU"):
         M.mep_plan_dispatch(h, i32(T * k), T, i32(R), i32(R * cap), ok["x"], ok["w"], None,
