@@ -62,7 +62,7 @@ def draw(seed):
                 src_rank=src_rank, sd=sd, plant=plant)
 
 
-CASES = [draw(i) for i in range(48)]
+CASES = [draw(i) for i in range(200)]
 
 
 def _label(c):
