@@ -2,7 +2,8 @@
 
 Each case draws a configuration -- ranks, experts per rank, top-k, tokens,
 capacity slack, hidden size, payload mode, layout, fused or separate plan,
-source rank, planted bad or repeated expert ids -- runs the whole path through
+source rank, planted bad or repeated expert ids, combine payload (bf16, the
+E4M3 rounding in flight, or cast + E4M3 combine) -- runs the whole path through
 the C ABI and checks it against the oracle: plan outputs, received rows and
 scales, the expert-major layout (by conversion or by the standard-MoE call),
 and the combine.  The draws are small so the oracle stays fast; they reach
@@ -58,8 +59,10 @@ def draw(seed):
     src_rank = int(rng.integers(0, R))
     sd = H // 128 if quantising else (int(rng.choice([0, 1, 5])) if "carry" in mode else 0)
     plant = bool(rng.integers(0, 3) == 0)
+    # combine payload: bf16 rows, the E4M3 rounding in flight, or cast + E4M3 combine
+    combine = str(rng.choice(["bf16", "inflight", "cast"])) if H % 16 == 0 else "bf16"
     return dict(R=R, epr=epr, k=k, T=T, cap=cap, mode=mode, H=H, layout=layout, fused=fused,
-                src_rank=src_rank, sd=sd, plant=plant)
+                src_rank=src_rank, sd=sd, plant=plant, combine=combine)
 
 
 CASES = [draw(i) for i in range(200)]
@@ -67,7 +70,7 @@ CASES = [draw(i) for i in range(200)]
 
 def _label(c):
     return (f"{c['mode']}-{c['layout']}-R{c['R']}x{c['epr']}-k{c['k']}-T{c['T']}-H{c['H']}"
-            f"{'-fused' if c['fused'] else ''}{'-plant' if c['plant'] else ''}")
+            f"{'-fused' if c['fused'] else ''}{'-plant' if c['plant'] else ''}-{c['combine']}")
 
 
 def _inputs(c, seed):
@@ -167,12 +170,36 @@ def test_random_config(c):
 
     # rank-major combine on bf16 expert outputs derived from the received rows
     y_np = _outputs(d["recv_x"], byte_rows, H)
-    out = torch.empty((max(T, 1), H), dtype=torch.int16, device="cuda")
-    M.mep_combine(m.h, M.MEP_RANK_MAJOR, dev(y_np), d_w, out)
-    ref = O.combine(y_np, w, idx.reshape(T, k), pl, epr, cap)
+    out = _run_combine(c, m, M.MEP_RANK_MAJOR, y_np, d_w, T, H)
+    ref = O.combine(_as_combined(c, y_np, written), w, idx.reshape(T, k), pl, epr, cap)
     torch.cuda.synchronize()
     if T:
         check_combine(host(out, np.uint16)[:T], ref)
+
+
+def _run_combine(c, m, layout, y_np, d_w, T, H):
+    """The configuration's combine call on bf16 expert outputs y_np."""
+    y = dev(y_np)
+    out = torch.empty((max(T, 1), H), dtype=torch.int16, device="cuda")
+    if c["combine"] == "inflight":
+        M.mep_combine_fp8_direct(m.h, layout, y, d_w, out)
+    elif c["combine"] == "cast":
+        y8 = torch.zeros(y.shape, dtype=torch.uint8, device="cuda")
+        M.mep_cast_fp8_direct(m.h, layout, y, y8)
+        M.mep_combine_fp8(m.h, layout, y8, d_w, out)
+    else:
+        M.mep_combine(m.h, layout, y, d_w, out)
+    return out
+
+
+def _as_combined(c, y_np, used):
+    """The values the combine multiplies: y_np itself, or, with the E4M3
+    payload, its direct cast decoded back (rows in `used` only)."""
+    if c["combine"] == "bf16":
+        return y_np
+    y = np.zeros_like(y_np)
+    y[used] = O.e4m3_to_bf16(O.cast_fp8_direct(y_np[used]))
+    return y
 
 
 def _outputs(rows, byte_rows, H):
@@ -215,9 +242,11 @@ def _check_em(c, em, emx, ems, emc, emo, emp, m, T, k, cap_em, byte_rows, sd):
 
 def _combine_em(c, m, em, em_route, emx, w, T, H, cap_em, byte_rows):
     y_np = _outputs(em["em_x"], byte_rows, H)
-    out = torch.empty((max(T, 1), H), dtype=torch.int16, device="cuda")
-    M.mep_combine(m.h, M.MEP_EXPERT_MAJOR, dev(y_np), dev(w) if T else None, out)
-    ref = O.combine_em(y_np, w, em["tok_em_row"])
+    out = _run_combine(c, m, M.MEP_EXPERT_MAJOR, y_np, dev(w) if T else None, T, H)
+    used = np.zeros(y_np.shape[0], bool)
+    rows = em["tok_em_row"]
+    used[rows[rows >= 0]] = True
+    ref = O.combine_em(_as_combined(c, y_np, used), w, em["tok_em_row"])
     torch.cuda.synchronize()
     if T:
         check_combine(host(out, np.uint16)[:T], ref)
