@@ -21,9 +21,9 @@ import combine_mep_plan_amd as M
 from oracle import oracle as O
 from synthetic import WORKLOADS, Workload, make_inputs
 
-from _gpu_harness import (SENT32, bf16_ulp_diff, check_combine, check_plan_dispatch, dev,
-                          gpu_plan_dispatch, host, oracle_plan_dispatch, run_full,
-                          stand_in_oracle)
+from _gpu_harness import (SENT32, GpuRun, alloc_recv, bf16_ulp_diff, check_combine,
+                          check_plan_dispatch, dev, gpu_plan_dispatch, host, oracle_plan_dispatch,
+                          run_full, stand_in_oracle)
 
 pytestmark = pytest.mark.gpu
 
@@ -337,6 +337,35 @@ def test_fused_plan_dispatch_long_batches(T, R):
         pl, d = oracle_plan_dispatch(wl, inp, src_rank=1)
         check_plan_dispatch(wl, inp, g, pl, d)
         assert M.mep_get_status(g.m.h) == 0
+
+
+@pytest.mark.parametrize("R", [1, 3, 8, 12, 16])
+def test_fused_plan_dispatch_repeated(R):
+    # one handle, successive fused calls with fresh routing each time, over
+    # batch sizes that take the two-launch path (above 256 tokens) and the
+    # one-launch path (100 tokens) in turn: every call must match the oracle
+    # whatever the call before it left in the workspace
+    cap = 4096
+    wl0 = Workload("lb", cap, 256, R, 8, 8, cap, "fp8", "uniform", "dequant_half", "rank_major")
+    src = min(2, R - 1)
+    m = M.Mep(wl0.hidden, wl0.experts_per_rank, wl0.topk, cap, R, rank=src, fp8=True)
+    for i, T in enumerate([cap, 257, 1000, 100, cap - 1, 64 * 5 + 3, cap]):
+        wl = dataclasses.replace(wl0, tokens=T)
+        inp = make_inputs(wl, 300 + i)
+        x, w, idx = dev(inp["x"]), dev(inp["weights"]), dev(inp["indices"])
+        counts = torch.full((R,), SENT32, dtype=torch.int32, device="cuda")
+        spos = torch.full((R, cap), SENT32, dtype=torch.int32, device="cuda")
+        recv = alloc_recv(wl)
+        M.mep_plan_dispatch(m.h, idx, T, counts, spos, x, w, None, *recv)
+        route = torch.full((T, wl.topk), SENT32, dtype=torch.int32, device="cuda")
+        M.mep_get_route(m.h, route)
+        torch.cuda.synchronize()
+        g = GpuRun(m, x, w, idx, counts, spos, *recv, route)
+        pl, d = oracle_plan_dispatch(wl, inp, src_rank=src)
+        _say(f"R={R} call {i} T={T}")
+        check_plan_dispatch(wl, inp, g, pl, d)
+        assert M.mep_get_status(m.h) == 0
+        M.mep_reset(m.h)
 
 
 @pytest.mark.parametrize("T", [128, 700])
