@@ -21,9 +21,9 @@ import combine_mep_plan_amd as M
 from oracle import oracle as O
 from synthetic import WORKLOADS, Workload, make_inputs
 
-from _gpu_harness import (SENT32, GpuRun, alloc_recv, bf16_ulp_diff, check_combine,
-                          check_plan_dispatch, dev, gpu_plan_dispatch, host, oracle_plan_dispatch,
-                          run_full, stand_in_oracle)
+from _gpu_harness import (SENT8, SENT32, GpuRun, alloc_recv, bf16_ulp_diff, check_combine,
+                          check_expert_major, check_plan_dispatch, dev, gpu_plan_dispatch, host,
+                          oracle_plan_dispatch, run_full, stand_in_oracle)
 
 pytestmark = pytest.mark.gpu
 
@@ -406,6 +406,55 @@ def test_hip_graph_capture_replay(T):
                                   d["recv_scales"][r, :n].view(np.uint32)), rep
         ref = O.combine(yo, new["weights"], new["indices"], pl, epr, cap)
         check_combine(host(out, np.uint16), ref)
+    assert M.mep_get_status(g.m.h) == 0
+
+
+def test_hip_graph_expert_major_replay():
+    # plan+dispatch, the expert-major conversion and the expert-major combine
+    # captured once in a HIP graph, replayed with new routing and token rows
+    # (eager refills in between): each replay must match the oracle
+    wl = _variant("stdmoe", tokens=700, cap=1024, hidden=1024)
+    T, H, cap_em = wl.tokens, wl.hidden, wl.cap_em
+    inp = make_inputs(wl, 400)
+    g = gpu_plan_dispatch(wl, inp, fused=True)
+    em_x = torch.empty((cap_em, H), dtype=torch.uint8, device="cuda")
+    em_s = torch.empty((cap_em, H // 128), dtype=torch.float32, device="cuda")
+    em_counts = torch.empty((wl.experts,), dtype=torch.int32, device="cuda")
+    em_offsets = torch.empty((wl.experts + 1,), dtype=torch.int32, device="cuda")
+    em_src = torch.empty((cap_em,), dtype=torch.int32, device="cuda")
+    y = torch.zeros((cap_em, H), dtype=torch.int16, device="cuda")
+    out = torch.zeros((T, H), dtype=torch.int16, device="cuda")
+    M.mep_to_expert_major(g.m.h, g.recv_x, g.recv_s, g.recv_i, g.counts, g.spos, em_x, em_s,
+                          em_counts, em_offsets, em_src, cap_em)  # eager warm-up
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        M.mep_plan_dispatch(g.m.h, g.idx, T, g.counts, g.spos, g.x, g.w, None, g.recv_x, g.recv_s,
+                            g.recv_w, g.recv_i)
+        M.mep_to_expert_major(g.m.h, g.recv_x, g.recv_s, g.recv_i, g.counts, g.spos, em_x, em_s,
+                              em_counts, em_offsets, em_src, cap_em)
+        M.mep_combine(g.m.h, M.MEP_EXPERT_MAJOR, y, g.w, out)
+    for rep in range(4):
+        new = make_inputs(wl, 500 + rep)
+        g.x.copy_(dev(new["x"]))
+        g.idx.copy_(dev(new["indices"]))
+        g.w.copy_(dev(new["weights"]))
+        em_x.fill_(SENT8)
+        em_src.fill_(SENT32)
+        pl, d = oracle_plan_dispatch(wl, new)
+        em = O.to_expert_major(d, pl, wl.ranks, wl.experts_per_rank, wl.cap, T, cap_em, 0)
+        y_ref = stand_in_oracle(wl, em["em_x"], em["em_scales"])
+        y.copy_(dev(y_ref))  # the expert stand-in for this replay, written before it
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _say(f"expert-major replay {rep}")
+        em_route = torch.full((T, wl.topk), SENT32, dtype=torch.int32, device="cuda")
+        M.mep_get_route(g.m.h, torch.empty((T, wl.topk), dtype=torch.int32, device="cuda"),
+                        em_route)
+        torch.cuda.synchronize()
+        check_expert_major(wl, em, em_x, em_s, em_counts, em_offsets, em_src, em_route)
+        check_combine(host(out, np.uint16), O.combine_em(y_ref, new["weights"], em["tok_em_row"]))
     assert M.mep_get_status(g.m.h) == 0
 
 
