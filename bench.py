@@ -383,7 +383,9 @@ def time_decode(M, torch, wl, inp, reps, warmup):
     the two events bracket only GPU work (launch processing included, host
     submission excluded); host: the GPU is idle when the first event is
     recorded, so host submission time is included.  graph: plan+dispatch and
-    combine captured in one HIP graph and replayed (device timing)."""
+    combine captured in one HIP graph and replayed (device timing).
+    launch_floor: the library's smallest kernel (one workgroup converting two
+    values: a load and a store) timed the same way."""
     r = Runner(M, torch, wl, inp, 4)
     stream = r.stream
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -400,8 +402,13 @@ def time_decode(M, torch, wl, inp, reps, warmup):
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e3
 
+    # launch floor: a one-workgroup kernel of the library (one load, one store)
+    # queued and timed the same way, for scale
+    fin = torch.zeros(64, dtype=torch.float32, device="cuda")
+    fout = torch.zeros(64, dtype=torch.int16, device="cuda")
     seqs = {"plan_dispatch": [r.plan_dispatch], "combine": [r.combine], "plan": [r.plan],
-            "dispatch": [r.dispatch]}
+            "dispatch": [r.dispatch],
+            "launch_floor": [lambda s: M.mep_probe_bf16(fin, fout, 2, stream)]}
     res = {}
     for i in range(warmup + reps):
         s = r.sets[i % len(r.sets)]
