@@ -493,6 +493,25 @@ def test_two_handles_on_two_streams():
         assert M.mep_get_status(g.m.h, streams[i]) == 0
 
 
+@pytest.mark.parametrize("H,T,R,epr,k,quant,layout", [
+    (16384, 200, 8, 4, 4, "fp8", "rank_major"),
+    (16384, 200, 8, 4, 4, "fp8", "expert_major"),
+    (16384, 77, 4, 4, 8, "none", "rank_major"),
+    (1 << 20, 9, 2, 2, 2, "fp8", "rank_major"),
+    (1 << 20, 9, 2, 2, 2, "none", "rank_major"),
+])
+def test_wide_hidden(H, T, R, epr, k, quant, layout):
+    # rows wider than the 7168-column workloads, up to the widest the config
+    # accepts (2^20 columns: 1024 combine slices per token, 8192 scale words
+    # per FP8 row); whole path, both call modes, last rank as the source
+    expert = "identity" if quant == "none" else "dequant_half"
+    wl = Workload("wide", T, H, R, epr, k, T, quant, "uniform", expert, layout)
+    for fused in (False, True):
+        _say(f"H={H} T={T} R={R} {quant} {layout} fused={fused}")
+        st = run_full(wl, 11, src_rank=R - 1, fused=fused)
+        assert st["max_ulp"] <= 1
+
+
 def test_buffers_past_4_gib():
     # 45000 bf16 tokens of 7168 columns: the receive buffers (5.2 GB) and the
     # expert-major rows (5.6 GB) reach byte offsets past 2^32, so every row
