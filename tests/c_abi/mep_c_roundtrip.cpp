@@ -15,6 +15,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
+#include <chrono>
 #include <vector>
 
 #include "mep.h"
@@ -206,7 +208,72 @@ static int run_case(const char* name, int H, int T, int R, int epr, int k, int c
   return bad;
 }
 
-int main() {
+// Host time of the C ABI calls themselves (argument checks and kernel
+// submission, no Python): 100 back-to-back calls of the 128-token x 7168 decode
+// shape, few enough that the queue never blocks the host; the GPU work is
+// waited for outside the timed region.  Median of 20 repeats, microseconds per
+// call.
+static void host_cost() {
+  const int H = 7168, T = 128, R = 8, epr = 32, k = 8, cap = 128, n = 100;
+  g_state = 5;
+  std::vector<uint16_t> x((size_t)T * H, 0x3f80);
+  std::vector<int32_t> idx((size_t)T * k);
+  for (int t = 0; t < T; ++t)
+    for (int j = 0; j < k; ++j) idx[(size_t)t * k + j] = (t * 37 + j * 32) % (R * epr);
+  std::vector<float> w((size_t)T * k, 0.125f);
+  mep_config cfg{H, 0, epr, k, cap, R, 0, MEP_QUANT_NONE};
+  const size_t wsb = mep_workspace_bytes(&cfg);
+  unsigned char* ws = dev_alloc<unsigned char>(wsb, 0);
+  mep_handle* h = nullptr;
+  if (mep_create(&cfg, ws, wsb, &h) != MEP_OK) { fprintf(stderr, "create\n"); exit(1); }
+  uint16_t* d_x = dev_alloc<uint16_t>(x.size(), 0);
+  int32_t* d_idx = dev_alloc<int32_t>(idx.size(), 0);
+  float* d_w = dev_alloc<float>(w.size(), 0);
+  HIP_OK(hipMemcpy(d_x, x.data(), x.size() * 2, hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(d_idx, idx.data(), idx.size() * 4, hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(d_w, w.data(), w.size() * 4, hipMemcpyHostToDevice));
+  int32_t* d_counts = dev_alloc<int32_t>(R, 0);
+  int32_t* d_spos = dev_alloc<int32_t>((size_t)R * cap, 0);
+  uint16_t* d_rx = dev_alloc<uint16_t>((size_t)R * cap * H, 0);
+  float* d_rw = dev_alloc<float>((size_t)R * cap * k, 0);
+  int32_t* d_ri = dev_alloc<int32_t>((size_t)R * cap * k, 0);
+  uint16_t* d_out = dev_alloc<uint16_t>((size_t)T * H, 0);
+  auto pd = [&]() {
+    return mep_plan_dispatch(h, d_idx, T, d_counts, d_spos, d_x, d_w, nullptr, d_rx, nullptr,
+                             d_rw, d_ri, nullptr);
+  };
+  auto cb = [&]() { return mep_combine(h, MEP_RANK_MAJOR, d_rx, d_w, d_out, nullptr); };
+  for (int i = 0; i < 50; ++i)
+    if (pd() != MEP_OK || cb() != MEP_OK) { fprintf(stderr, "call failed\n"); exit(1); }
+  HIP_OK(hipDeviceSynchronize());
+  std::vector<double> t_pd, t_cb;
+  for (int rep = 0; rep < 20; ++rep) {
+    auto t0 = std::chrono::steady_clock::now();
+    for (int i = 0; i < n; ++i) pd();
+    auto t1 = std::chrono::steady_clock::now();
+    HIP_OK(hipDeviceSynchronize());
+    auto t2 = std::chrono::steady_clock::now();
+    for (int i = 0; i < n; ++i) cb();
+    auto t3 = std::chrono::steady_clock::now();
+    HIP_OK(hipDeviceSynchronize());
+    t_pd.push_back(std::chrono::duration<double, std::micro>(t1 - t0).count() / n);
+    t_cb.push_back(std::chrono::duration<double, std::micro>(t3 - t2).count() / n);
+  }
+  std::sort(t_pd.begin(), t_pd.end());
+  std::sort(t_cb.begin(), t_cb.end());
+  printf("host us per call (C, decode 128 x 7168): plan_dispatch %.2f combine %.2f\n",
+         t_pd[t_pd.size() / 2], t_cb[t_cb.size() / 2]);
+  mep_destroy(h);
+  for (void* p : {(void*)ws, (void*)d_x, (void*)d_idx, (void*)d_w, (void*)d_counts,
+                  (void*)d_spos, (void*)d_rx, (void*)d_rw, (void*)d_ri, (void*)d_out})
+    HIP_OK(hipFree(p));
+}
+
+int main(int argc, char** argv) {
+  if (argc > 1 && strcmp(argv[1], "--host-cost") == 0) {
+    host_cost();
+    return 0;
+  }
   int bad = 0;
   bad += run_case("ragged bf16", 256, 37, 4, 2, 2, 40, MEP_QUANT_NONE, 1, true, 1);
   bad += run_case("ragged bf16", 256, 37, 4, 2, 2, 40, MEP_QUANT_NONE, 1, false, 2);

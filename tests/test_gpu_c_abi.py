@@ -4,7 +4,8 @@ allocates device memory with the HIP runtime, runs plan+dispatch (fused and
 separate, one and two plan launches) and combine through the mep_* entry
 points on the default stream, including the 128-token x 7168 decode shape,
 and compares every output with the CPU oracle: bit-exact receive data,
-combine within 1 bf16 ulp.  It runs as a child process."""
+combine within 1 bf16 ulp.  It runs as a child process; a second run reports
+the host time of the ABI calls themselves (no Python) at the decode shape."""
 
 import os
 import subprocess
@@ -22,3 +23,11 @@ def test_c_program_round_trip():
     print(r.stdout, r.stderr, flush=True)
     assert r.returncode == 0, r.stderr
     assert "c_abi ok" in r.stdout
+
+
+def test_c_program_host_cost():
+    assert os.path.exists(BIN), f"{BIN} is missing: build it with __graft_entry__.build()"
+    r = subprocess.run([BIN, "--host-cost"], capture_output=True, text=True, timeout=120)
+    print(r.stdout, r.stderr, flush=True)
+    assert r.returncode == 0, r.stderr
+    assert "host us per call" in r.stdout
