@@ -109,11 +109,20 @@ def _ptr(t):
 
 
 def _stream(stream, *tensors):
+    """The HIP stream to launch on: the one given, else torch's current stream
+    on the device of the first GPU tensor (the current device if none).  The
+    raw-handle query takes ~0.1 us against ~2.5 us for building a Stream
+    object, a fifth of a decode call's host time."""
     if stream is not None:
         return stream if isinstance(stream, int) else stream.cuda_stream
     import torch
-    dev = next((t.device for t in tensors if hasattr(t, "device") and t.device.type == "cuda"),
-               None)
+    dev = next((d for d in (t.get_device() for t in tensors if hasattr(t, "get_device"))
+                if d >= 0), None)
+    if dev is None:
+        dev = torch.cuda.current_device()
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(dev)
     return torch.cuda.current_stream(dev).cuda_stream
 
 
@@ -164,7 +173,7 @@ def _need(fn: str, name: str, t, nbytes: int) -> None:
         raise ValueError(f"{fn}: {name} must be {want}, not {t.dtype}")
     if nbytes <= 0:
         return
-    have = t.numel() * t.element_size()
+    have = t.nbytes
     if have < nbytes:
         raise ValueError(f"{fn}: {name} holds {have} bytes, the call touches {nbytes}")
 
