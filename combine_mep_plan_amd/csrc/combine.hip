@@ -229,12 +229,17 @@ __global__ __launch_bounds__(256) void combine_wide_kernel(CombineArgs a) {
   }
 }
 
-// Every top-k position loads its row, also when it shares a rank row with an
-// earlier position (about half of such repeats hit the caches): selecting
-// among already loaded registers, as the bf16 kernel does, here made the
-// compiler wait on each load in turn.
-template <int KMAX>
+// Up to top-8, each distinct row is loaded once.  Positions sharing a rank
+// row (DEDUPE) read it back from LDS: every lane parks the units of the rows
+// that later positions repeat in its own LDS slots (at most KMAX/2 per wave)
+// and reads them at a uniform slot.  (Selecting among loaded registers, as
+// the bf16 kernel does, here compiled to a dynamic register index with a
+// wait after every load.)  Whether a position loads is folded into the lane's
+// column bound, so the loads are masked instructions in straight-line code.
+template <int KMAX, bool DEDUPE>
 __global__ __launch_bounds__(256) void combine_fp8_kernel(CombineArgs a) {
+  constexpr int kSlots = DEDUPE ? KMAX / 2 : 1;  // repeated rows per wave
+  __shared__ u32x4 stage[4 * kSlots][kWave];
   const int lane = threadIdx.x & 63;
   const int g = first_lane(blockIdx.x * 4 + (threadIdx.x >> 6));
   const int t = g / a.slices, sl = g - t * a.slices;
@@ -247,22 +252,44 @@ __global__ __launch_bounds__(256) void combine_fp8_kernel(CombineArgs a) {
     row[j] = j < a.k ? a.rows[(size_t)t * a.k + j] : -1;
     w[j] = j < a.k ? a.w[(size_t)t * a.k + j] : 0.0f;
   }
+  // src[j]: first top-k position holding the same row as j; need: positions
+  // whose row a later one repeats (both uniform)
+  int src[KMAX];
+  uint32_t need = 0;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    src[j] = j;
+    if (DEDUPE) {
+#pragma unroll
+      for (int jj = KMAX - 1; jj >= 0; --jj)
+        if (jj < j && row[jj] == row[j]) src[j] = jj;
+      if (src[j] != j) need |= 1u << src[j];
+    }
+  }
   const u32x4* y = reinterpret_cast<const u32x4*>(a.y);
   const int v = sl * kWave + lane;
   u32x4 in[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
     in[j] = u32x4{0, 0, 0, 0};
-    if (row[j] >= 0 && v < nv8) in[j] = __builtin_nontemporal_load(y + (size_t)row[j] * nv8 + v);
+    const int lim = row[j] >= 0 && src[j] == j ? nv8 : 0;
+    if (v < lim) in[j] = __builtin_nontemporal_load(y + (size_t)row[j] * nv8 + v);
   }
   if (v >= nv8) return;
+  u32x4(*mine)[kWave] = stage + (threadIdx.x >> 6) * kSlots;  // this wave's slots
+  if (DEDUPE) {
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if ((need >> j) & 1u) mine[__popc(need & ((1u << j) - 1u))][lane] = in[j];
+  }
   float acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
     if (row[j] < 0) continue;  // uniform
-    const u32x4 x = in[j];
+    u32x4 x = in[j];
+    if (DEDUPE && src[j] != j) x = mine[__popc(need & ((1u << src[j]) - 1u))][lane];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[i], false);  // bytes 0, 1
@@ -417,7 +444,10 @@ hipError_t launch_combine_fp8(const CombineArgs& a0, hipStream_t s) {
   a.slice_units = kWave;
   a.slices = (a.H / 16 + kWave - 1) / kWave;
   const int blocks = (int)(((int64_t)a.T * a.slices + 3) / 4);
-  if (a.k <= 8) combine_fp8_kernel<8><<<blocks, 256, 0, s>>>(a);
+  if (a.k <= 8) {
+    if (a.distinct_rows) combine_fp8_kernel<8, false><<<blocks, 256, 0, s>>>(a);
+    else combine_fp8_kernel<8, true><<<blocks, 256, 0, s>>>(a);
+  }
   else combine_fp8_wide_kernel<<<blocks, 256, 0, s>>>(a);
   return hipGetLastError();
 }
