@@ -247,6 +247,39 @@ def test_fp8_direct_cast_and_combine_rank_major(T, sample):
     _say(f"[fp8 direct] T={T}: {stats}")
 
 
+@pytest.mark.parametrize("R,epr,k", [(1, 8, 8), (2, 8, 8), (4, 4, 8), (3, 4, 7), (8, 2, 5)])
+def test_fp8_combine_shared_rank_rows(R, epr, k):
+    # top-k positions sharing rank rows: one rank (eight positions on one row),
+    # four ranks at top-8 (up to four rows repeated), an odd top-7, top-5:
+    # every repeated row is read back from where the E4M3 combine parks it
+    wl = dataclasses.replace(WORKLOADS["prefill"], tokens=300, cap=300, hidden=512, ranks=R,
+                             experts_per_rank=epr, topk=k)
+    _say(f"[fp8 direct] shared rank rows R={R} epr={epr} k={k}")
+    inp = make_inputs(wl, 61)
+    T, cap, H = wl.tokens, wl.cap, wl.hidden
+    m = _mep(wl, M.MEP_QUANT_NONE, 0)
+    counts = torch.empty(R, dtype=torch.int32, device="cuda")
+    spos = torch.empty((R, cap), dtype=torch.int32, device="cuda")
+    idx, w = dev(inp["indices"]), dev(inp["weights"])
+    M.mep_plan(m.h, idx, T, counts, spos)
+    y = _expert_outputs((R * cap, H), 61)
+    y_dev = dev(y)
+    y8 = torch.full((R, cap, H), SENT8, dtype=torch.uint8, device="cuda")
+    M.mep_cast_fp8_direct(m.h, M.MEP_RANK_MAJOR, y_dev, y8)
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    M.mep_combine_fp8(m.h, M.MEP_RANK_MAJOR, y8, w, out)
+    torch.cuda.synchronize()
+    _check_in_flight(m, M.MEP_RANK_MAJOR, y_dev, w, out)
+    pl = O.plan(inp["indices"], R, epr, cap)
+    used = (np.arange(cap)[None, :] < pl["recv_counts"][:, None]).reshape(-1)
+    tok_rows = (inp["indices"] // epr) * cap + pl["slot"]
+    ref_fn = lambda y8r: O.combine(y8r.reshape(R, cap, H), inp["weights"], inp["indices"],  # noqa: E731
+                                   pl, epr, cap)
+    stats = _check_cast_combine(y, y8, out, used, tok_rows, ref_fn, T, None)
+    _say(f"[fp8 direct] R={R} k={k}: {stats}")
+    assert M.mep_get_status(m.h) == 0
+
+
 @pytest.mark.parametrize("T,sample", [(300, None), (4096, 48)])
 def test_fp8_direct_cast_and_combine_expert_major(T, sample):
     wl = WORKLOADS["stdmoe"].with_tokens(T)
