@@ -68,6 +68,19 @@
  *      combine): each expert-output value is cast
  *      to OCP E4M3 with no scale (round to nearest even, saturating at 448);
  *      the combine accumulates the decoded values exactly as R6.
+ *   R21 standard-MoE expert outputs back to the combine input ([Guide]
+ *      section 4, convert_combine_input(packed rows, source info, layout
+ *      range), which takes no weights): one bf16 row per received row (rank
+ *      r, slot s), the fp32 chain acc = fmaf(w_j, y_j, acc) from +0 over the
+ *      top-k positions j of that row whose expert lives on rank r and that are
+ *      the first naming their expert, in j order, rounded once; w_j is the
+ *      dispatched weight (recv weights [r][s][j]) and y_j the expert-major row
+ *      of expert j whose source info is the row's src_token_pos.  The weights
+ *      are applied here because one merged row per (token, rank) can carry a
+ *      top-k weighted sum only if each expert's weight is applied before the
+ *      merge; the combine of converted rows therefore adds a token's distinct
+ *      rank rows without weights, in the order of their first top-k position,
+ *      one fp32 rounding per addition, then bf16.
  */
 #include <math.h>
 #include <stdint.h>
@@ -459,4 +472,91 @@ void oracle_expert_dequant(const uint8_t *q, const float *scales, int64_t rows, 
       p = p * mult;
       y[i * H + h] = oracle_bf16_rne(p);
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Expert-major expert outputs back to the rank-major combine input          */
+/* ([Guide] section 4, convert_combine_input(): standard-MoE rows, their      */
+/* source info and layout, turned into the rows the combine takes; reading   */
+/* R21).                                                                     */
+/*                                                                          */
+/* y_em [cap_em,H] bf16 expert outputs in the layout em_counts/em_offsets/   */
+/* em_src_pos describe; recv_w, recv_idx [R,cap,k], recv_counts [R] and      */
+/* src_token_pos [R,cap] from the dispatch.  For every received row (r, s),  */
+/* s < recv_counts[r], with source position p = src_token_pos[r][s]:         */
+/*   y_rm[r][s][h] = bf16_rne(acc), acc = +0, then for j = 0..k-1 in order,  */
+/*   over positions whose expert e lives on rank r and that are the first    */
+/*   naming e: acc = fmaf(recv_w[r][s][j], y_em[i][h], acc), i the row of    */
+/*   e's segment whose source info is p.                                     */
+/* Rows past recv_counts[r] are not written.  A position whose expert-major  */
+/* row is absent (dropped past cap_em) adds nothing.  em_of_j: [k] scratch.  */
+/* ------------------------------------------------------------------------ */
+void oracle_convert_combine_input(const uint16_t *y_em, int64_t cap_em, const int32_t *em_counts,
+                                  const int32_t *em_offsets, const int32_t *em_src_pos,
+                                  const float *recv_w, const int32_t *recv_idx,
+                                  const int32_t *recv_counts, const int32_t *src_token_pos,
+                                  int32_t R, int32_t epr, int32_t cap, int32_t H, int32_t k,
+                                  uint16_t *y_rm, int64_t *em_of_j) {
+  int32_t E = R * epr;
+  for (int32_t r = 0; r < R; r++) {
+    for (int32_t s = 0; s < recv_counts[r]; ++s) {
+      int64_t row = (int64_t)r * cap + s;
+      const int32_t *ids = recv_idx + row * k;
+      int32_t pos = src_token_pos[row];
+      for (int32_t j = 0; j < k; j++) {
+        int32_t e = ids[j];
+        em_of_j[j] = -1;
+        if (e < 0 || e >= E) continue;
+        if (e / epr != r) continue; /* the expert lives on another rank */
+        int first = 1;
+        for (int32_t jj = 0; jj < j; jj++)
+          if (ids[jj] == e) first = 0;
+        if (!first) continue; /* a repeated expert has one row */
+        int64_t end = (int64_t)em_offsets[e] + em_counts[e];
+        if (end > cap_em) end = cap_em;
+        for (int64_t i = em_offsets[e]; i < end; i++)
+          if (em_src_pos[i] == pos) { em_of_j[j] = i; break; }
+      }
+      for (int32_t h = 0; h < H; h++) {
+        float acc = 0.0f;
+        for (int32_t j = 0; j < k; j++) {
+          if (em_of_j[j] < 0) continue;
+          acc = fmaf(recv_w[row * k + j], oracle_bf16_to_f32(y_em[em_of_j[j] * H + h]), acc);
+        }
+        y_rm[row * H + h] = oracle_bf16_rne(acc);
+      }
+    }
+  }
+}
+
+/* Combine of converted rows (reading R21): for every token t,
+ *   out[t][h] = bf16_rne(acc), acc = +0, then over t's destination ranks in
+ *   the order of their first top-k position: acc = acc + y_rm[r][slot][h]
+ *   (one fp32 rounding per addition, no weights: the converted rows already
+ *   carry them).  Tokens that were not dispatched give +0.
+ * rank_of_j: [k] scratch. */
+void oracle_combine_rank_sum(const uint16_t *y_rm, const int32_t *idx, const int32_t *slot,
+                             int32_t T, int32_t H, int32_t k, int32_t epr, int32_t cap,
+                             uint16_t *out, int64_t *row_of_j) {
+  for (int32_t t = 0; t < T; t++) {
+    const int32_t *e = idx + (int64_t)t * k;
+    for (int32_t j = 0; j < k; j++) {
+      int32_t s = slot[(int64_t)t * k + j];
+      int32_t r = e[j] / epr;
+      row_of_j[j] = -1;
+      if (s < 0) continue;
+      int first = 1;
+      for (int32_t jj = 0; jj < j; jj++)
+        if (e[jj] / epr == r) first = 0;
+      if (first) row_of_j[j] = (int64_t)r * cap + s; /* one row per destination rank */
+    }
+    for (int32_t h = 0; h < H; h++) {
+      float acc = 0.0f;
+      for (int32_t j = 0; j < k; j++) {
+        if (row_of_j[j] < 0) continue;
+        acc = acc + oracle_bf16_to_f32(y_rm[row_of_j[j] * H + h]);
+      }
+      out[(int64_t)t * H + h] = oracle_bf16_rne(acc);
+    }
+  }
 }

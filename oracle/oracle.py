@@ -70,6 +70,9 @@ def lib():
         L.oracle_to_expert_major.restype = i32
         L.oracle_combine_em.argtypes = [p, p, p, i32, i32, i32, p]
         L.oracle_expert_dequant.argtypes = [p, p, i64, i32, f32, p]
+        L.oracle_convert_combine_input.argtypes = [p, i64, p, p, p, p, p, p, p, i32, i32, i32,
+                                                   i32, i32, p, p]
+        L.oracle_combine_rank_sum.argtypes = [p, p, p, i32, i32, i32, i32, i32, p, p]
         _lib = L
     return _lib
 
@@ -267,6 +270,46 @@ def combine_em(y_em: np.ndarray, weights: np.ndarray, tok_em_row: np.ndarray) ->
     H = y_em.shape[-1]
     out = np.empty((T, H), dtype=np.uint16)
     lib().oracle_combine_em(_p(y_em), _p(w), _p(tok), T, H, k, _p(out))
+    return out
+
+
+def convert_combine_input(y_em: np.ndarray, em: dict, disp: dict, pl: dict, R: int, epr: int,
+                          cap: int, fill: int = 0) -> np.ndarray:
+    """Reading R21: expert-major expert outputs y_em ([cap_em,H] bf16 bits, in
+    the layout `em` describes) back to one bf16 row per received row,
+    [R,cap,H]; each row is its rank's experts' outputs weighted by the
+    dispatched weights (disp["recv_weights"]).  Rows past the counts keep
+    ``fill``."""
+    y_em = np.ascontiguousarray(y_em, dtype=np.uint16)
+    cap_em, H = y_em.shape
+    rw = np.ascontiguousarray(disp["recv_weights"], dtype=np.float32)
+    ri = np.ascontiguousarray(disp["recv_indices"], dtype=np.int32)
+    k = ri.shape[-1]
+    out = np.full((R, cap, H), fill, dtype=np.uint16)
+    tmp = np.empty(k, dtype=np.int64)
+    lib().oracle_convert_combine_input(
+        _p(y_em), cap_em, _p(np.ascontiguousarray(em["em_counts"], dtype=np.int32)),
+        _p(np.ascontiguousarray(em["em_offsets"], dtype=np.int32)),
+        _p(np.ascontiguousarray(em["em_src_pos"], dtype=np.int32)), _p(rw), _p(ri),
+        _p(np.ascontiguousarray(pl["recv_counts"], dtype=np.int32)),
+        _p(np.ascontiguousarray(pl["src_token_pos"], dtype=np.int32)), R, epr, cap, H, k,
+        _p(out), _p(tmp))
+    return out
+
+
+def combine_rank_sum(y_rm: np.ndarray, indices: np.ndarray, pl: dict, epr: int,
+                     cap: int) -> np.ndarray:
+    """Reading R21: combine of converted rows -- each token's distinct rank
+    rows added in fp32 in the order of their first top-k position, no
+    weights, then bf16."""
+    y_rm = np.ascontiguousarray(y_rm, dtype=np.uint16)
+    idx = np.ascontiguousarray(indices, dtype=np.int32)
+    T, k = idx.shape
+    H = y_rm.shape[-1]
+    out = np.empty((T, H), dtype=np.uint16)
+    tmp = np.empty(k, dtype=np.int64)
+    lib().oracle_combine_rank_sum(_p(y_rm), _p(idx), _p(np.ascontiguousarray(pl["slot"])), T, H,
+                                  k, epr, cap, _p(out), _p(tmp))
     return out
 
 

@@ -81,6 +81,32 @@ MUTATIONS = [
      "test_mx4_exact_blocks_round_trip"),
     ("mx_nibble_order", "q[(b * 32 + i) / 2] = (uint8_t)(c0 | (c1 << 4));",
      "q[(b * 32 + i) / 2] = (uint8_t)(c1 | (c0 << 4));", "test_mx4_exact_blocks_round_trip"),
+    ("convert_all_ranks", "if (e / epr != r) continue; /* the expert lives on another rank */",
+     "(void)0; /* the expert lives on another rank */", "test_convert_combine_hand_worked_example"),
+    ("convert_unweighted",
+     "acc = fmaf(recv_w[row * k + j], oracle_bf16_to_f32(y_em[em_of_j[j] * H + h]), acc);",
+     "acc = fmaf(1.0f, oracle_bf16_to_f32(y_em[em_of_j[j] * H + h]), acc);",
+     "test_convert_combine_hand_worked_example"),
+    ("convert_unfused",
+     "acc = fmaf(recv_w[row * k + j], oracle_bf16_to_f32(y_em[em_of_j[j] * H + h]), acc);",
+     "acc = acc + recv_w[row * k + j] * oracle_bf16_to_f32(y_em[em_of_j[j] * H + h]);",
+     "test_convert_combine_input_is_fused_chain_per_rank"),
+    ("convert_reversed_order",
+     "for (int32_t j = 0; j < k; j++) {\n          if (em_of_j[j] < 0) continue;",
+     "for (int32_t j = k - 1; j >= 0; j--) {\n          if (em_of_j[j] < 0) continue;",
+     "test_convert_combine_input_is_fused_chain_per_rank"),
+    ("convert_repeated_expert_twice", "if (!first) continue; /* a repeated expert has one row */",
+     "(void)first; /* a repeated expert has one row */",
+     "test_convert_then_rank_sum_equals_expert_major_combine_on_exact_data"),
+    ("convert_rank_local_source", "if (em_src_pos[i] == pos) { em_of_j[j] = i; break; }",
+     "if (em_src_pos[i] == pos % cap) { em_of_j[j] = i; break; }",
+     "test_convert_combine_hand_worked_example"),
+    ("rank_sum_every_position", "if (first) row_of_j[j] = (int64_t)r * cap + s;",
+     "row_of_j[j] = (int64_t)r * cap + s;", "test_convert_combine_hand_worked_example"),
+    ("rank_sum_reversed_order",
+     "for (int32_t j = 0; j < k; j++) {\n        if (row_of_j[j] < 0) continue;",
+     "for (int32_t j = k - 1; j >= 0; j--) {\n        if (row_of_j[j] < 0) continue;",
+     "test_combine_rank_sum_adds_rank_rows_in_first_position_order"),
 ]
 
 

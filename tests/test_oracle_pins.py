@@ -736,3 +736,202 @@ def test_fp8_direct_cast_combine(oracle):
     assert np.all(np.abs(got - ref) <= bound)
     big = oracle.cast_fp8_direct(_bf16_of(np.array([1000.0, -1000.0, 448.0, 464.0])))
     assert list(big) == [0x7E, 0xFE, 0x7E, 0x7E]  # saturates at +-448
+
+
+# ----------------------------------------------------------------------------
+# expert-major expert outputs back to the combine input (convert_combine_input)
+# and the combine of converted rows ("MORI-EP User Guide" section 4)
+# ----------------------------------------------------------------------------
+
+def _read_golden_rows(name):
+    """Golden file with float values; keys that repeat collect a row each."""
+    d = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            d.setdefault(key, []).append([float(v) for v in vals])
+    return d
+
+
+def _em_of(oracle, idx, w, R, epr, cap, src=0, H=8, x=None):
+    """Plan, bf16 dispatch and expert-major layout of the given routing."""
+    T = idx.shape[0]
+    if x is None:
+        x = np.zeros((T, H), np.uint16)
+    pl = oracle.plan(idx, R, epr, cap, src)
+    d = oracle.dispatch(x, w, idx, pl, R, epr, cap, False)
+    cap_em = T * idx.shape[1] + 127 * R * epr
+    em = oracle.to_expert_major(d, pl, R, epr, cap, T, cap_em, src)
+    return pl, d, em
+
+
+def test_convert_combine_hand_worked_example(oracle):
+    g = _read_golden_rows("convert_combine_tiny.txt")
+    R, epr, k, cap, src = (int(g[n][0][0]) for n in ("R", "epr", "k", "cap", "src_rank"))
+    idx = np.array(g["indices"][0], np.int32).reshape(-1, k)
+    w = np.array(g["weights"][0], np.float32).reshape(-1, k)
+    T, H = idx.shape[0], 2
+    pl, d, em = _em_of(oracle, idx, w, R, epr, cap, src, H)
+    # the layout the hand-worked rows assume
+    assert list(em["em_counts"]) == [int(v) for v in g["em_counts"][0]]
+    assert list(em["em_offsets"]) == [int(v) for v in g["em_offsets"][0]]
+    for e in range(R * epr):
+        toks = [int(v) for v in g[f"em_tokens_e{e}"][0]]
+        o = em["em_offsets"][e]
+        assert list(em["em_src_pos"][o:o + len(toks)]) == [src * R * cap + t for t in toks]
+    # expert outputs at their rows; every other row is a NaN that would show
+    y_em = np.full(em["em_x"].shape, 0x7FC0, np.uint16)
+    for e, t, *v in g["y"]:
+        e, t = int(e), int(t)
+        toks = [int(u) for u in g[f"em_tokens_e{e}"][0]]
+        y_em[em["em_offsets"][e] + toks.index(t)] = torch_bf16(np.array(v, np.float32))
+    conv = oracle.convert_combine_input(y_em, em, d, pl, R, epr, cap, fill=0x7F80)
+    for r, s, *v in g["conv"]:
+        assert np.array_equal(conv[int(r), int(s)], torch_bf16(np.array(v, np.float32))), (r, s)
+    assert np.all(conv[:, T:] == 0x7F80)  # rows past the counts are not written
+    out = oracle.combine_rank_sum(conv, idx, pl, epr, cap)
+    for t, *v in g["out"]:
+        assert np.array_equal(out[int(t)], torch_bf16(np.array(v, np.float32))), t
+
+
+def test_convert_combine_input_is_fused_chain_per_rank(oracle):
+    # Each converted row is the chain of exact fp32 fmas, in top-k order, over
+    # the row's positions on its own rank, with the dispatched weights.  The
+    # reference reaches the expert-major rows through the token-side map
+    # (tok_em_row), not through the source info the oracle searches, and forms
+    # each step in float64 with one rounding to float32 (w*y is exact in
+    # float64 and the magnitudes are bounded, so that is exactly fmaf).
+    rng = np.random.default_rng(23)
+    T, H, R, epr, k, cap, src = 256, 512, 4, 4, 8, 256, 2
+    idx = np.stack([rng.permutation(R * epr)[:k] for _ in range(T)]).astype(np.int32)
+    w = rng.uniform(0.1, 1.0, size=(T, k)).astype(np.float32)
+    pl, d, em = _em_of(oracle, idx, w, R, epr, cap, src, H)
+    mag = rng.uniform(0.5, 2.0, size=(em["em_x"].shape[0], H))
+    y_em = torch_bf16((mag * rng.choice([-1.0, 1.0], size=mag.shape)).astype(np.float32))
+    conv = oracle.convert_combine_input(y_em, em, d, pl, R, epr, cap)
+    yv = bf16_f32(y_em)
+    ranks = idx // epr
+
+    def chain(order, fused=True):
+        ref = {}
+        for t in range(T):
+            for r in np.unique(ranks[t]):
+                acc = np.zeros(H, np.float32)
+                for j in order:
+                    if ranks[t, j] != r:
+                        continue
+                    p = np.float64(w[t, j]) * yv[em["tok_em_row"][t, j]].astype(np.float64)
+                    if fused:
+                        acc = (p + acc.astype(np.float64)).astype(np.float32)
+                    else:
+                        acc = (acc + p.astype(np.float32)).astype(np.float32)
+                ref[(int(r), int(pl["slot"][t, list(ranks[t]).index(r)]))] = torch_bf16(acc)
+        return ref
+
+    ref = chain(range(k))
+    assert len(ref) == int(pl["recv_counts"].sum())
+    for (r, s), v in ref.items():
+        assert np.array_equal(conv[r, s], v), (r, s)
+    # the data tells the top-k order and the fused chain from the alternatives
+    rev, unf = chain(range(k - 1, -1, -1)), chain(range(k), fused=False)
+    assert any(not np.array_equal(rev[key], v) for key, v in ref.items())
+    assert any(not np.array_equal(unf[key], v) for key, v in ref.items())
+
+
+def test_convert_undoes_the_expert_major_layout(oracle):
+    # Unit weights and every token's experts on distinct ranks: a received row
+    # holds one expert, so converting the expert-major copies of the received
+    # rows gives the received rows back bit for bit (fmaf(1, y, +0) = y).
+    rng = np.random.default_rng(29)
+    T, H, R, epr, k, cap = 300, 256, 8, 4, 4, 300
+    ranks = np.stack([rng.permutation(R)[:k] for _ in range(T)])
+    idx = (ranks * epr + rng.integers(0, epr, size=(T, k))).astype(np.int32)
+    x = torch_bf16(rng.standard_normal((T, H)).astype(np.float32))
+    w = np.ones((T, k), np.float32)
+    pl, d, em = _em_of(oracle, idx, w, R, epr, cap, 0, H, x)
+    conv = oracle.convert_combine_input(em["em_x"], em, d, pl, R, epr, cap, fill=0x5A5A)
+    for r in range(R):
+        n = int(pl["recv_counts"][r])
+        assert np.array_equal(conv[r, :n], d["recv_x"][r, :n])
+        assert np.all(conv[r, n:] == 0x5A5A)
+
+
+def test_convert_then_rank_sum_equals_expert_major_combine_on_exact_data(oracle):
+    # With dyadic values of few bits every fp32 step is exact, so converting and
+    # adding the rank rows must give exactly the expert-major combine (the top-k
+    # weighted sum over the experts each token names once).  Tokens naming one
+    # expert twice are included: the expert counts once on both sides.
+    rng = np.random.default_rng(31)
+    T, H, R, epr, k, cap = 200, 64, 4, 3, 6, 200
+    idx = np.stack([rng.permutation(R * epr)[:k] for _ in range(T)]).astype(np.int32)
+    idx[::7, 3] = idx[::7, 1]                      # repeated experts
+    w = rng.choice([0.125, 0.25, 0.375, 0.5, 0.75], size=(T, k)).astype(np.float32)
+    pl, d, em = _em_of(oracle, idx, w, R, epr, cap, 1, H)
+    assert pl["status"] == oracle.ST_DUP_EXPERT
+    vals = np.array([-3, -2, -1.5, -1, -0.5, 0, 0.5, 1, 1.5, 2, 3, 4], np.float32)
+    y_em = torch_bf16(rng.choice(vals, size=(em["em_x"].shape[0], H)))
+    conv = oracle.convert_combine_input(y_em, em, d, pl, R, epr, cap)
+    got = oracle.combine_rank_sum(conv, idx, pl, epr, cap)
+    ref = oracle.combine_em(y_em, w, em["tok_em_row"])
+    assert np.array_equal(got, ref)
+    # and it is the plain weighted sum, each named expert once
+    yv = bf16_f32(y_em).astype(np.float64)
+    for t in range(T):
+        s = np.zeros(H)
+        for j in range(k):
+            if idx[t, j] not in idx[t, :j]:
+                s += np.float64(w[t, j]) * yv[em["tok_em_row"][t, j]]
+        assert np.array_equal(bf16_f32(got[t]).astype(np.float64), s), t
+
+
+def test_convert_then_rank_sum_identity_round_trip(oracle):
+    # Identity experts: every output is x * (sum of the token's weights) up to
+    # the two roundings of the path (each within half a bf16 ulp of a term of
+    # one sign), so within 2 ulp of the float64 value.
+    wl = WORKLOADS["stdmoe"].with_tokens(256)
+    wl = dataclasses.replace(wl, quant="none", ranks=8, experts_per_rank=4, hidden=256)
+    inp = make_inputs(wl, 5)
+    idx, w = inp["indices"], inp["weights"]
+    pl, d, em = _em_of(oracle, idx, w, wl.ranks, wl.experts_per_rank, wl.cap, 0, wl.hidden,
+                       inp["x"])
+    conv = oracle.convert_combine_input(em["em_x"], em, d, pl, wl.ranks, wl.experts_per_rank,
+                                        wl.cap)
+    out = bf16_f32(oracle.combine_rank_sum(conv, idx, pl, wl.experts_per_rank, wl.cap))
+    want = bf16_f32(inp["x"]).astype(np.float64) * w.astype(np.float64).sum(1)[:, None]
+    ulp = np.exp2(np.floor(np.log2(np.abs(want) + 1e-300)) - 7)
+    assert np.all(np.abs(out - want) <= 2 * ulp)
+
+
+def test_combine_rank_sum_adds_rank_rows_in_first_position_order(oracle):
+    # Rows of widely different magnitudes, so that fp32 addition order shows:
+    # the reference adds each token's distinct rank rows with float32 numpy
+    # additions (one rounding each) in the order of their first top-k position.
+    rng = np.random.default_rng(37)
+    T, H, R, epr, k, cap = 128, 64, 8, 2, 6, 128
+    idx = np.stack([rng.permutation(R * epr)[:k] for _ in range(T)]).astype(np.int32)
+    pl = oracle.plan(idx, R, epr, cap)
+    big = rng.choice([2.0 ** 30, -2.0 ** 30, 1.0, -1.0, 2.0 ** 12], size=(R, cap, H))
+    y_rm = torch_bf16(big.astype(np.float32))
+    out = oracle.combine_rank_sum(y_rm, idx, pl, epr, cap)
+    yv = bf16_f32(y_rm)
+
+    def ref(order):
+        res = np.empty((T, H), np.uint16)
+        for t in range(T):
+            rs = []
+            for j in range(k):
+                r = int(idx[t, j]) // epr
+                if r not in [q for q, _ in rs]:
+                    rs.append((r, int(pl["slot"][t, j])))
+            acc = np.zeros(H, np.float32)
+            for i in order(len(rs)):
+                acc = acc + yv[rs[i][0], rs[i][1]]
+            res[t] = torch_bf16(acc)
+        return res
+
+    fwd = ref(lambda n: range(n))
+    assert np.array_equal(out, fwd)
+    assert np.count_nonzero(ref(lambda n: range(n - 1, -1, -1)) != fwd) > 0
