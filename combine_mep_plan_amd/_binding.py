@@ -33,6 +33,7 @@ MEP_QUANT_FP4_CARRY = 3
 MEP_QUANT_MXFP4 = 4
 MEP_RANK_MAJOR = 0
 MEP_EXPERT_MAJOR = 1
+MEP_RANK_SUM = 2
 
 
 class MepConfig(C.Structure):
@@ -80,6 +81,7 @@ def lib() -> C.CDLL:
             "mep_combine_fp8": ([p, i32, p, p, p, p], C.c_int),
             "mep_combine_fp8_direct": ([p, i32, p, p, p, p], C.c_int),
             "mep_cast_fp8_direct": ([p, i32, p, p, p], C.c_int),
+            "mep_convert_combine_input": ([p, p, p, p, p], C.c_int),
             "mep_reset": ([p, p], C.c_int),
             "mep_get_status": ([p, p, C.POINTER(i32)], C.c_int),
             "mep_get_route": ([p, p, p, p], C.c_int),
@@ -217,7 +219,9 @@ def _check_em_buffers(fn, st, cap_em, em_x, em_scales, em_counts, em_offsets, em
 
 
 def _layout_ready(st, layout) -> bool:
-    return st is not None and st.get("rm" if layout == MEP_RANK_MAJOR else "em", False)
+    if st is None or layout not in (MEP_RANK_MAJOR, MEP_EXPERT_MAJOR, MEP_RANK_SUM):
+        return False
+    return st.get("em" if layout == MEP_EXPERT_MAJOR else "rm", False)
 
 
 def _combine_rows(st, layout) -> int:
@@ -226,7 +230,7 @@ def _combine_rows(st, layout) -> int:
     c = st["cfg"]
     if not st.get("T"):
         return 0
-    if layout == MEP_RANK_MAJOR:
+    if layout in (MEP_RANK_MAJOR, MEP_RANK_SUM):
         return c.world_size * c.max_num_inp_token_per_rank
     return st.get("cap_em") or 0
 
@@ -235,7 +239,8 @@ def _check_combine_buffers(fn, st, layout, y, y_value_bytes, weights, out):
     c = st["cfg"]
     T = st.get("T") or 0
     _need(fn, "y", y, _combine_rows(st, layout) * c.hidden_dim * y_value_bytes)
-    _need(fn, "weights", weights, 4 * T * c.num_experts_per_token)
+    if layout != MEP_RANK_SUM:  # converted rows carry their weights
+        _need(fn, "weights", weights, 4 * T * c.num_experts_per_token)
     _need(fn, "out", out, 2 * T * c.hidden_dim)
 
 
@@ -378,6 +383,19 @@ def mep_cast_fp8_direct(h, layout, y, y8, stream=None) -> None:
         _need("mep_cast_fp8_direct", "y8", y8, rows * H)
     s = _stream(stream, y8)
     _check("mep_cast_fp8_direct", lib().mep_cast_fp8_direct(h, layout, _ptr(y), _ptr(y8), s))
+
+
+def mep_convert_combine_input(h, em_y, recv_weights, y, stream=None) -> None:
+    st = _state(h)
+    fn = "mep_convert_combine_input"
+    if st is not None and st["rm"] and st["em"] and st["T"]:
+        c = st["cfg"]
+        rows = c.world_size * c.max_num_inp_token_per_rank
+        _need(fn, "em_y", em_y, (st.get("cap_em") or 0) * c.hidden_dim * 2)
+        _need(fn, "recv_weights", recv_weights, 4 * rows * c.num_experts_per_token)
+        _need(fn, "y", y, rows * c.hidden_dim * 2)
+    s = _stream(stream, y)
+    _check(fn, lib().mep_convert_combine_input(h, _ptr(em_y), _ptr(recv_weights), _ptr(y), s))
 
 
 def mep_reset(h, stream=None) -> None:

@@ -16,6 +16,11 @@
 // are read exactly once -- and all of a slice's loads are issued before the
 // FMAs.  Wider top-k takes the positions in groups of 8 (see below).
 //
+// Converted rank rows ("MORI-EP User Guide", section 4 convert_combine_input():
+// each row already holds its rank's weighted expert outputs): the same kernel
+// adds a token's distinct rank rows with unit weights, in the order of their
+// first top-k position.
+//
 // FP8 direct-cast payload ("MORI-EP User Guide", section 10 Tuning: the
 // intra-node tuning matrix pairs quant type fp8_direct_cast with a bf16
 // combine; the cast rule -- OCP E4M3, no scale, round to nearest even,
@@ -62,19 +67,23 @@ __device__ __forceinline__ void round_e4m3_unit(u32x4& x) {
   }
 }
 
-template <int KMAX, bool DEDUPE, bool ROUND>
+// SUM: the rows are converted rank rows that already carry the weights; each
+// token's distinct rank rows (the positions owning them) are added with unit
+// weight -- fmaf(1, y, acc) is acc + y with one rounding.
+template <int KMAX, bool DEDUPE, bool ROUND, bool SUM = false>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int lane = threadIdx.x & 63;
   const int g = first_lane(blockIdx.x * 4 + (threadIdx.x >> 6));
   const int t = g / a.slices, sl = g - t * a.slices;
   if (t >= a.T) return;
   const int nv = a.H / 8;
+  const uint32_t own = SUM ? a.ufirst[t] : 0xFFFFFFFFu;
   int row[KMAX];
   float w[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
-    row[j] = j < a.k ? a.rows[(size_t)t * a.k + j] : -1;
-    w[j] = j < a.k ? a.w[(size_t)t * a.k + j] : 0.0f;
+    row[j] = j < a.k && ((own >> j) & 1u) ? a.rows[(size_t)t * a.k + j] : -1;
+    w[j] = SUM ? 1.0f : j < a.k ? a.w[(size_t)t * a.k + j] : 0.0f;
   }
   // src[j]: first top-k position holding the same row as j (uniform)
   int src[KMAX];
@@ -146,7 +155,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 // group is loaded again; the loads are ordinary cached ones so that such
 // repeats can hit the caches (at top-16 on 8 ranks: 100 us against 116 us
 // with non-temporal loads).
-template <bool DEDUPE, bool ROUND>
+template <bool DEDUPE, bool ROUND, bool SUM = false>
 __global__ __launch_bounds__(256) void combine_wide_kernel(CombineArgs a) {
   constexpr int G = 8;
   const int lane = threadIdx.x & 63;
@@ -154,6 +163,7 @@ __global__ __launch_bounds__(256) void combine_wide_kernel(CombineArgs a) {
   const int t = g / a.slices, sl = g - t * a.slices;
   if (t >= a.T) return;
   const int nv = a.H / 8;
+  const uint32_t own = SUM ? a.ufirst[t] : 0xFFFFFFFFu;
   const u32x4* y = reinterpret_cast<const u32x4*>(a.y);
   const int v0 = sl * (kWave * kUnitsPerLane) + lane;
   float acc[kUnitsPerLane][8];
@@ -167,8 +177,8 @@ __global__ __launch_bounds__(256) void combine_wide_kernel(CombineArgs a) {
 #pragma unroll
     for (int q = 0; q < G; ++q) {
       const int j = j0 + q;
-      row[q] = j < a.k ? a.rows[(size_t)t * a.k + j] : -1;
-      w[q] = j < a.k ? a.w[(size_t)t * a.k + j] : 0.0f;
+      row[q] = j < a.k && ((own >> j) & 1u) ? a.rows[(size_t)t * a.k + j] : -1;
+      w[q] = SUM ? 1.0f : j < a.k ? a.w[(size_t)t * a.k + j] : 0.0f;
     }
 #pragma unroll
     for (int q = 0; q < G; ++q) {
@@ -420,7 +430,10 @@ hipError_t launch_combine(const CombineArgs& a0, hipStream_t s) {
   a.slices = (a.H / 8 + per - 1) / per;
   const int blocks = (int)(((int64_t)a.T * a.slices + 3) / 4);
   const bool dedupe = !a.distinct_rows;
-  if (a.k > 8) {
+  if (a.sum_rows) {  // converted rank rows: the owning positions' rows are distinct
+    if (a.k > 8) combine_wide_kernel<false, false, true><<<blocks, 256, 0, s>>>(a);
+    else combine_kernel<8, false, false, true><<<blocks, 256, 0, s>>>(a);
+  } else if (a.k > 8) {
     if (a.round_e4m3) {
       if (dedupe) combine_wide_kernel<true, true><<<blocks, 256, 0, s>>>(a);
       else combine_wide_kernel<false, true><<<blocks, 256, 0, s>>>(a);

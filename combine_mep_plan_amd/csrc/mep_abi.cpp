@@ -15,6 +15,7 @@ struct mep_handle {
   bool plan_valid;
   bool em_valid;
   bool planned_since_reset;
+  bool captured;   // the last iteration's plan was recorded into a HIP graph
   uint32_t epoch;  // selects the status word; advanced by mep_reset
   int32_t plan_T;
 };
@@ -30,7 +31,7 @@ WsLayout ws_layout(const mep_config& c) {
   const size_t C = (cap + kChunk - 1) / kChunk;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
-  L.status = take(2 * sizeof(uint32_t));
+  L.status = take(4 * sizeof(uint32_t));
   L.chunk_cnt = take(C * R * sizeof(int32_t));
   L.block_cnt = take((C + 15) / 16 * R * sizeof(int32_t));
   L.mask = take(cap * sizeof(uint64_t));
@@ -91,10 +92,44 @@ static T* ws_ptr(mep_handle* h, size_t off) {
 
 static int hip_rc(hipError_t e) { return e == hipSuccess ? MEP_OK : MEP_ERR_HIP; }
 
-// The status word of a reset epoch.  A plan clears the word of the next epoch,
-// so that it is zero when mep_reset moves there.
-static uint32_t* status_word(mep_handle* h, uint32_t epoch) {
-  return ws_ptr<uint32_t>(h, h->lay.status) + (epoch & 1u);
+// Status words.  Outside graph capture, the word of the current reset epoch;
+// a plan clears the word of the next epoch, so that it is zero when mep_reset
+// moves there, and reset launches nothing.  A replayed graph keeps the
+// pointers it was captured with while mep_reset moves the host epoch, so an
+// iteration whose plan is captured uses a word of its own (index 2), cleared
+// by a one-thread kernel captured in front of the plan: every replay starts
+// clean and reports its own bits, whatever resets run between replays.  Its
+// plan's clear of a next word goes to a word nobody reads (index 3).
+static uint32_t* status_base(mep_handle* h) { return ws_ptr<uint32_t>(h, h->lay.status); }
+
+static uint32_t* status_word(mep_handle* h) {
+  return status_base(h) + (h->captured ? 2u : (h->epoch & 1u));
+}
+
+static uint32_t* status_next_word(mep_handle* h) {
+  return status_base(h) + (h->captured ? 3u : ((h->epoch + 1u) & 1u));
+}
+
+// Start of an iteration (a plan, fused plan+dispatch or standard-MoE
+// dispatch): choose the status words by whether the stream is being captured.
+// Captured: clear the graph's word first (a kernel node, not a memset node).
+// Back from a captured iteration: the current epoch's word may hold bits from
+// before the capture, so it is cleared the same way once.
+static int begin_iteration(mep_handle* h, hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return MEP_ERR_HIP;
+  const bool capturing = cs == hipStreamCaptureStatusActive;
+  const bool was = h->captured;
+  h->captured = capturing;
+  if (capturing || was) return hip_rc(mep::launch_clear_word(status_word(h), stream));
+  return MEP_OK;
+}
+
+// Expert-major segment offsets are int32 sums of per-expert counts padded to
+// 128 rows; T*k rows and 127 padding rows per expert must fit.
+static bool em_offsets_fit(const mep_config& c, int32_t T) {
+  return (int64_t)T * c.num_experts_per_token +
+             127 * (int64_t)c.world_size * c.num_experts_per_rank <= INT32_MAX;
 }
 
 extern "C" {
@@ -156,8 +191,8 @@ static mep::PlanArgs plan_args(mep_handle* h, const int32_t* indices, int32_t T,
   a.indices = indices;
   a.recv_counts = recv_counts;
   a.spos = src_token_pos;
-  a.status = status_word(h, h->epoch);
-  a.status_next = status_word(h, h->epoch + 1);
+  a.status = status_word(h);
+  a.status_next = status_next_word(h);
   a.chunk_cnt = ws_ptr<int32_t>(h, h->lay.chunk_cnt);
   a.block_cnt = ws_ptr<int32_t>(h, h->lay.block_cnt);
   a.mask = ws_ptr<uint64_t>(h, h->lay.mask);
@@ -228,8 +263,8 @@ static mep::DispatchArgs dispatch_args(mep_handle* h, int32_t T, const void* x,
   a.mask = ws_ptr<uint64_t>(h, h->lay.mask);
   a.chunk_cnt = ws_ptr<int32_t>(h, h->lay.chunk_cnt);
   a.block_cnt = ws_ptr<int32_t>(h, h->lay.block_cnt);
-  a.status = status_word(h, h->epoch);
-  a.status_next = status_word(h, h->epoch + 1);
+  a.status = status_word(h);
+  a.status_next = status_next_word(h);
   a.T = T;
   a.H = c.hidden_dim;
   a.k = c.num_experts_per_token;
@@ -245,9 +280,11 @@ int mep_plan(mep_handle* h, const int32_t* indices, int32_t T, int32_t* recv_cou
              int32_t* src_token_pos, void* stream) {
   int rc = check_plan_args(h, indices, T, recv_counts, src_token_pos);
   if (rc != MEP_OK) return rc;
-  const mep::PlanArgs a = plan_args(h, indices, T, recv_counts, src_token_pos);
   h->plan_valid = false;
   h->em_valid = false;
+  rc = begin_iteration(h, (hipStream_t)stream);
+  if (rc != MEP_OK) return rc;
+  const mep::PlanArgs a = plan_args(h, indices, T, recv_counts, src_token_pos);
   rc = hip_rc(mep::launch_plan(a, (hipStream_t)stream));
   if (rc != MEP_OK) return rc;
   h->plan_valid = true;
@@ -279,13 +316,15 @@ int mep_plan_dispatch(mep_handle* h, const int32_t* indices, int32_t T, int32_t*
   rc = check_dispatch_args(h, T, x, weights, scales, indices, recv_x, recv_scales, recv_weights,
                            recv_indices);
   if (rc != MEP_OK) return rc;
+  h->plan_valid = false;
+  h->em_valid = false;
+  rc = begin_iteration(h, (hipStream_t)stream);
+  if (rc != MEP_OK) return rc;
   const mep::PlanArgs p = plan_args(h, indices, T, recv_counts, src_token_pos);
   mep::DispatchArgs a = dispatch_args(h, T, x, weights, scales, indices, recv_x, recv_scales,
                                       recv_weights, recv_indices);
   a.recv_counts = recv_counts;
   a.spos = src_token_pos;
-  h->plan_valid = false;
-  h->em_valid = false;
   rc = hip_rc(mep::launch_plan_dispatch(p, a, (hipStream_t)stream));
   if (rc != MEP_OK) return rc;
   h->plan_valid = true;
@@ -308,6 +347,7 @@ int mep_to_expert_major(mep_handle* h, const void* recv_x, const float* recv_sca
     return MEP_ERR_NULL;
   if (nb > 0 && (!recv_scales || !em_scales)) return MEP_ERR_NULL;
   if (cap_em < 0 || cap_em > INT32_MAX) return MEP_ERR_SHAPE;
+  if (!em_offsets_fit(c, h->plan_T)) return MEP_ERR_SHAPE;
   if (!aligned16(recv_x) || !aligned16(recv_indices) || !aligned16(recv_counts) ||
       !aligned16(src_token_pos) || !aligned16(em_x) || !aligned16(em_counts) ||
       !aligned16(em_offsets) || !aligned16(em_src_pos) ||
@@ -328,7 +368,7 @@ int mep_to_expert_major(mep_handle* h, const void* recv_x, const float* recv_sca
   a.em_row = ws_ptr<int32_t>(h, h->lay.em_row);
   a.lmask = ws_ptr<uint64_t>(h, h->lay.em_lmask);
   a.ccnt = ws_ptr<int32_t>(h, h->lay.em_ccnt);
-  a.status = status_word(h, h->epoch);
+  a.status = status_word(h);
   a.cap_em = cap_em;
   a.T = h->plan_T;
   a.H = c.hidden_dim;
@@ -356,7 +396,7 @@ int mep_dispatch_standard_moe(mep_handle* h, const int32_t* indices, int32_t T, 
   const int nb = scale_cols(c);
   const bool carry = mep::is_carry(c.quant);
   if (T < 0 || T > c.max_num_inp_token_per_rank) return MEP_ERR_SHAPE;
-  if (cap_em < 0 || cap_em > INT32_MAX) return MEP_ERR_SHAPE;
+  if (cap_em < 0 || cap_em > INT32_MAX || !em_offsets_fit(c, T)) return MEP_ERR_SHAPE;
   if (!em_x || !em_counts || !em_offsets || !em_src_pos) return MEP_ERR_NULL;
   if (nb > 0 && !em_scales) return MEP_ERR_NULL;
   if (T > 0 && (!indices || !x)) return MEP_ERR_NULL;
@@ -366,6 +406,10 @@ int mep_dispatch_standard_moe(mep_handle* h, const int32_t* indices, int32_t T, 
       (em_scales && !aligned16(em_scales)) || !aligned16(em_counts) ||
       !aligned16(em_offsets) || !aligned16(em_src_pos))
     return MEP_ERR_ALIGN;
+  h->plan_valid = false;  // no rank-major plan: only the expert-major combine follows
+  h->em_valid = false;
+  int rc = begin_iteration(h, (hipStream_t)stream);
+  if (rc != MEP_OK) return rc;
   mep::SmArgs a{};
   a.x = x;
   a.x_scales = carry ? scales : nullptr;
@@ -377,8 +421,8 @@ int mep_dispatch_standard_moe(mep_handle* h, const int32_t* indices, int32_t T, 
   a.em_src_pos = em_src_pos;
   a.em_row = ws_ptr<int32_t>(h, h->lay.em_row);
   a.chunk_hist = ws_ptr<int32_t>(h, h->lay.sm_hist);
-  a.status = status_word(h, h->epoch);
-  a.status_next = status_word(h, h->epoch + 1);
+  a.status = status_word(h);
+  a.status_next = status_next_word(h);
   a.cap_em = cap_em;
   a.T = T;
   a.H = c.hidden_dim;
@@ -387,9 +431,7 @@ int mep_dispatch_standard_moe(mep_handle* h, const int32_t* indices, int32_t T, 
   a.quant = c.quant;
   a.scale_dim = nb;
   a.spos_base = c.rank * c.world_size * c.max_num_inp_token_per_rank;
-  h->plan_valid = false;  // no rank-major plan: only the expert-major combine follows
-  h->em_valid = false;
-  int rc = hip_rc(mep::launch_dispatch_standard_moe(a, (hipStream_t)stream));
+  rc = hip_rc(mep::launch_dispatch_standard_moe(a, (hipStream_t)stream));
   if (rc != MEP_OK) return rc;
   h->em_valid = true;
   h->planned_since_reset = true;
@@ -398,9 +440,11 @@ int mep_dispatch_standard_moe(mep_handle* h, const int32_t* indices, int32_t T, 
 }
 
 // Layout and call-order checks shared by the combine-side entry points.
-static int check_combine_layout(mep_handle* h, int32_t layout) {
-  if (layout != MEP_RANK_MAJOR && layout != MEP_EXPERT_MAJOR) return MEP_ERR_SHAPE;
-  if (layout == MEP_RANK_MAJOR && !h->plan_valid) return MEP_ERR_STATE;
+static int check_combine_layout(mep_handle* h, int32_t layout, bool sum_ok) {
+  const bool sum = layout == MEP_RANK_SUM;
+  if (layout != MEP_RANK_MAJOR && layout != MEP_EXPERT_MAJOR && !(sum && sum_ok))
+    return MEP_ERR_SHAPE;
+  if ((layout == MEP_RANK_MAJOR || sum) && !h->plan_valid) return MEP_ERR_STATE;
   if (layout == MEP_EXPERT_MAJOR && !h->em_valid) return MEP_ERR_STATE;
   return MEP_OK;
 }
@@ -410,19 +454,22 @@ static int combine_common(mep_handle* h, int32_t layout, const void* y, const fl
                           void* out, void* stream, int kind) {
   const bool fp8 = kind == 1;
   if (!h) return MEP_ERR_NULL;
-  int rc = check_combine_layout(h, layout);
+  int rc = check_combine_layout(h, layout, kind == 0);
   if (rc != MEP_OK) return rc;
+  const bool sum = layout == MEP_RANK_SUM;
   if (fp8 && h->cfg.hidden_dim % 16 != 0) return MEP_ERR_SHAPE;
   const int32_t T = h->plan_T;
   if (!out) return MEP_ERR_NULL;
-  if (T > 0 && (!y || !weights)) return MEP_ERR_NULL;
+  if (T > 0 && (!y || (!weights && !sum))) return MEP_ERR_NULL;
   if ((y && !aligned16(y)) || (weights && !aligned16(weights)) || !aligned16(out))
     return MEP_ERR_ALIGN;
   mep::CombineArgs a{};
   a.y = y;
-  a.w = weights;
-  a.rows = ws_ptr<int32_t>(h, layout == MEP_RANK_MAJOR ? h->lay.rrow : h->lay.em_row);
+  a.w = sum ? nullptr : weights;
+  a.rows = ws_ptr<int32_t>(h, layout == MEP_EXPERT_MAJOR ? h->lay.em_row : h->lay.rrow);
+  a.ufirst = ws_ptr<uint32_t>(h, h->lay.ufirst);
   a.distinct_rows = layout == MEP_EXPERT_MAJOR ? 1 : 0;
+  a.sum_rows = sum ? 1 : 0;
   a.out = out;
   a.T = T;
   a.H = h->cfg.hidden_dim;
@@ -449,7 +496,7 @@ int mep_combine_fp8_direct(mep_handle* h, int32_t layout, const void* y, const f
 
 int mep_cast_fp8_direct(mep_handle* h, int32_t layout, const void* y, void* y8, void* stream) {
   if (!h) return MEP_ERR_NULL;
-  int rc = check_combine_layout(h, layout);
+  int rc = check_combine_layout(h, layout, false);
   if (rc != MEP_OK) return rc;
   if (h->cfg.hidden_dim % 16 != 0) return MEP_ERR_SHAPE;
   const int32_t T = h->plan_T;
@@ -467,6 +514,28 @@ int mep_cast_fp8_direct(mep_handle* h, int32_t layout, const void* y, void* y8, 
   return hip_rc(mep::launch_cast_fp8(a, (hipStream_t)stream));
 }
 
+int mep_convert_combine_input(mep_handle* h, const void* em_y, const float* recv_weights,
+                              void* y, void* stream) {
+  if (!h) return MEP_ERR_NULL;
+  if (!h->plan_valid || !h->em_valid) return MEP_ERR_STATE;
+  const int32_t T = h->plan_T;
+  if (T > 0 && (!em_y || !recv_weights || !y)) return MEP_ERR_NULL;
+  if ((em_y && !aligned16(em_y)) || (recv_weights && !aligned16(recv_weights)) ||
+      (y && !aligned16(y)))
+    return MEP_ERR_ALIGN;
+  mep::ConvertArgs a{};
+  a.y_em = em_y;
+  a.recv_w = recv_weights;
+  a.rrow = ws_ptr<int32_t>(h, h->lay.rrow);
+  a.em_row = ws_ptr<int32_t>(h, h->lay.em_row);
+  a.ufirst = ws_ptr<uint32_t>(h, h->lay.ufirst);
+  a.y = y;
+  a.T = T;
+  a.H = h->cfg.hidden_dim;
+  a.k = h->cfg.num_experts_per_token;
+  return hip_rc(mep::launch_convert_combine_input(a, (hipStream_t)stream));
+}
+
 int mep_reset(mep_handle* h, void* stream) {
   if (!h) return MEP_ERR_NULL;
   (void)stream;  // nothing to launch: the last plan cleared the next status word
@@ -480,7 +549,7 @@ int mep_reset(mep_handle* h, void* stream) {
 int mep_get_status(mep_handle* h, void* stream, int32_t* device_status) {
   if (!h || !device_status) return MEP_ERR_NULL;
   uint32_t v = 0;
-  hipError_t e = hipMemcpyAsync(&v, status_word(h, h->epoch), sizeof(v),
+  hipError_t e = hipMemcpyAsync(&v, status_word(h), sizeof(v),
                                 hipMemcpyDeviceToHost, (hipStream_t)stream);
   if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
   if (e != hipSuccess) return MEP_ERR_HIP;

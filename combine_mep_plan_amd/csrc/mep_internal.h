@@ -39,7 +39,8 @@ struct RankDiv {
 
 // Byte offsets of the workspace sections (each 256-byte aligned).
 struct WsLayout {
-  size_t status;     // uint32 [2]: sticky MEP_DEV_* bits, one word per reset epoch
+  size_t status;     // uint32 [4]: sticky MEP_DEV_* bits, one word per reset epoch [0, 1];
+                     // the word of captured iterations [2]; a word no one reads [3]
   size_t chunk_cnt;  // int32 [C][R]: rows earlier chunks of the same 16-chunk block send to each rank
   size_t block_cnt;  // int32 [ceil(C/16)][R]: rows each 16-chunk block sends to each rank
   size_t mask;       // uint64 [cap]: destination-rank mask of each token (0 = dropped)
@@ -99,11 +100,13 @@ constexpr int kInlinePlanTokens = 256;
 
 struct CombineArgs {
   const void* y;           // bf16 rows
-  const float* w;          // [T,k]
+  const float* w;          // [T,k]; unused when sum_rows
   const int32_t* rows;     // [T,k] row of (t, j) in y, -1 = skip
+  const uint32_t* ufirst;  // [T] positions owning a rank row (sum_rows only)
   void* out;               // [T,H] bf16
   int32_t T, H, k;
   int32_t distinct_rows;   // 1: the k rows of a token are distinct (no dedupe needed)
+  int32_t sum_rows;        // 1: add the token's distinct rank rows, no weights
   int32_t round_e4m3;      // 1: each value rounded through E4M3 (direct cast) before use
   int32_t slices, slice_units;  // waves per token and 16-byte lane units per wave
 };
@@ -113,6 +116,16 @@ struct CastArgs {           // E4M3 direct cast of the routed expert-output rows
   void* y8;                  // E4M3 rows, same row indices
   const int32_t* rows;       // [T,k] row of (t, j), -1 = none
   const uint32_t* ufirst;    // [T] positions owning a distinct row (rank-major), or null
+  int32_t T, H, k, slices;
+};
+
+struct ConvertArgs {         // expert-major expert outputs back to rank-major rows
+  const void* y_em;          // [cap_em,H] bf16
+  const float* recv_w;       // [R*cap,k] dispatched weights
+  const int32_t* rrow;       // [T,k] receive row of (t, j)
+  const int32_t* em_row;     // [T,k] expert-major row of (t, j), -1 = none
+  const uint32_t* ufirst;    // [T] positions owning a rank row
+  void* y;                   // [R*cap,H] bf16
   int32_t T, H, k, slices;
 };
 
@@ -164,6 +177,8 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_combine_fp8(const CombineArgs& a, hipStream_t s);  // y holds E4M3 rows
 hipError_t launch_cast_fp8(const CastArgs& a, hipStream_t s);
 hipError_t launch_to_expert_major(const EmArgs& a, hipStream_t s);
+hipError_t launch_convert_combine_input(const ConvertArgs& a, hipStream_t s);
+hipError_t launch_clear_word(uint32_t* word, hipStream_t s);  // one-thread kernel: *word = 0
 hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int64_t n, hipStream_t s);
 hipError_t launch_probe_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t s);
 hipError_t launch_probe_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);

@@ -1,5 +1,6 @@
-// Small launches: a device copy for route inspection, and probes that run the
-// kernels' own device conversions over caller arrays.
+// Small launches: a device copy for route inspection, the status-word clear of
+// captured iterations, and probes that run the kernels' own device conversions
+// over caller arrays.
 #include "dev.h"
 #include "mep_internal.h"
 
@@ -12,6 +13,8 @@ __global__ void copy_i32_kernel(const int32_t* src, int32_t* dst, int64_t n) {
        i += (int64_t)gridDim.x * blockDim.x)
     dst[i] = src[i];
 }
+
+__global__ void clear_word_kernel(uint32_t* word) { *word = 0u; }
 
 __global__ void probe_e4m3_kernel(const float* in, uint8_t* out, int64_t n) {
   const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
@@ -40,6 +43,11 @@ hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int64_t n, hipStrea
   if (n == 0) return hipSuccess;
   const int blocks = (int)std::min<int64_t>((n + 255) / 256, 1024);
   copy_i32_kernel<<<blocks, 256, 0, s>>>(src, dst, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_clear_word(uint32_t* word, hipStream_t s) {
+  clear_word_kernel<<<1, 1, 0, s>>>(word);
   return hipGetLastError();
 }
 

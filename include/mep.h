@@ -26,8 +26,13 @@
  *   - Layouts are row-major and dense: [T,H] means row t at offset t*H.
  *   - Apart from mep_get_status, the calls launch kernels only (no memset,
  *     copy or host wait), so a sequence of them can be captured into a HIP
- *     graph; a replay reuses the handle state of the capture (its plan and its
- *     status word).
+ *     graph; a replay reuses the handle state of the capture (its plan).  An
+ *     iteration whose plan (mep_plan, mep_plan_dispatch or
+ *     mep_dispatch_standard_moe) is captured reports its MEP_DEV_* bits in a
+ *     status word of its own, cleared by a one-thread kernel captured in front
+ *     of the plan: each replay starts clean, mep_get_status returns the bits
+ *     of the latest replay (mep_reset between replays is allowed and changes
+ *     nothing there), until a plan is issued outside capture again.
  */
 #ifndef MEP_H
 #define MEP_H
@@ -85,6 +90,9 @@ extern "C" {
                                          this library's reading)                */
 #define MEP_RANK_MAJOR 0              /* combine input: [R, cap, H] bf16         */
 #define MEP_EXPERT_MAJOR 1            /* combine input: [cap_em, H] bf16         */
+#define MEP_RANK_SUM 2                /* combine input: [R, cap, H] bf16 rows from
+                                         mep_convert_combine_input, which already
+                                         carry the weights                       */
 
 /*
  * Configuration.  Fields follow EpDispatchCombineConfig ("MORI-EP User Guide",
@@ -197,7 +205,9 @@ int mep_plan_dispatch(mep_handle *h, const int32_t *indices, int32_t T, int32_t 
  *   em_src_pos[...]     its src_token_pos.
  * Padding rows are not written.  cap_em is the row capacity of em_x /
  * em_scales / em_src_pos; T*k + 127*E always suffices.  Rows past cap_em are
- * dropped and set MEP_DEV_EM_OVERFLOW.  Needs a valid plan.
+ * dropped and set MEP_DEV_EM_OVERFLOW.  Needs a valid plan.  MEP_ERR_SHAPE if
+ * T*k + 127*E exceeds INT32_MAX (the int32 offsets could not hold the
+ * padded segments).
  */
 int mep_to_expert_major(mep_handle *h, const void *recv_x, const float *recv_scales,
                         const int32_t *recv_indices, const int32_t *recv_counts,
@@ -216,7 +226,8 @@ int mep_to_expert_major(mep_handle *h, const void *recv_x, const float *recv_sca
  * first position naming it).  Leaves the handle ready for
  * mep_combine(MEP_EXPERT_MAJOR) and mep_get_route(NULL, em_row); the
  * rank-major calls need a new mep_plan.  scales as for mep_dispatch.
- * 0 <= T <= cap; cap_em as for mep_to_expert_major.
+ * 0 <= T <= cap; cap_em (and the T*k + 127*E bound) as for
+ * mep_to_expert_major.
  */
 int mep_dispatch_standard_moe(mep_handle *h, const int32_t *indices, int32_t T, const void *x,
                               const float *scales, void *em_x, float *em_scales,
@@ -239,6 +250,12 @@ int mep_dispatch_standard_moe(mep_handle *h, const int32_t *indices, int32_t T, 
  *                     after the current plan).
  * weights are token-major fp32 [T,k]; out is [T,H] bf16.  Tokens that were
  * not dispatched (bad expert id) produce +0.
+ *   MEP_RANK_SUM:     y is [R,cap,H] rows written by mep_convert_combine_input
+ *                     (each already weighted); out[t, h] = bf16_rne(acc),
+ *                     acc = +0, then acc = acc + y_r[h] over t's distinct
+ *                     destination ranks r in the order of their first top-k
+ *                     position (one fp32 rounding per addition); weights is
+ *                     not read and may be NULL.  Needs a valid plan.
  */
 int mep_combine(mep_handle *h, int32_t layout, const void *y, const float *weights, void *out,
                 void *stream);
@@ -268,6 +285,28 @@ int mep_combine_fp8(mep_handle *h, int32_t layout, const void *y8, const float *
  */
 int mep_combine_fp8_direct(mep_handle *h, int32_t layout, const void *y, const float *weights,
                            void *out, void *stream);
+
+/*
+ * Standard-MoE expert outputs back to the combine input ("MORI-EP User
+ * Guide" section 4, convert_combine_input(packed rows, source info, layout
+ * range): the experts' expert-major outputs turned into the rows combine()
+ * takes).  em_y is [cap_em,H] bf16 in the layout of the last
+ * mep_to_expert_major (whose source info and segments this handle keeps);
+ * recv_weights is the dispatch's [R,cap,k] fp32 output.  For every received
+ * row (rank r, slot s < recv_counts[r]) of token t:
+ *   y[r, s, h] = bf16_rne(acc), acc = +0, then for j = 0..k-1 in order, over
+ *   t's positions whose expert lives on rank r and is not named by an earlier
+ *   position: acc = fmaf(recv_weights[r, s, j], em_y[row of (t, j)][h], acc).
+ * The pages pass no weights to this step; applying the dispatched weights
+ * here is this library's reading -- a row merging several local experts can
+ * carry their weighted sum only if the weights go in before the merge -- so
+ * the combine that follows is mep_combine(MEP_RANK_SUM), which adds rank rows
+ * without weights.  y is [R,cap,H] bf16; rows past recv_counts[r] are not
+ * written; a position whose expert-major row was dropped (MEP_DEV_EM_OVERFLOW)
+ * adds nothing.  Needs a valid plan and mep_to_expert_major after it.
+ */
+int mep_convert_combine_input(mep_handle *h, const void *em_y, const float *recv_weights,
+                              void *y, void *stream);
 
 /*
  * Reset between iterations ("MORI-EP User Guide" section 3 reset()):

@@ -100,6 +100,13 @@ def test_call_order_and_argument_checks_before_any_launch():
     assert L.mep_combine(h, M.MEP_RANK_MAJOR, f, f, f, None) == M.MEP_ERR_STATE
     assert L.mep_combine(h, 5, f, f, f, None) == M.MEP_ERR_SHAPE
     assert L.mep_get_route(h, f, None, None) == M.MEP_ERR_STATE
+    # converted rows: the conversion needs a plan and an expert-major layout,
+    # their combine a plan; only the bf16 combine takes them
+    assert L.mep_convert_combine_input(h, f, f, f, None) == M.MEP_ERR_STATE
+    assert L.mep_combine(h, M.MEP_RANK_SUM, f, None, f, None) == M.MEP_ERR_STATE
+    assert L.mep_combine_fp8(h, M.MEP_RANK_SUM, f, f, f, None) == M.MEP_ERR_SHAPE
+    assert L.mep_combine_fp8_direct(h, M.MEP_RANK_SUM, f, f, f, None) == M.MEP_ERR_SHAPE
+    assert L.mep_cast_fp8_direct(h, M.MEP_RANK_SUM, f, f, None) == M.MEP_ERR_SHAPE
     # plan argument checks
     assert L.mep_plan(h, f, 4097, f, f, None) == M.MEP_ERR_SHAPE
     assert L.mep_plan(h, f, -1, f, f, None) == M.MEP_ERR_SHAPE
@@ -151,6 +158,25 @@ def test_standard_moe_and_carry_argument_checks():
     assert L.mep_dispatch(h, f, f, None, f, f, f, f, f, None) == M.MEP_ERR_STATE
     assert L.mep_plan_dispatch(h, f, 16, f, f, f, f, None, f, f, f, f, None) == M.MEP_ERR_NULL
     assert L.mep_plan_dispatch(h, f, 16, f, f, f, f, f + 4, f, f, f, f, None) == M.MEP_ERR_ALIGN
+    assert L.mep_destroy(h) == M.MEP_OK
+
+
+def test_expert_major_offsets_must_fit_int32():
+    # segment offsets are int32 sums of counts padded to 128 rows: a batch whose
+    # T*k + 127*E could pass INT32_MAX is refused before any launch
+    L = M.lib()
+    f = FAKE
+    c = cfg(world_size=1, num_experts_per_rank=64, num_experts_per_token=32,
+            max_num_inp_token_per_rank=1 << 27, hidden_dim=256)
+    n = M.mep_workspace_bytes(c)
+    assert n > 0
+    h = C.c_void_p()
+    assert L.mep_create(C.byref(c), f, n, C.byref(h)) == M.MEP_OK
+    h = h.value
+    T = (2**31 - 1 - 127 * 64) // 32 + 1      # the smallest batch that does not fit
+    sm = L.mep_dispatch_standard_moe
+    assert sm(h, f, T, f, None, f, None, f, f, f, 1 << 30, None) == M.MEP_ERR_SHAPE
+    assert sm(h, f, 1 << 26, f, None, f, None, f, f, f, 1 << 30, None) == M.MEP_ERR_SHAPE
     assert L.mep_destroy(h) == M.MEP_OK
 
 
