@@ -87,6 +87,7 @@ def lib() -> C.CDLL:
             "mep_get_route": ([p, p, p, p], C.c_int),
             "mep_probe_e4m3": ([p, p, i64, p], C.c_int),
             "mep_probe_bf16": ([p, p, i64, p], C.c_int),
+            "mep_probe_stream": ([p, p, i64, i64, i64, p], C.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -431,6 +432,14 @@ def mep_probe_e4m3(inp, out, n, stream=None) -> None:
 
 def mep_probe_bf16(inp, out, n, stream=None) -> None:
     _check("mep_probe_bf16", lib().mep_probe_bf16(_ptr(inp), _ptr(out), n, _stream(stream, out)))
+
+
+def mep_probe_stream(src, dst, waves, rd_units, wr_units, stream=None) -> None:
+    fn = "mep_probe_stream"
+    _need(fn, "src", src, rd_units * 1024)
+    _need(fn, "dst", dst, max(wr_units * 1024, 16))
+    _check(fn, lib().mep_probe_stream(_ptr(src), _ptr(dst), waves, rd_units, wr_units,
+                                      _stream(stream, dst)))
 
 
 class Mep:

@@ -184,7 +184,13 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
     uint32_t st = 0;
     w = wave_route<MODE, KMAX>(a, t, lane, st);
     if (sl == 0) {
-      if (MODE == kInline) or_status(a.status, lane == w.tl ? st : 0u);
+      if (MODE == kInline) {
+        if (a.tok_status) {
+          if (lane == w.tl) a.tok_status[t] = (uint8_t)st;
+        } else {
+          or_status(a.status, lane == w.tl ? st : 0u);
+        }
+      }
       write_route(a, w, t, lane, meta.id);
     }
     if (w.tok_mask == 0) return;

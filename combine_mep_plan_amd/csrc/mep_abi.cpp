@@ -4,6 +4,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "mep_internal.h"
 
 struct mep_handle {
@@ -16,6 +18,8 @@ struct mep_handle {
   bool em_valid;
   bool planned_since_reset;
   bool captured;   // the last iteration's plan was recorded into a HIP graph
+  bool eager_planned;     // a plan has run outside capture
+  uint32_t eager_epoch;   // the epoch of the last plan outside capture
   uint32_t epoch;  // selects the status word; advanced by mep_reset
   int32_t plan_T;
 };
@@ -31,7 +35,8 @@ WsLayout ws_layout(const mep_config& c) {
   const size_t C = (cap + kChunk - 1) / kChunk;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
-  L.status = take(4 * sizeof(uint32_t));
+  L.status = take(3 * sizeof(uint32_t));
+  L.tok_status = take(cap);
   L.chunk_cnt = take(C * R * sizeof(int32_t));
   L.block_cnt = take((C + 15) / 16 * R * sizeof(int32_t));
   L.mask = take(cap * sizeof(uint64_t));
@@ -92,14 +97,17 @@ static T* ws_ptr(mep_handle* h, size_t off) {
 
 static int hip_rc(hipError_t e) { return e == hipSuccess ? MEP_OK : MEP_ERR_HIP; }
 
-// Status words.  Outside graph capture, the word of the current reset epoch;
-// a plan clears the word of the next epoch, so that it is zero when mep_reset
-// moves there, and reset launches nothing.  A replayed graph keeps the
-// pointers it was captured with while mep_reset moves the host epoch, so an
-// iteration whose plan is captured uses a word of its own (index 2), cleared
-// by a one-thread kernel captured in front of the plan: every replay starts
-// clean and reports its own bits, whatever resets run between replays.  Its
-// plan's clear of a next word goes to a word nobody reads (index 3).
+// Status words.  Outside graph capture: the word of the current reset epoch,
+// ORed into by the kernels; a plan clears the word of the next epoch, so that
+// it is zero when mep_reset moves there, and reset launches nothing.
+//
+// A replayed graph keeps the pointers it was captured with while mep_reset
+// moves only the host epoch, so an iteration whose plan is captured reports
+// differently, with nothing to clear beforehand: its plan kernels store each
+// token's bad/repeated-id bits in the token's own byte (every replay rewrites
+// all of them), and the expert-major overflow bit goes to word 2, which the
+// plan's first launch clears (as it clears a next-epoch word) and only later
+// launches set.  mep_get_status then ORs word 2 with the planned tokens' bytes.
 static uint32_t* status_base(mep_handle* h) { return ws_ptr<uint32_t>(h, h->lay.status); }
 
 static uint32_t* status_word(mep_handle* h) {
@@ -107,21 +115,28 @@ static uint32_t* status_word(mep_handle* h) {
 }
 
 static uint32_t* status_next_word(mep_handle* h) {
-  return status_base(h) + (h->captured ? 3u : ((h->epoch + 1u) & 1u));
+  return status_base(h) + (h->captured ? 2u : ((h->epoch + 1u) & 1u));
+}
+
+static uint8_t* tok_status(mep_handle* h) {
+  return h->captured ? ws_ptr<uint8_t>(h, h->lay.tok_status) : nullptr;
 }
 
 // Start of an iteration (a plan, fused plan+dispatch or standard-MoE
-// dispatch): choose the status words by whether the stream is being captured.
-// Captured: clear the graph's word first (a kernel node, not a memset node).
-// Back from a captured iteration: the current epoch's word may hold bits from
-// before the capture, so it is cleared the same way once.
+// dispatch): note whether the stream is being captured.  Back outside capture,
+// the iteration starts in the epoch after the last plan outside capture, whose
+// word that plan cleared (no plan outside capture yet: both words still hold
+// the zeros of the fresh workspace); nothing is launched.
 static int begin_iteration(mep_handle* h, hipStream_t stream) {
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return MEP_ERR_HIP;
   const bool capturing = cs == hipStreamCaptureStatusActive;
-  const bool was = h->captured;
+  if (!capturing) {
+    if (h->captured && h->eager_planned) h->epoch = h->eager_epoch + 1u;
+    h->eager_planned = true;
+    h->eager_epoch = h->epoch;
+  }
   h->captured = capturing;
-  if (capturing || was) return hip_rc(mep::launch_clear_word(status_word(h), stream));
   return MEP_OK;
 }
 
@@ -193,6 +208,7 @@ static mep::PlanArgs plan_args(mep_handle* h, const int32_t* indices, int32_t T,
   a.spos = src_token_pos;
   a.status = status_word(h);
   a.status_next = status_next_word(h);
+  a.tok_status = tok_status(h);
   a.chunk_cnt = ws_ptr<int32_t>(h, h->lay.chunk_cnt);
   a.block_cnt = ws_ptr<int32_t>(h, h->lay.block_cnt);
   a.mask = ws_ptr<uint64_t>(h, h->lay.mask);
@@ -265,6 +281,7 @@ static mep::DispatchArgs dispatch_args(mep_handle* h, int32_t T, const void* x,
   a.block_cnt = ws_ptr<int32_t>(h, h->lay.block_cnt);
   a.status = status_word(h);
   a.status_next = status_next_word(h);
+  a.tok_status = tok_status(h);
   a.T = T;
   a.H = c.hidden_dim;
   a.k = c.num_experts_per_token;
@@ -423,6 +440,7 @@ int mep_dispatch_standard_moe(mep_handle* h, const int32_t* indices, int32_t T, 
   a.chunk_hist = ws_ptr<int32_t>(h, h->lay.sm_hist);
   a.status = status_word(h);
   a.status_next = status_next_word(h);
+  a.tok_status = tok_status(h);
   a.cap_em = cap_em;
   a.T = T;
   a.H = c.hidden_dim;
@@ -552,6 +570,18 @@ int mep_get_status(mep_handle* h, void* stream, int32_t* device_status) {
   hipError_t e = hipMemcpyAsync(&v, status_word(h), sizeof(v),
                                 hipMemcpyDeviceToHost, (hipStream_t)stream);
   if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e == hipSuccess && h->captured && h->plan_T > 0) {
+    // a captured iteration: OR in the per-token bits of its planned tokens,
+    // copied in pieces through a host buffer on the stack
+    const uint8_t* src = ws_ptr<uint8_t>(h, h->lay.tok_status);
+    uint8_t buf[4096];
+    for (int64_t i = 0; e == hipSuccess && i < h->plan_T; i += (int64_t)sizeof(buf)) {
+      const size_t n = (size_t)std::min<int64_t>(sizeof(buf), h->plan_T - i);
+      e = hipMemcpyAsync(buf, src + i, n, hipMemcpyDeviceToHost, (hipStream_t)stream);
+      if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+      for (size_t j = 0; e == hipSuccess && j < n; ++j) v |= buf[j];
+    }
+  }
   if (e != hipSuccess) return MEP_ERR_HIP;
   *device_status = (int32_t)v;
   return v ? MEP_ERR_DEVICE : MEP_OK;
@@ -585,6 +615,20 @@ int mep_probe_bf16(const float* in, uint16_t* out, int64_t n, void* stream) {
   if (n > 0 && (!in || !out)) return MEP_ERR_NULL;
   if (n > 0 && (!aligned16(in) || !aligned16(out))) return MEP_ERR_ALIGN;
   return hip_rc(mep::launch_probe_bf16(in, out, n, (hipStream_t)stream));
+}
+
+int mep_probe_stream(const void* src, void* dst, int64_t waves, int64_t rd_units,
+                     int64_t wr_units, void* stream) {
+  const int64_t kMaxUnits = (int64_t)1 << 30;  // 1 TiB either way
+  if (waves < 0 || rd_units < 0 || wr_units < 0) return MEP_ERR_SHAPE;
+  if (rd_units > kMaxUnits || wr_units > kMaxUnits) return MEP_ERR_SHAPE;
+  if (waves == 0) return (rd_units || wr_units) ? MEP_ERR_SHAPE : MEP_OK;
+  if (waves > ((int64_t)1 << 24)) return MEP_ERR_SHAPE;  // 256-thread blocks: 2^32 threads
+  if ((rd_units + waves - 1) / waves > mep::stream_probe_max_units()) return MEP_ERR_SHAPE;
+  if ((rd_units && !src) || !dst) return MEP_ERR_NULL;  // a read-only wave may store
+  if ((src && !aligned16(src)) || !aligned16(dst)) return MEP_ERR_ALIGN;
+  return hip_rc(mep::launch_stream_probe(src, dst, waves, rd_units, wr_units,
+                                         (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -39,8 +39,9 @@ struct RankDiv {
 
 // Byte offsets of the workspace sections (each 256-byte aligned).
 struct WsLayout {
-  size_t status;     // uint32 [4]: sticky MEP_DEV_* bits, one word per reset epoch [0, 1];
-                     // the word of captured iterations [2]; a word no one reads [3]
+  size_t status;     // uint32 [3]: sticky MEP_DEV_* bits, one word per reset epoch [0, 1];
+                     // the expert-major overflow word of captured iterations [2]
+  size_t tok_status; // uint8 [cap]: bad/repeated-id bits of each token of a captured plan
   size_t chunk_cnt;  // int32 [C][R]: rows earlier chunks of the same 16-chunk block send to each rank
   size_t block_cnt;  // int32 [ceil(C/16)][R]: rows each 16-chunk block sends to each rank
   size_t mask;       // uint64 [cap]: destination-rank mask of each token (0 = dropped)
@@ -61,6 +62,7 @@ struct PlanArgs {
   int32_t* spos;           // [R,cap]
   uint32_t* status;       // this epoch's status word
   uint32_t* status_next;  // the other epoch's word, cleared by the plan
+  uint8_t* tok_status;    // captured iteration: per-token bits stored here instead
   int32_t* chunk_cnt;
   int32_t* block_cnt;
   uint64_t* mask;
@@ -89,6 +91,7 @@ struct DispatchArgs {
   int32_t* spos;           // [R,cap]
   uint32_t* status;
   uint32_t* status_next;
+  uint8_t* tok_status;     // as PlanArgs
   int32_t T, H, k, R, E, cap, spos_base;
   int32_t quant, scale_dim;
   RankDiv rdiv;
@@ -163,6 +166,7 @@ struct SmArgs {                // standard-MoE dispatch
   int32_t* chunk_hist;          // [C][E]
   uint32_t* status;
   uint32_t* status_next;
+  uint8_t* tok_status;          // as PlanArgs
   int64_t cap_em;
   int32_t T, H, k, E, quant, scale_dim, spos_base, slices;
 };
@@ -178,9 +182,11 @@ hipError_t launch_combine_fp8(const CombineArgs& a, hipStream_t s);  // y holds 
 hipError_t launch_cast_fp8(const CastArgs& a, hipStream_t s);
 hipError_t launch_to_expert_major(const EmArgs& a, hipStream_t s);
 hipError_t launch_convert_combine_input(const ConvertArgs& a, hipStream_t s);
-hipError_t launch_clear_word(uint32_t* word, hipStream_t s);  // one-thread kernel: *word = 0
 hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int64_t n, hipStream_t s);
 hipError_t launch_probe_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t s);
 hipError_t launch_probe_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);
+hipError_t launch_stream_probe(const void* src, void* dst, int64_t waves, int64_t rd_units,
+                               int64_t wr_units, hipStream_t s);
+int stream_probe_max_units();  // read units (1 KiB each) one probe wave can take
 
 }  // namespace mep

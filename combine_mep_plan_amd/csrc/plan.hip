@@ -88,7 +88,7 @@ __global__ __launch_bounds__(1024) void plan_single_kernel(PlanArgs a) {
   const uint64_t mask = t < a.T ? load_token<KMAX>(a.indices, t, a.k, a.E, a.rdiv, ids, st) : 0ull;
   const int mine = ranks_popcount(mask, a.R, lane);
   if (lane < a.R) cnt[w][lane] = mine;
-  or_status(a.status, st);
+  report_status(a.status, a.tok_status, t, a.T, st);
   __syncthreads();
   int base = 0;
   if (lane < a.R) {
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(1024) void plan_count_kernel(PlanArgs a) {
   if (t < a.T) a.mask[t] = mask;
   const int mine = ranks_popcount(mask, a.R, lane);
   if (lane < a.R) cnt[w][lane] = mine;
-  or_status(a.status, st);
+  report_status(a.status, a.tok_status, t, a.T, st);
   __syncthreads();
   if (lane < a.R) {
     int pre = 0;

@@ -77,6 +77,20 @@ __device__ __forceinline__ void or_status(uint32_t* status, uint32_t st) {
     atomicOr(status, (any_bad ? MEP_DEV_BAD_INDEX : 0u) | (any_dup ? MEP_DEV_DUP_EXPERT : 0u));
 }
 
+// A plan kernel's report of its tokens' bits (st: this lane's token t).
+// Outside graph capture the wave ORs them into the status word (sticky until
+// reset).  In a captured iteration (tok_status set) every token's bits are
+// stored in its own byte -- each replay rewrites all of them, so nothing has
+// to be cleared first and no extra launch is captured.  Whole-wave call.
+__device__ __forceinline__ void report_status(uint32_t* status, uint8_t* tok_status, int t, int T,
+                                              uint32_t st) {
+  if (tok_status) {
+    if (t < T) tok_status[t] = (uint8_t)st;
+  } else {
+    or_status(status, st);
+  }
+}
+
 __device__ __forceinline__ uint64_t lane_value64(uint64_t v, int lane) {
   const uint32_t lo = (uint32_t)lane_value((int)(uint32_t)v, lane);
   const uint32_t hi = (uint32_t)lane_value((int)(uint32_t)(v >> 32), lane);

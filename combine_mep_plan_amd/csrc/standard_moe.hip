@@ -49,6 +49,9 @@ __global__ __launch_bounds__(64) void sm_count_kernel(SmArgs a) {
   extern __shared__ int32_t hist[];  // [E]
   const int lane = threadIdx.x;
   const int c = blockIdx.x;
+  // the next status word starts clean (the overflow bits come later, from the
+  // route launch)
+  if (c == 0 && lane == 0) *a.status_next = 0u;
   for (int e = lane; e < a.E; e += kWave) hist[e] = 0;
   __syncthreads();
   const int t = c * kChunk + lane;
@@ -72,7 +75,7 @@ __global__ __launch_bounds__(64) void sm_count_kernel(SmArgs a) {
       }
     }
   }
-  or_status(a.status, st);
+  report_status(a.status, a.tok_status, t, a.T, st);
   __syncthreads();
   for (int e = lane; e < a.E; e += kWave) a.chunk_hist[(size_t)c * a.E + e] = hist[e];
 }
@@ -188,7 +191,6 @@ __global__ __launch_bounds__(kRouteThreads) void sm_route_kernel(SmArgs a) {
   const int C = (a.T + kChunk - 1) / kChunk;
   const int32_t* hist = a.chunk_hist;
   if (FUSED) {
-    if (c == 0 && tid == 0) *a.status_next = 0u;  // the next reset epoch starts clean
     // per expert: total over all chunks and prefix over the chunks before c
     for (int e = tid; e < E; e += kRouteThreads) {
       int tot = 0, pre = 0;

@@ -1,6 +1,6 @@
-// Small launches: a device copy for route inspection, the status-word clear of
-// captured iterations, and probes that run the kernels' own device conversions
-// over caller arrays.
+// Small launches: a device copy for route inspection, probes that run the
+// kernels' own device conversions over caller arrays, and a streaming probe
+// that measures what HBM gives a given mix of reads and writes.
 #include "dev.h"
 #include "mep_internal.h"
 
@@ -13,8 +13,6 @@ __global__ void copy_i32_kernel(const int32_t* src, int32_t* dst, int64_t n) {
        i += (int64_t)gridDim.x * blockDim.x)
     dst[i] = src[i];
 }
-
-__global__ void clear_word_kernel(uint32_t* word) { *word = 0u; }
 
 __global__ void probe_e4m3_kernel(const float* in, uint8_t* out, int64_t n) {
   const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
@@ -37,17 +35,56 @@ __global__ void probe_bf16_kernel(const float* in, uint16_t* out, int64_t n) {
   }
 }
 
+// Streaming probe: `waves` waves share rd_units reads and wr_units writes of
+// 1 KiB (64 lanes x 16 bytes) as evenly as the counts allow; wave g reads
+// units [g*rd/waves, (g+1)*rd/waves) of src and writes its share of dst, each
+// a contiguous run.  Loads are non-temporal and all issued before the
+// stores (at most kProbeMaxRd units per wave, checked on the host); the
+// stored words fold in every loaded word, so no load can be dropped.
+constexpr int kProbeMaxRd = 16;
+
+__global__ __launch_bounds__(256) void stream_probe_kernel(const u32x4* src, u32x4* dst,
+                                                           int64_t waves, int64_t rd, int64_t wr) {
+  const int lane = threadIdx.x & 63;
+  const int64_t g = first_lane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (g >= waves) return;
+  const int64_t r0 = g * rd / waves, r1 = (g + 1) * rd / waves;
+  const int64_t w0 = g * wr / waves, w1 = (g + 1) * wr / waves;
+  u32x4 in[kProbeMaxRd];
+#pragma unroll
+  for (int i = 0; i < kProbeMaxRd; ++i) {
+    in[i] = u32x4{0, 0, 0, 0};
+    if (r0 + i < r1) in[i] = __builtin_nontemporal_load(src + (r0 + i) * kWave + lane);
+  }
+  u32x4 acc = u32x4{(uint32_t)g, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < kProbeMaxRd; ++i) acc ^= in[i];
+  for (int64_t u = w0; u < w1; ++u) {
+    acc[1] += 1u;
+    store_nt(dst + u * kWave + lane, acc);
+  }
+  if (w0 == w1 && lane == 0 && acc[0] == 0xFFFFFFFFu && acc[1] == 0xFFFFFFFFu)
+    dst[0] = acc;  // a read-only wave's loads must stay live; practically never taken
+}
+
 }  // namespace
+
+hipError_t launch_stream_probe(const void* src, void* dst, int64_t waves, int64_t rd_units,
+                               int64_t wr_units, hipStream_t s) {
+  if (waves == 0) return hipSuccess;
+  const int64_t blocks = (waves + 3) / 4;
+  stream_probe_kernel<<<(unsigned)blocks, 256, 0, s>>>(reinterpret_cast<const u32x4*>(src),
+                                                        reinterpret_cast<u32x4*>(dst), waves,
+                                                        rd_units, wr_units);
+  return hipGetLastError();
+}
+
+int stream_probe_max_units() { return kProbeMaxRd; }
 
 hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int64_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const int blocks = (int)std::min<int64_t>((n + 255) / 256, 1024);
   copy_i32_kernel<<<blocks, 256, 0, s>>>(src, dst, n);
-  return hipGetLastError();
-}
-
-hipError_t launch_clear_word(uint32_t* word, hipStream_t s) {
-  clear_word_kernel<<<1, 1, 0, s>>>(word);
   return hipGetLastError();
 }
 

@@ -28,11 +28,13 @@
  *     copy or host wait), so a sequence of them can be captured into a HIP
  *     graph; a replay reuses the handle state of the capture (its plan).  An
  *     iteration whose plan (mep_plan, mep_plan_dispatch or
- *     mep_dispatch_standard_moe) is captured reports its MEP_DEV_* bits in a
- *     status word of its own, cleared by a one-thread kernel captured in front
- *     of the plan: each replay starts clean, mep_get_status returns the bits
- *     of the latest replay (mep_reset between replays is allowed and changes
- *     nothing there), until a plan is issued outside capture again.
+ *     mep_dispatch_standard_moe) is captured keeps its MEP_DEV_* bits apart
+ *     (per planned token, and one word for the expert-major overflow that its
+ *     plan clears), so every replay starts clean without an extra launch:
+ *     mep_get_status returns the bits of the latest replay (of its last plan,
+ *     if it holds several), mep_reset between replays is allowed and changes
+ *     nothing there.  The next plan issued outside capture starts a new reset
+ *     epoch.
  */
 #ifndef MEP_H
 #define MEP_H
@@ -340,6 +342,22 @@ int mep_get_route(mep_handle *h, int32_t *recv_row, int32_t *em_row, void *strea
  */
 int mep_probe_e4m3(const float *in, uint8_t *out, int64_t n, void *stream);
 int mep_probe_bf16(const float *in, uint16_t *out, int64_t n, void *stream);
+
+/*
+ * Streaming probe (measurement, not part of the path): what HBM gives a mix of
+ * reads and writes spread over a number of waves, for comparing a kernel with
+ * plain streams of its own byte mix.  `waves` 64-lane waves share rd_units
+ * reads of src and wr_units writes of dst, each unit 1 KiB (16 bytes per
+ * lane), as evenly as the counts allow; each wave's share of src and of dst is
+ * one contiguous run, its loads are non-temporal and all issued before its
+ * non-temporal stores.  src holds rd_units KiB and dst wr_units KiB (at least
+ * 16 bytes when wr_units is 0: a never-taken store keeps read-only waves'
+ * loads live).  MEP_ERR_SHAPE when a wave would take more than 16 read units,
+ * for more than 2^24 waves or more than 2^30 units.  The values written are
+ * unspecified.
+ */
+int mep_probe_stream(const void *src, void *dst, int64_t waves, int64_t rd_units,
+                     int64_t wr_units, void *stream);
 
 #ifdef __cplusplus
 }

@@ -119,6 +119,15 @@ def test_call_order_and_argument_checks_before_any_launch():
     assert L.mep_probe_bf16(None, f, 8, None) == M.MEP_ERR_NULL
     assert L.mep_probe_bf16(f + 2, f, 8, None) == M.MEP_ERR_ALIGN
     assert L.mep_get_status(None, None, None) == M.MEP_ERR_NULL
+    ps = L.mep_probe_stream  # (src, dst, waves, rd_units, wr_units, stream)
+    assert ps(f, f, 100, 1601, 0, None) == M.MEP_ERR_SHAPE      # 17 read units in a wave
+    assert ps(f, f, (1 << 24) + 1, 0, 1, None) == M.MEP_ERR_SHAPE
+    assert ps(f, f, -1, 0, 0, None) == M.MEP_ERR_SHAPE
+    assert ps(f, f, 0, 1, 0, None) == M.MEP_ERR_SHAPE
+    assert ps(f, f, 0, 0, 0, None) == M.MEP_OK                  # nothing to do, no launch
+    assert ps(None, f, 10, 5, 5, None) == M.MEP_ERR_NULL
+    assert ps(f, None, 10, 5, 0, None) == M.MEP_ERR_NULL
+    assert ps(f + 4, f, 10, 5, 5, None) == M.MEP_ERR_ALIGN
     assert L.mep_destroy(h) == M.MEP_OK
     assert L.mep_destroy(None) == M.MEP_ERR_NULL
 

@@ -42,3 +42,11 @@ def test_byte_counts_match_the_buffers_they_move():
     # standard-MoE dispatch writes each expert row, its scales and source once
     assert bench.standard_moe_bytes(T, H, k, E, T * k, "fp8") == \
         T * H * 2 + T * k * i32 + T * k * (fp8_row + i32) + E * 8
+    # conversion back to rank rows: every expert-major row read with its
+    # dispatched weight, the route of every (token, position) read, each rank
+    # row written; their combine reads the rank rows and one route entry per
+    # position, writes the tokens
+    Uem = T * k
+    assert bench.convert_combine_input_bytes(T, H, k, U, Uem) == \
+        Uem * (H * 2 + f32) + T * k * 2 * i32 + U * H * 2
+    assert bench.combine_rank_sum_bytes(T, H, k, U) == U * H * 2 + T * k * i32 + T * H * 2

@@ -284,3 +284,38 @@ def test_hip_graph_status_across_replays_and_resets():
     assert M.mep_get_status(g.m.h) == 0
     M.mep_plan(g.m.h, dev(good), T, g.counts, g.spos)
     assert M.mep_get_status(g.m.h) == 0
+
+
+def test_hip_graph_expert_major_overflow_per_replay():
+    # plan+dispatch and the expert-major conversion captured with a small
+    # cap_em: routing every token to experts 0 and 1 fits (rows 0..191),
+    # routing spread over all 8 experts needs segments starting at row 256 and
+    # overflows; each replay reports its own overflow bit
+    wl = Workload("gov", 64, 256, 2, 4, 2, 64, "none", "uniform", "identity", "expert_major")
+    T, H, cap_em = wl.tokens, wl.hidden, 200
+    inp = make_inputs(wl, 13)
+    compact = np.tile(np.array([[0, 1]], np.int32), (T, 1))
+    spread = np.stack([np.array([t % 8, (t + 3) % 8]) for t in range(T)]).astype(np.int32)
+    inp = dict(inp, indices=compact)
+    g = gpu_plan_dispatch(wl, inp, fused=True)
+    b = _em_buffers(wl, cap_em)
+    M.mep_reset(g.m.h)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        M.mep_plan_dispatch(g.m.h, g.idx, T, g.counts, g.spos, g.x, g.w, None, g.recv_x, None,
+                            g.recv_w, g.recv_i)
+        M.mep_to_expert_major(g.m.h, g.recv_x, None, g.recv_i, g.counts, g.spos, b["em_x"],
+                              None, b["em_counts"], b["em_offsets"], b["em_src"], cap_em)
+    for ids, want in ((compact, 0), (spread, M.MEP_DEV_EM_OVERFLOW), (compact, 0),
+                      (spread, M.MEP_DEV_EM_OVERFLOW), (spread, M.MEP_DEV_EM_OVERFLOW),
+                      (compact, 0)):
+        g.idx.copy_(dev(ids))
+        torch.cuda.synchronize()
+        graph.replay()
+        assert M.mep_get_status(g.m.h) == want
+        M.mep_reset(g.m.h)
+    # the last replay's layout matches the oracle
+    pl, d = oracle_plan_dispatch(wl, dict(inp, indices=compact))
+    em = O.to_expert_major(d, pl, wl.ranks, wl.experts_per_rank, wl.cap, T, cap_em, 0)
+    assert np.array_equal(host(b["em_counts"]), em["em_counts"])
+    assert np.array_equal(host(b["em_offsets"]), em["em_offsets"])
