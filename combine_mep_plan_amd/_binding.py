@@ -75,6 +75,8 @@ def lib() -> C.CDLL:
             "mep_plan": ([p, p, i32, p, p, p], C.c_int),
             "mep_dispatch": ([p, p, p, p, p, p, p, p, p, p], C.c_int),
             "mep_plan_dispatch": ([p, p, i32, p, p, p, p, p, p, p, p, p, p], C.c_int),
+            "mep_plan_dispatch_noalloc": ([cfgp, p, i32, p, p, p, p, p, p, p, p, p, p],
+                                          C.c_int),
             "mep_dispatch_standard_moe": ([p, p, i32, p, p, p, p, p, p, p, i64, p], C.c_int),
             "mep_to_expert_major": ([p, p, p, p, p, p, p, p, p, p, p, i64, p], C.c_int),
             "mep_combine": ([p, i32, p, p, p, p], C.c_int),
@@ -305,6 +307,24 @@ def mep_plan_dispatch(h, indices, T, recv_counts, src_token_pos, x, weights, sca
         s))
     if st is not None:
         st.update(T=T, rm=True, em=False)
+
+
+def mep_plan_dispatch_noalloc(cfg, indices, T, recv_counts, src_token_pos, x, weights, scales,
+                              recv_x, recv_scales, recv_weights, recv_indices,
+                              stream=None) -> None:
+    """mep_plan_dispatch without a handle or workspace (the library's own
+    scratch); buffers are checked against cfg as for mep_plan_dispatch."""
+    fn = "mep_plan_dispatch_noalloc"
+    if 0 <= T <= cfg.max_num_inp_token_per_rank:
+        st = {"cfg": cfg}
+        _check_plan_buffers(fn, st, indices, T, recv_counts, src_token_pos)
+        _check_dispatch_buffers(fn, st, T, x, weights, scales, indices, recv_x, recv_scales,
+                                recv_weights, recv_indices)
+    s = _stream(stream, recv_x)
+    _check(fn, lib().mep_plan_dispatch_noalloc(
+        C.byref(cfg), _ptr(indices), T, _ptr(recv_counts), _ptr(src_token_pos), _ptr(x),
+        _ptr(weights), _ptr(scales), _ptr(recv_x), _ptr(recv_scales), _ptr(recv_weights),
+        _ptr(recv_indices), s))
 
 
 def mep_dispatch_standard_moe(h, indices, T, x, scales, em_x, em_scales, em_counts, em_offsets,

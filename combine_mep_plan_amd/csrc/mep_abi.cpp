@@ -56,7 +56,9 @@ using mep::WsLayout;
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-static int check_config(const mep_config* c) {
+namespace mep {
+
+int check_config(const mep_config* c) {
   if (!c) return MEP_ERR_NULL;
   const int64_t H = c->hidden_dim, R = c->world_size, epr = c->num_experts_per_rank;
   const int64_t k = c->num_experts_per_token, cap = c->max_num_inp_token_per_rank;
@@ -84,11 +86,114 @@ static int check_config(const mep_config* c) {
   return MEP_OK;
 }
 
-static mep::RankDiv make_rdiv(int32_t epr) {
-  mep::RankDiv d;
+RankDiv make_rdiv(int32_t epr) {
+  RankDiv d;
   d.m = (uint32_t)(((1u << 20) + (uint32_t)epr - 1) / (uint32_t)epr);
   return d;
 }
+
+int check_rank_map(const mep_config& c, RankDiv rd) {
+  const uint32_t E = (uint32_t)c.world_size * (uint32_t)c.num_experts_per_rank;
+  for (uint32_t e = 0; e < E; ++e)
+    if (rd(e) != e / (uint32_t)c.num_experts_per_rank) return MEP_ERR_CONFIG;
+  return MEP_OK;
+}
+
+int check_plan_args(const mep_config& c, const int32_t* indices, int32_t T,
+                    const int32_t* recv_counts, const int32_t* src_token_pos) {
+  if (!recv_counts || !src_token_pos) return MEP_ERR_NULL;
+  if (T < 0 || T > c.max_num_inp_token_per_rank) return MEP_ERR_SHAPE;
+  if (T > 0 && !indices) return MEP_ERR_NULL;
+  if ((indices && !aligned16(indices)) || !aligned16(recv_counts) || !aligned16(src_token_pos))
+    return MEP_ERR_ALIGN;
+  return MEP_OK;
+}
+
+// Scale columns the payload carries per row (0 for bf16 rows).
+static int scale_cols(const mep_config& c) {
+  return c.quant == MEP_QUANT_NONE ? 0 : c.scale_dim;
+}
+
+int check_dispatch_args(const mep_config& c, int32_t T, const void* x, const float* weights,
+                        const float* scales, const int32_t* indices, const void* recv_x,
+                        const float* recv_scales, const float* recv_weights,
+                        const int32_t* recv_indices) {
+  const bool carry = is_carry(c.quant);
+  if (!recv_x || !recv_weights || !recv_indices) return MEP_ERR_NULL;
+  if (scale_cols(c) > 0 && !recv_scales) return MEP_ERR_NULL;
+  if (T > 0 && (!x || !weights || !indices)) return MEP_ERR_NULL;
+  if (T > 0 && carry && c.scale_dim > 0 && !scales) return MEP_ERR_NULL;
+  if ((x && !aligned16(x)) || (weights && !aligned16(weights)) ||
+      (indices && !aligned16(indices)) || !aligned16(recv_x) ||
+      (carry && scales && !aligned16(scales)) ||
+      (recv_scales && !aligned16(recv_scales)) || !aligned16(recv_weights) ||
+      !aligned16(recv_indices))
+    return MEP_ERR_ALIGN;
+  return MEP_OK;
+}
+
+PlanArgs plan_args(const mep_config& c, RankDiv rd, const WsPtrs& w, const int32_t* indices,
+                   int32_t T, int32_t* recv_counts, int32_t* src_token_pos) {
+  PlanArgs a{};
+  a.indices = indices;
+  a.recv_counts = recv_counts;
+  a.spos = src_token_pos;
+  a.status = w.status;
+  a.status_next = w.status_next;
+  a.tok_status = w.tok_status;
+  a.chunk_cnt = w.chunk_cnt;
+  a.block_cnt = w.block_cnt;
+  a.mask = w.mask;
+  a.rrow = w.rrow;
+  a.ufirst = w.ufirst;
+  a.T = T;
+  a.k = c.num_experts_per_token;
+  a.R = c.world_size;
+  a.E = c.world_size * c.num_experts_per_rank;
+  a.cap = c.max_num_inp_token_per_rank;
+  a.spos_base = c.rank * c.world_size * c.max_num_inp_token_per_rank;
+  a.rdiv = rd;
+  return a;
+}
+
+DispatchArgs dispatch_args(const mep_config& c, RankDiv rd, const WsPtrs& w, int32_t T,
+                           const void* x, const float* weights, const float* scales,
+                           const int32_t* indices, void* recv_x, float* recv_scales,
+                           float* recv_weights, int32_t* recv_indices) {
+  DispatchArgs a{};
+  a.x = x;
+  a.x_scales = is_carry(c.quant) ? scales : nullptr;
+  a.quant = c.quant;
+  a.scale_dim = scale_cols(c);
+  a.w = weights;
+  a.idx = indices;
+  a.rrow = w.rrow;
+  a.ufirst = w.ufirst;
+  a.recv_x = recv_x;
+  a.recv_scales = recv_scales;
+  a.recv_w = recv_weights;
+  a.recv_idx = recv_indices;
+  a.mask = w.mask;
+  a.chunk_cnt = w.chunk_cnt;
+  a.block_cnt = w.block_cnt;
+  a.status = w.status;
+  a.status_next = w.status_next;
+  a.tok_status = w.tok_status;
+  a.T = T;
+  a.H = c.hidden_dim;
+  a.k = c.num_experts_per_token;
+  a.R = c.world_size;
+  a.E = c.world_size * c.num_experts_per_rank;
+  a.cap = c.max_num_inp_token_per_rank;
+  a.spos_base = c.rank * c.world_size * c.max_num_inp_token_per_rank;
+  a.rdiv = rd;
+  return a;
+}
+
+}  // namespace mep
+
+using mep::check_config;
+using mep::scale_cols;
 
 template <class T>
 static T* ws_ptr(mep_handle* h, size_t off) {
@@ -178,10 +283,8 @@ int mep_create(const mep_config* cfg, void* workspace, size_t workspace_bytes, m
   if (!aligned16(workspace)) return MEP_ERR_ALIGN;
   const WsLayout lay = mep::ws_layout(*cfg);
   if (workspace_bytes < lay.total) return MEP_ERR_SHAPE;
-  const mep::RankDiv rd = make_rdiv(cfg->num_experts_per_rank);
-  const uint32_t E = (uint32_t)cfg->world_size * (uint32_t)cfg->num_experts_per_rank;
-  for (uint32_t e = 0; e < E; ++e)
-    if (rd(e) != e / (uint32_t)cfg->num_experts_per_rank) return MEP_ERR_CONFIG;
+  const mep::RankDiv rd = mep::make_rdiv(cfg->num_experts_per_rank);
+  if (mep::check_rank_map(*cfg, rd) != MEP_OK) return MEP_ERR_CONFIG;
   mep_handle* h = (mep_handle*)calloc(1, sizeof(mep_handle));
   if (!h) return MEP_ERR_NOMEM;
   h->cfg = *cfg;
@@ -199,98 +302,45 @@ int mep_destroy(mep_handle* h) {
   return MEP_OK;
 }
 
+// The workspace pointers of a handle's next call.
+static mep::WsPtrs ws_ptrs(mep_handle* h) {
+  mep::WsPtrs w{};
+  w.status = status_word(h);
+  w.status_next = status_next_word(h);
+  w.tok_status = tok_status(h);
+  w.chunk_cnt = ws_ptr<int32_t>(h, h->lay.chunk_cnt);
+  w.block_cnt = ws_ptr<int32_t>(h, h->lay.block_cnt);
+  w.mask = ws_ptr<uint64_t>(h, h->lay.mask);
+  w.rrow = ws_ptr<int32_t>(h, h->lay.rrow);
+  w.ufirst = ws_ptr<uint32_t>(h, h->lay.ufirst);
+  return w;
+}
+
 static mep::PlanArgs plan_args(mep_handle* h, const int32_t* indices, int32_t T,
                                int32_t* recv_counts, int32_t* src_token_pos) {
-  const mep_config& c = h->cfg;
-  mep::PlanArgs a{};
-  a.indices = indices;
-  a.recv_counts = recv_counts;
-  a.spos = src_token_pos;
-  a.status = status_word(h);
-  a.status_next = status_next_word(h);
-  a.tok_status = tok_status(h);
-  a.chunk_cnt = ws_ptr<int32_t>(h, h->lay.chunk_cnt);
-  a.block_cnt = ws_ptr<int32_t>(h, h->lay.block_cnt);
-  a.mask = ws_ptr<uint64_t>(h, h->lay.mask);
-  a.rrow = ws_ptr<int32_t>(h, h->lay.rrow);
-  a.ufirst = ws_ptr<uint32_t>(h, h->lay.ufirst);
-  a.T = T;
-  a.k = c.num_experts_per_token;
-  a.R = c.world_size;
-  a.E = c.world_size * c.num_experts_per_rank;
-  a.cap = c.max_num_inp_token_per_rank;
-  a.spos_base = c.rank * c.world_size * c.max_num_inp_token_per_rank;
-  a.rdiv = h->rdiv;
-  return a;
+  return mep::plan_args(h->cfg, h->rdiv, ws_ptrs(h), indices, T, recv_counts, src_token_pos);
 }
 
 static int check_plan_args(mep_handle* h, const int32_t* indices, int32_t T,
                            const int32_t* recv_counts, const int32_t* src_token_pos) {
-  if (!h || !recv_counts || !src_token_pos) return MEP_ERR_NULL;
-  if (T < 0 || T > h->cfg.max_num_inp_token_per_rank) return MEP_ERR_SHAPE;
-  if (T > 0 && !indices) return MEP_ERR_NULL;
-  if ((indices && !aligned16(indices)) || !aligned16(recv_counts) || !aligned16(src_token_pos))
-    return MEP_ERR_ALIGN;
-  return MEP_OK;
-}
-
-// Scale columns the payload carries per row (0 for bf16 rows).
-static int scale_cols(const mep_config& c) {
-  return c.quant == MEP_QUANT_NONE ? 0 : c.scale_dim;
+  if (!h) return MEP_ERR_NULL;
+  return mep::check_plan_args(h->cfg, indices, T, recv_counts, src_token_pos);
 }
 
 static int check_dispatch_args(mep_handle* h, int32_t T, const void* x, const float* weights,
                                const float* scales, const int32_t* indices, const void* recv_x,
                                const float* recv_scales, const float* recv_weights,
                                const int32_t* recv_indices) {
-  const mep_config& c = h->cfg;
-  const bool carry = mep::is_carry(c.quant);
-  if (!recv_x || !recv_weights || !recv_indices) return MEP_ERR_NULL;
-  if (scale_cols(c) > 0 && !recv_scales) return MEP_ERR_NULL;
-  if (T > 0 && (!x || !weights || !indices)) return MEP_ERR_NULL;
-  if (T > 0 && carry && c.scale_dim > 0 && !scales) return MEP_ERR_NULL;
-  if ((x && !aligned16(x)) || (weights && !aligned16(weights)) ||
-      (indices && !aligned16(indices)) || !aligned16(recv_x) ||
-      (carry && scales && !aligned16(scales)) ||
-      (recv_scales && !aligned16(recv_scales)) || !aligned16(recv_weights) ||
-      !aligned16(recv_indices))
-    return MEP_ERR_ALIGN;
-  return MEP_OK;
+  return mep::check_dispatch_args(h->cfg, T, x, weights, scales, indices, recv_x, recv_scales,
+                                  recv_weights, recv_indices);
 }
 
 static mep::DispatchArgs dispatch_args(mep_handle* h, int32_t T, const void* x,
                                        const float* weights, const float* scales,
                                        const int32_t* indices, void* recv_x, float* recv_scales,
                                        float* recv_weights, int32_t* recv_indices) {
-  const mep_config& c = h->cfg;
-  mep::DispatchArgs a{};
-  a.x = x;
-  a.x_scales = mep::is_carry(c.quant) ? scales : nullptr;
-  a.quant = c.quant;
-  a.scale_dim = scale_cols(c);
-  a.w = weights;
-  a.idx = indices;
-  a.rrow = ws_ptr<int32_t>(h, h->lay.rrow);
-  a.ufirst = ws_ptr<uint32_t>(h, h->lay.ufirst);
-  a.recv_x = recv_x;
-  a.recv_scales = recv_scales;
-  a.recv_w = recv_weights;
-  a.recv_idx = recv_indices;
-  a.mask = ws_ptr<uint64_t>(h, h->lay.mask);
-  a.chunk_cnt = ws_ptr<int32_t>(h, h->lay.chunk_cnt);
-  a.block_cnt = ws_ptr<int32_t>(h, h->lay.block_cnt);
-  a.status = status_word(h);
-  a.status_next = status_next_word(h);
-  a.tok_status = tok_status(h);
-  a.T = T;
-  a.H = c.hidden_dim;
-  a.k = c.num_experts_per_token;
-  a.R = c.world_size;
-  a.E = c.world_size * c.num_experts_per_rank;
-  a.cap = c.max_num_inp_token_per_rank;
-  a.spos_base = c.rank * c.world_size * c.max_num_inp_token_per_rank;
-  a.rdiv = h->rdiv;
-  return a;
+  return mep::dispatch_args(h->cfg, h->rdiv, ws_ptrs(h), T, x, weights, scales, indices, recv_x,
+                            recv_scales, recv_weights, recv_indices);
 }
 
 int mep_plan(mep_handle* h, const int32_t* indices, int32_t T, int32_t* recv_counts,

@@ -171,6 +171,37 @@ struct SmArgs {                // standard-MoE dispatch
   int32_t T, H, k, E, quant, scale_dim, spos_base, slices;
 };
 
+// Workspace pointers one call uses: a handle's workspace, or the library's own
+// scratch in the entry point that allocates nothing.
+struct WsPtrs {
+  uint32_t* status;       // status bits ORed in
+  uint32_t* status_next;  // the word the plan clears
+  uint8_t* tok_status;    // per-token status bytes (captured iterations), or null
+  int32_t* chunk_cnt;
+  int32_t* block_cnt;
+  uint64_t* mask;
+  int32_t* rrow;
+  uint32_t* ufirst;
+};
+
+// Host-side checks and argument packing shared by the entry points
+// (mep_abi.cpp); each check returns MEP_OK or a MEP_ERR_* code.
+int check_config(const mep_config* c);
+RankDiv make_rdiv(int32_t epr);
+int check_rank_map(const mep_config& c, RankDiv rd);  // the divide-free map is exact
+int check_plan_args(const mep_config& c, const int32_t* indices, int32_t T,
+                    const int32_t* recv_counts, const int32_t* src_token_pos);
+int check_dispatch_args(const mep_config& c, int32_t T, const void* x, const float* weights,
+                        const float* scales, const int32_t* indices, const void* recv_x,
+                        const float* recv_scales, const float* recv_weights,
+                        const int32_t* recv_indices);
+PlanArgs plan_args(const mep_config& c, RankDiv rd, const WsPtrs& w, const int32_t* indices,
+                   int32_t T, int32_t* recv_counts, int32_t* src_token_pos);
+DispatchArgs dispatch_args(const mep_config& c, RankDiv rd, const WsPtrs& w, int32_t T,
+                           const void* x, const float* weights, const float* scales,
+                           const int32_t* indices, void* recv_x, float* recv_scales,
+                           float* recv_weights, int32_t* recv_indices);
+
 // Launchers (return hipError_t of the launch).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_plan_counts(const PlanArgs& a, hipStream_t s);  // count launch only, T > 0

@@ -192,6 +192,29 @@ int mep_plan_dispatch(mep_handle *h, const int32_t *indices, int32_t T, int32_t 
                       float *recv_weights, int32_t *recv_indices, void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * outputs as mep_plan_dispatch (recv_counts, src_token_pos, the receive rows,
+ * scales, weights and ids, with the same argument layouts, alignment and
+ * host-side checks) with no handle and no workspace.  The plan's scratch is a
+ * 2 MiB device array inside the library, one per GPU, held until the process
+ * ends; its address on the stream's GPU is looked up on the first call there
+ * (hipGetSymbolAddress, no allocation).  The batch must fit it: about
+ * 183 KiB for 4096 tokens at top-8 on 8 ranks, roughly
+ * T*(12 + 4k) + (T/64)*R*4 bytes in general; MEP_ERR_SHAPE beyond 2 MiB
+ * (no launch).  Every call on one GPU shares that scratch, so calls that
+ * overlap on one GPU (concurrent streams, or threads) race; calls ordered on
+ * one stream do not.  Tokens with bad expert ids are not dispatched, as in
+ * mep_plan_dispatch, but no status word is kept for mep_get_status.  No plan
+ * is left behind: combine needs a handle and its own plan.
+ */
+int mep_plan_dispatch_noalloc(const mep_config *cfg, const int32_t *indices, int32_t T,
+                              int32_t *recv_counts, int32_t *src_token_pos, const void *x,
+                              const float *weights, const float *scales, void *recv_x,
+                              float *recv_scales, float *recv_weights, int32_t *recv_indices,
+                              void *stream);
+
+/*
  * Standard-MoE layout ("MORI-EP User Guide" section 4,
  * convert_dispatch_output(): packed rows, per-expert counts, source info).
  * From the dispatch outputs (recv_x, recv_scales or NULL, recv_indices,

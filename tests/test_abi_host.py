@@ -189,6 +189,23 @@ def test_expert_major_offsets_must_fit_int32():
     assert L.mep_destroy(h) == M.MEP_OK
 
 
+def test_noalloc_refuses_batches_beyond_its_scratch():
+    # the entry point that allocates nothing keeps its plan in a 2 MiB scratch:
+    # 16384 tokens at top-32 on 64 ranks need more and are refused before any
+    # HIP call (the pointers are fake), as are the usual argument errors
+    L = M.lib()
+    f = FAKE
+    cfg = M.MepConfig(256, 0, 2, 32, 16384, 64, 0, M.MEP_QUANT_NONE)
+    na = L.mep_plan_dispatch_noalloc
+    assert na(C.byref(cfg), f, 16384, f, f, f, f, None, f, None, f, f, None) == M.MEP_ERR_SHAPE
+    assert na(C.byref(cfg), f, 16385, f, f, f, f, None, f, None, f, f, None) == M.MEP_ERR_SHAPE
+    assert na(None, f, 16, f, f, f, f, None, f, None, f, f, None) == M.MEP_ERR_NULL
+    assert na(C.byref(cfg), None, 16, f, f, f, f, None, f, None, f, f, None) == M.MEP_ERR_NULL
+    assert na(C.byref(cfg), f, 16, f, f + 4, f, f, None, f, None, f, f, None) == M.MEP_ERR_ALIGN
+    bad = M.MepConfig(256, 0, 2, 32, 16384, 64, 64, M.MEP_QUANT_NONE)  # rank out of range
+    assert na(C.byref(bad), f, 16, f, f, f, f, None, f, None, f, f, None) == M.MEP_ERR_CONFIG
+
+
 def test_error_strings():
     for code in range(-8, 1):
         assert M.mep_error_string(code) not in ("", "unknown")
