@@ -198,6 +198,26 @@ def _check_in_flight(m, layout, y_dev, w_dev, out_two_step):
     assert torch.equal(out, out_two_step), "in-flight rounding differs from cast + combine"
 
 
+_TABLES = {}
+
+
+def _oracle_cast(y_bits):
+    """The oracle's E4M3 direct cast of bf16 values, looked up in the oracle's
+    own encodes of all 65536 bf16 patterns (the cast depends on the input
+    pattern alone, so this is the oracle's result for every element; its
+    search-based encoder over 10^8 values would take minutes)."""
+    if "cast" not in _TABLES:
+        _TABLES["cast"] = O.cast_fp8_direct(np.arange(65536, dtype=np.uint16))
+    return _TABLES["cast"][y_bits]
+
+
+def _oracle_e4m3_to_bf16(codes):
+    """The oracle's exact E4M3 -> bf16 of every code, looked up likewise."""
+    if "dec" not in _TABLES:
+        _TABLES["dec"] = O.e4m3_to_bf16(np.arange(256, dtype=np.uint8))
+    return _TABLES["dec"][codes]
+
+
 def _check_cast_combine(y, y8_gpu, out_gpu, used, tok_rows, combine_ref, T, sample):
     """y: bf16 bits [rows, H]; used: routed rows; tok_rows[t]: rows token t reads.
     Checks the cast of the routed rows (all of them, or those of `sample`
@@ -211,15 +231,15 @@ def _check_cast_combine(y, y8_gpu, out_gpu, used, tok_rows, combine_ref, T, samp
     if sample is None:
         need |= used
     ref8 = np.full(y.shape, SENT8, dtype=np.uint8)
-    ref8[need] = O.cast_fp8_direct(y[need])
+    ref8[need] = _oracle_cast(y[need])
     g8 = host(y8_gpu).reshape(y.shape)
     assert np.array_equal(g8[need], ref8[need]), "direct cast differs"
     assert np.all(g8[~used] == SENT8), "direct cast touched rows that are not routed"
-    ref = combine_ref(O.e4m3_to_bf16(ref8))
+    ref = combine_ref(_oracle_e4m3_to_bf16(ref8))
     return check_combine(host(out_gpu, np.uint16)[toks], ref[toks])
 
 
-@pytest.mark.parametrize("T,sample", [(1, None), (200, None), (4096, 48)])
+@pytest.mark.parametrize("T,sample", [(1, None), (200, None), (4096, None)])
 def test_fp8_direct_cast_and_combine_rank_major(T, sample):
     wl = WORKLOADS["prefill"].with_tokens(T)
     _say(f"[fp8 direct] rank-major T={T}")
@@ -280,7 +300,7 @@ def test_fp8_combine_shared_rank_rows(R, epr, k):
     assert M.mep_get_status(m.h) == 0
 
 
-@pytest.mark.parametrize("T,sample", [(300, None), (4096, 48)])
+@pytest.mark.parametrize("T,sample", [(300, None), (4096, None)])
 def test_fp8_direct_cast_and_combine_expert_major(T, sample):
     wl = WORKLOADS["stdmoe"].with_tokens(T)
     wl = dataclasses.replace(wl, quant="none")

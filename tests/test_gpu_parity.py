@@ -515,10 +515,10 @@ def test_wide_hidden(H, T, R, epr, k, quant, layout):
 def test_buffers_past_4_gib():
     # 45000 bf16 tokens of 7168 columns: the receive buffers (5.2 GB) and the
     # expert-major rows (5.6 GB) reach byte offsets past 2^32, so every row
-    # address needs 64-bit arithmetic.  Checked: plan outputs in full; the rows
-    # at the top of every rank's buffer, of the last experts' segments and a
-    # random sample; the combine of the last and of sampled tokens (identity
-    # expert, so the oracle runs the same tokens as a small batch of their own).
+    # address needs 64-bit arithmetic.  Checked in full against the oracle:
+    # plan outputs, every received row, weight and id, the combine of every
+    # token (identity expert); then the expert-major layout and rows from the
+    # standard-MoE dispatch and its combine, every token.
     wl = dataclasses.replace(WORKLOADS["decode"], tokens=45000, cap=45000)
     T, R, cap, H, k, epr, E = wl.tokens, wl.ranks, wl.cap, wl.hidden, wl.topk, \
         wl.experts_per_rank, wl.experts
@@ -548,21 +548,15 @@ def test_buffers_past_4_gib():
         assert np.array_equal(sp[r, :n[r]], pl["src_token_pos"][r, :n[r]])
     rt = host(route)
     assert np.array_equal(rt, np.where(pl["slot"] >= 0, (idx_h // epr) * cap + pl["slot"], -1))
-    rng = np.random.default_rng(5)
-    rr = np.concatenate([np.repeat(np.arange(R), 16), rng.integers(0, R, 64)])
-    ss = np.concatenate([np.concatenate([np.arange(n[r] - 16, n[r]) for r in range(R)]),
-                         rng.integers(0, n.min(), 64)])
-    tt = pl["src_token_pos"][rr, ss]
-    ri_t, si_t = torch.from_numpy(rr).cuda(), torch.from_numpy(ss).cuda()
-    assert np.array_equal(host(recv_x[ri_t, si_t], np.uint16), x_h[tt])
-    assert np.array_equal(host(recv_w[ri_t, si_t]), w_h[tt])
-    assert np.array_equal(host(recv_i[ri_t, si_t]), idx_h[tt])
-    toks = np.unique(np.concatenate([np.arange(T - 32, T), rng.choice(T, 32, replace=False)]))
-    pl_s = O.plan(idx_h[toks], R, epr, len(toks))
-    d_s = O.dispatch(x_h[toks], w_h[toks], idx_h[toks], pl_s, R, epr, len(toks), False)
-    ref = O.combine(d_s["recv_x"], w_h[toks], idx_h[toks], pl_s, epr, len(toks))
-    tk = torch.from_numpy(toks).cuda()
-    check_combine(host(out[tk], np.uint16), ref)
+    d = O.dispatch(x_h, w_h, idx_h, pl, R, epr, cap, False)
+    for r in range(R):  # rank by rank, to keep host copies to one rank's rows
+        nr = int(n[r])
+        assert np.array_equal(host(recv_x[r, :nr], np.uint16), d["recv_x"][r, :nr]), r
+        assert np.array_equal(host(recv_w[r, :nr]).view(np.uint32),
+                              d["recv_weights"][r, :nr].view(np.uint32)), r
+        assert np.array_equal(host(recv_i[r, :nr]), d["recv_indices"][r, :nr]), r
+    ref = O.combine(d["recv_x"], w_h, idx_h, pl, epr, cap)
+    _say(f"[big] rank-major combine: {check_combine(host(out, np.uint16), ref)}")
     del recv_x, recv_w, recv_i
     torch.cuda.empty_cache()
 
@@ -586,19 +580,16 @@ def test_buffers_past_4_gib():
     assert np.array_equal(host(emc), cnt)
     offs = np.concatenate([[0], np.cumsum((cnt + 127) // 128 * 128)])
     assert np.array_equal(host(emo), offs)
+    em = O.to_expert_major(d, pl, R, epr, cap, T, cap_em, 0)
+    del d
+    assert np.array_equal(host(em_route), em["tok_em_row"])
     pos = host(emp)
-    for e in (E - 2, E - 1):  # the highest segments
-        toks_e = np.nonzero((idx_h == e).any(axis=1))[0]
-        o = offs[e]
-        assert np.array_equal(pos[o:o + cnt[e]], toks_e)
-        rows = host(em_x[o:o + cnt[e]], np.uint16)
-        assert np.array_equal(rows, x_h[toks_e])
-    er = host(em_route)
-    for t in toks:
-        for j in range(k):
-            e = idx_h[t, j]
-            assert offs[e] <= er[t, j] < offs[e] + cnt[e]
-    check_combine(host(out2[tk], np.uint16), ref)
+    for e in range(E):
+        o, ne = int(offs[e]), int(cnt[e])
+        assert np.array_equal(pos[o:o + ne], em["em_src_pos"][o:o + ne]), e
+        assert np.array_equal(host(em_x[o:o + ne], np.uint16), em["em_x"][o:o + ne]), e
+    ref2 = O.combine_em(em["em_x"], w_h, em["tok_em_row"])
+    _say(f"[big] expert-major combine: {check_combine(host(out2, np.uint16), ref2)}")
 
 
 @pytest.mark.parametrize("R,epr,k,layout", [(8, 32, 16, "rank_major"), (8, 32, 32, "rank_major"),
