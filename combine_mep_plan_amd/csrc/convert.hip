@@ -17,11 +17,12 @@
 // conversion's row of each position locates its expert output (-1 for a
 // position repeating an earlier position's expert, or dropped past cap_em).
 //
-// One wave per (token, 2 KiB slice of its rows), as in the combine: every
-// expert-major row of the token is loaded once with non-temporal loads (each
-// is read by exactly one wave), all loads before the multiply-adds, and each
-// rank row is written once with non-temporal stores.  Beyond top-8 the
-// positions are taken rank by rank with ordinary loads.
+// One wave per (token, 1 KiB slice of its rows): every expert-major row of
+// the token is loaded once with non-temporal loads (each is read by exactly
+// one wave), all loads before the multiply-adds, and each rank row is written
+// once with non-temporal stores.  Beyond top-8 the positions are taken rank by
+// rank with ordinary loads.  (At 4096 x 7168 on 32 ranks: 175 us against 179
+// us with 2 KiB slices, and 182 us with one wave per (token, rank, slice).)
 #include "dev.h"
 #include "mep_internal.h"
 
@@ -29,7 +30,7 @@ namespace mep {
 
 namespace {
 
-constexpr int kUnits = 2;  // 16-byte units per lane per wave (8 bf16 each)
+constexpr int kUnits = 1;  // 16-byte units per lane per wave (8 bf16 each)
 
 template <int KMAX>
 __global__ __launch_bounds__(256) void convert_kernel(ConvertArgs a) {
