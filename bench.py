@@ -555,6 +555,29 @@ def env_info(torch):
             "torch": torch.__version__, "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def sets_sweep(M, torch, wl, counts, steps):
+    """How the prefill loops depend on the number of rotated buffer sets (all
+    seed 0): step, combine and fused plan+dispatch µs for each count.  The
+    token rows of a few sets stay in the 256 MB Infinity Cache; many sets
+    leave every launch cold."""
+    r = Runner(M, torch, wl, (0,), max(counts))
+    out = {}
+    for n in counts:
+        sets = r.sets[:n]
+        for i in range(20):
+            r.step(sets[i % n])
+        st = r.loop(r.step, steps, sets=sets)
+        r.plan_dispatch(sets[0])
+        cb = r.loop(r.combine, steps, sets=sets)
+        pd = r.loop(r.plan_dispatch, steps, sets=sets)
+        r.M.mep_reset(r.m.h, r.stream)
+        out[n] = {"step_us": round(st * 1e3, 2), "combine_us": round(cb * 1e3, 2),
+                  "plan_dispatch_us": round(pd * 1e3, 2)}
+    del r
+    torch.cuda.empty_cache()
+    return out
+
+
 def stream_ceilings(M, torch, wl, U, reps=20):
     """What HBM gives plain streams with the prefill kernels' own byte mixes:
     the library's streaming probe with the same wave count (4096 tokens x 7
@@ -570,8 +593,15 @@ def stream_ceilings(M, torch, wl, U, reps=20):
         "dispatch_mix": (T * H * 2 + T * k * 8, U * (row_bytes(H, "fp8") + k * 8)),
         "combine_reads_only": (U * H * 2 + T * k * 8, 0),
         "combine_writes_only": (0, T * H * 2),
+        # the shapes plain streams do best with on this GPU (one wave per
+        # 2 KiB read, per 1 KiB written), for the same byte counts
+        "combine_reads_2k_waves": (U * H * 2 + T * k * 8, 0),
+        "dispatch_writes_1k_waves": (0, U * (row_bytes(H, "fp8") + k * 8)),
     }
     units = {n: (-(-r // 1024), -(-w // 1024)) for n, (r, w) in mixes.items()}
+    wave_count = {n: waves for n in mixes}
+    wave_count["combine_reads_2k_waves"] = -(-units["combine_reads_2k_waves"][0] // 2)
+    wave_count["dispatch_writes_1k_waves"] = units["dispatch_writes_1k_waves"][1]
     # one source and one destination buffer, each launch on the next region of
     # them, the regions of a cycle spanning at least 1 GiB each way (so no
     # launch finds its data in the 256 MB Infinity Cache)
@@ -583,17 +613,17 @@ def stream_ceilings(M, torch, wl, U, reps=20):
     for name, (ru, wu) in units.items():
         nreg = span // (1024 * max(ru, wu))
 
-        def fn(i, ru=ru, wu=wu, nreg=nreg):
+        def fn(i, ru=ru, wu=wu, nreg=nreg, nw=wave_count[name]):
             j = i % nreg
             src = src_all[j * ru * 1024:(j + 1) * ru * 1024] if ru else src_all[:16]
             dst = dst_all[j * wu * 1024:(j + 1) * wu * 1024] if wu else dst_all[:16]
-            M.mep_probe_stream(src, dst, waves, ru, wu, stream)
+            M.mep_probe_stream(src, dst, nw, ru, wu, stream)
         for i in range(nreg):
             fn(i)
         ms = _loop_ms(torch, stream, fn, max(reps, nreg))
         out[name] = {"GBps": round((ru + wu) * 1024 / (ms * 1e-3) / 1e9, 1),
                      "us": round(ms * 1e3, 2), "read_bytes": ru * 1024, "write_bytes": wu * 1024,
-                     "waves": waves}
+                     "waves": wave_count[name]}
     del src_all, dst_all
     return out
 
@@ -646,6 +676,9 @@ def main():
                          "(step, fused plan+dispatch, combine), reported under 'sweep'")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the 128-token decode leg (for kernel traces of it)")
+    ap.add_argument("--sets-sweep", default="",
+                    help="comma-separated buffer-set counts: prefill step, combine and fused "
+                         "plan+dispatch at each, reported under 'sets_sweep'")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -712,6 +745,12 @@ def main():
             del r
             torch.cuda.empty_cache()
 
+    ssweep = {}
+    if args.sets_sweep:
+        say("buffer-set sweep")
+        ssweep = sets_sweep(M, torch, wl, [int(v) for v in args.sets_sweep.split(",") if v],
+                            args.steps)
+
     sweep = {}
     for T in [int(v) for v in args.sweep.split(",") if v]:
         swl = wl.with_tokens(T, cap=max(T, wl.cap))
@@ -754,6 +793,7 @@ def main():
         "roofline": roofline,
         "workloads": extra,
         **({"sweep": sweep} if sweep else {}),
+        **({"sets_sweep": ssweep} if ssweep else {}),
         "cpu_baseline": cpu,
         "env": env_info(torch),
     }
