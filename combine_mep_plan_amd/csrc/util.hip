@@ -35,21 +35,33 @@ __global__ void probe_bf16_kernel(const float* in, uint16_t* out, int64_t n) {
   }
 }
 
-// Streaming probe: `waves` waves share rd_units reads and wr_units writes of
-// 1 KiB (64 lanes x 16 bytes) as evenly as the counts allow; wave g reads
-// units [g*rd/waves, (g+1)*rd/waves) of src and writes its share of dst, each
-// a contiguous run.  Loads are non-temporal and all issued before the
-// stores (at most kProbeMaxRd units per wave, checked on the host); the
-// stored words fold in every loaded word, so no load can be dropped.
+// Streaming probe: `waves` waves share rd reads and wr writes of 1 KiB units
+// (64 lanes x 16 bytes) as evenly as the counts allow: with rd = rq*waves + rr,
+// wave g reads rq units, plus one if g < rr, from a contiguous run of src
+// starting at unit g*rq + min(g, rr); writes likewise (quotients and
+// remainders come from the host, so no wave divides).  Loads are non-temporal
+// and all issued before the stores (at most kProbeMaxRd units per wave,
+// checked on the host); the stored words fold in every loaded word, so no
+// load can be dropped.
 constexpr int kProbeMaxRd = 16;
 
+struct ProbeShare {
+  int64_t q, r;  // units per wave and waves taking one more
+  __device__ __forceinline__ void range(int64_t g, int64_t& u0, int64_t& u1) const {
+    u0 = g * q + (g < r ? g : r);
+    u1 = u0 + q + (g < r ? 1 : 0);
+  }
+};
+
 __global__ __launch_bounds__(256) void stream_probe_kernel(const u32x4* src, u32x4* dst,
-                                                           int64_t waves, int64_t rd, int64_t wr) {
+                                                           int64_t waves, ProbeShare rd,
+                                                           ProbeShare wr) {
   const int lane = threadIdx.x & 63;
   const int64_t g = first_lane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (g >= waves) return;
-  const int64_t r0 = g * rd / waves, r1 = (g + 1) * rd / waves;
-  const int64_t w0 = g * wr / waves, w1 = (g + 1) * wr / waves;
+  int64_t r0, r1, w0, w1;
+  rd.range(g, r0, r1);
+  wr.range(g, w0, w1);
   u32x4 in[kProbeMaxRd];
 #pragma unroll
   for (int i = 0; i < kProbeMaxRd; ++i) {
@@ -73,9 +85,11 @@ hipError_t launch_stream_probe(const void* src, void* dst, int64_t waves, int64_
                                int64_t wr_units, hipStream_t s) {
   if (waves == 0) return hipSuccess;
   const int64_t blocks = (waves + 3) / 4;
+  const ProbeShare rd{rd_units / waves, rd_units % waves};
+  const ProbeShare wr{wr_units / waves, wr_units % waves};
   stream_probe_kernel<<<(unsigned)blocks, 256, 0, s>>>(reinterpret_cast<const u32x4*>(src),
-                                                        reinterpret_cast<u32x4*>(dst), waves,
-                                                        rd_units, wr_units);
+                                                        reinterpret_cast<u32x4*>(dst), waves, rd,
+                                                        wr);
   return hipGetLastError();
 }
 
