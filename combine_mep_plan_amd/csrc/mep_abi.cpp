@@ -667,6 +667,14 @@ int mep_probe_bf16(const float* in, uint16_t* out, int64_t n, void* stream) {
   return hip_rc(mep::launch_probe_bf16(in, out, n, (hipStream_t)stream));
 }
 
+int mep_probe_mxfp4(const uint16_t* in, uint8_t* q, uint8_t* e8, int64_t nblocks,
+                    void* stream) {
+  if (nblocks < 0 || nblocks > ((int64_t)1 << 32)) return MEP_ERR_SHAPE;
+  if (nblocks > 0 && (!in || !q || !e8)) return MEP_ERR_NULL;
+  if (nblocks > 0 && (!aligned16(in) || !aligned16(q))) return MEP_ERR_ALIGN;
+  return hip_rc(mep::launch_probe_mxfp4(in, q, e8, nblocks, (hipStream_t)stream));
+}
+
 int mep_probe_stream(const void* src, void* dst, int64_t waves, int64_t rd_units,
                      int64_t wr_units, void* stream) {
   const int64_t kMaxUnits = (int64_t)1 << 30;  // 1 TiB either way

@@ -52,42 +52,49 @@ __device__ __forceinline__ u32x4 quant16(u32x4 in0, u32x4 in1, float& scale) {
   return u32x4{w[0], w[1], w[2], w[3]};
 }
 
-// E2M1 code of v (round to nearest, ties to the even code, saturating at 6;
-// sign kept): the magnitude code counts the rounding boundaries below |v|,
-// with the boundaries that are ties between an odd and an even code belonging
-// to the even side.  Magnitudes by code: 0, 0.5, 1, 1.5, 2, 3, 4, 6.
-__device__ __forceinline__ uint32_t e2m1_code(float v) {
-  const float a = fabsf(v);
-  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                     (uint32_t)(a > 5.0f);
-  return c | ((__float_as_uint(v) >> 31) << 3);
-}
-
-// OCP MX FP4 block of one lane's 32 columns (in[0..3], bf16): shared exponent
-// floor(log2(amax)) - 2, clamped to [-127, 127], from amax's exponent field
-// (a subnormal or zero amax clamps to -127, so an all-zero block gets scale
-// byte 0 and signed-zero codes); codes E2M1(x * 2^-exponent), the product by a
-// power of two being exact.  Even column in the low nibble.
+// OCP MX FP4 block of one lane's 32 columns (in[0..3], bf16 pairs): shared
+// exponent floor(log2(amax)) - 2, clamped to [-127, 127], from amax's exponent
+// field (a subnormal or zero amax clamps to -127, so an all-zero block gets
+// scale byte 0 and signed-zero codes); codes E2M1(x / 2^exponent), round to
+// nearest with ties to the even code, saturating at 6, sign kept.  Even column
+// in the low nibble.
+//
+// amax is taken on the bf16 bit patterns: for finite values |x| orders like
+// its bits with the sign cleared, two columns per packed 16-bit max.  The
+// codes come from gfx950's scaled packed-bf16 -> FP4 convert, which divides
+// each value by the scale and rounds as above (checked on the GPU against the
+// rule for every finite bf16 value under every scale 2^-127 .. 2^127); each
+// call fills one byte (two columns) of an output word.  Its bf16 pairs are
+// taken by shuffles of the unit viewed as 8 bf16 values: a bit cast of each
+// 32-bit word of the unit compiled to the first word for all four calls.
 __device__ __forceinline__ u32x4 quant_mx4(const u32x4 (&in)[4], uint32_t& e8) {
-  float f[32];
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 m2 = {0, 0};
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      f[8 * i + 2 * w] = bf16_lo(in[i][w]);
-      f[8 * i + 2 * w + 1] = bf16_hi(in[i][w]);
+      const u16x2 v = __builtin_bit_cast(u16x2, in[i][w] & 0x7fff7fffu);
+      m2 = __builtin_elementwise_max(m2, v);
     }
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(f[i]));
-  const int biased = (int)(__float_as_uint(amax) >> 23);  // amax >= 0: no sign bit
+  const uint32_t amax = m2[0] > m2[1] ? m2[0] : m2[1];  // bf16 bits of the block's amax
+  const int biased = (int)(amax >> 7);
   const int se = max(biased - 127 - 2, -127);
   e8 = (uint32_t)(se + 127);
-  const float inv = __uint_as_float((uint32_t)(127 - se) << 23);  // 2^-se, a normal float
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  // 2^se as an fp32 value (2^-127 is the subnormal with only mantissa bit 22 set)
+  const float scale = __uint_as_float(se > -127 ? (uint32_t)(se + 127) << 23 : 0x00400000u);
+  uint32_t w[4];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) w[i / 8] |= e2m1_code(f[i] * inv) << (4 * (i % 8));
+  for (int i = 0; i < 4; ++i) {
+    const bf16x8 x = __builtin_bit_cast(bf16x8, in[i]);
+    uint32_t o = 0u;
+    o = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(o, __builtin_shufflevector(x, x, 0, 1), scale, 0);
+    o = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(o, __builtin_shufflevector(x, x, 2, 3), scale, 1);
+    o = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(o, __builtin_shufflevector(x, x, 4, 5), scale, 2);
+    o = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(o, __builtin_shufflevector(x, x, 6, 7), scale, 3);
+    w[i] = o;
+  }
   return u32x4{w[0], w[1], w[2], w[3]};
 }
 

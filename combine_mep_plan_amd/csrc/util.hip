@@ -3,6 +3,7 @@
 // that measures what HBM gives a given mix of reads and writes.
 #include "dev.h"
 #include "mep_internal.h"
+#include "payload.h"
 
 namespace mep {
 
@@ -22,6 +23,17 @@ __global__ void probe_e4m3_kernel(const float* in, uint8_t* out, int64_t n) {
   } else {
     for (int64_t j = i; j < n; ++j) out[j] = (uint8_t)pack_e4m3x4(in[j], 0.0f, 0.0f, 0.0f);
   }
+}
+
+// One MX FP4 block (32 bf16 columns) per thread, through the dispatch's own
+// block encoder: 16 code bytes and one scale byte per block.
+__global__ void probe_mxfp4_kernel(const u32x4* in, u32x4* q, uint8_t* e8, int64_t nblocks) {
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblocks) return;
+  const u32x4 x[4] = {in[4 * b], in[4 * b + 1], in[4 * b + 2], in[4 * b + 3]};
+  uint32_t e = 0;
+  q[b] = quant_mx4(x, e);
+  e8[b] = (uint8_t)e;
 }
 
 __global__ void probe_bf16_kernel(const float* in, uint16_t* out, int64_t n) {
@@ -106,6 +118,14 @@ hipError_t launch_probe_e4m3(const float* in, uint8_t* out, int64_t n, hipStream
   if (n == 0) return hipSuccess;
   const int64_t threads = (n + 3) / 4;
   probe_e4m3_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(in, out, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_mxfp4(const uint16_t* in, uint8_t* q, uint8_t* e8, int64_t nblocks,
+                              hipStream_t s) {
+  if (nblocks == 0) return hipSuccess;
+  probe_mxfp4_kernel<<<(unsigned)((nblocks + 255) / 256), 256, 0, s>>>(
+      reinterpret_cast<const u32x4*>(in), reinterpret_cast<u32x4*>(q), e8, nblocks);
   return hipGetLastError();
 }
 

@@ -167,7 +167,8 @@ int mep_plan(mep_handle *h, const int32_t *indices, int32_t T, int32_t *recv_cou
  *   recv_scales[r, s, :]  the block scales ([R,cap,H/128] fp32), or the carried
  *                         scales[t, :] ([R,cap,scale_dim]); NULL for bf16;
  * MEP_QUANT_MXFP4 writes [R,cap,H/2] packed E2M1 bytes and [R,cap,H/32] E8M0
- * bytes (= H/128 words); MEP_QUANT_FP4_CARRY copies H/2 bytes of x and the
+ * bytes (= H/128 words; x finite: NaN/Inf inputs are not supported);
+ * MEP_QUANT_FP4_CARRY copies H/2 bytes of x and the
  * scale_dim words of scales[t, :];
  *   recv_weights[r, s, :] the token's k weights (fp32 [R,cap,k]);
  *   recv_indices[r, s, :] the token's k expert ids (int32 [R,cap,k]).
@@ -365,6 +366,15 @@ int mep_get_route(mep_handle *h, int32_t *recv_row, int32_t *em_row, void *strea
  */
 int mep_probe_e4m3(const float *in, uint8_t *out, int64_t n, void *stream);
 int mep_probe_bf16(const float *in, uint16_t *out, int64_t n, void *stream);
+
+/*
+ * MX FP4 block probe: the dispatch's MEP_QUANT_MXFP4 block encoder over
+ * nblocks blocks of 32 bf16 values (in: uint16 bit patterns [nblocks,32],
+ * finite values only), writing each block's 16 packed E2M1 code bytes (q:
+ * uint8 [nblocks,16], even column in the low nibble) and its E8M0 scale byte
+ * (e8: uint8 [nblocks]).  in and q 16-byte aligned; nblocks <= 2^32.
+ */
+int mep_probe_mxfp4(const uint16_t *in, uint8_t *q, uint8_t *e8, int64_t nblocks, void *stream);
 
 /*
  * Streaming probe (measurement, not part of the path): what HBM gives a mix of

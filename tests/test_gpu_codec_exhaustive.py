@@ -1,9 +1,11 @@
-"""The two device conversions of the path over every input they take.
+"""The device conversions of the path over every input they take.
 
 The kernels' fp32 -> bf16 round-to-nearest-even (every combine output) and
 fp32 -> OCP E4M3 (every quantised dispatch code) run through the library's
 codec probes over all fp32 bit patterns in their domain, chunk by chunk on the
-device.  The sampled probe tests compare against the oracle; here the
+device; the MX FP4 block encoder (every MEP_QUANT_MXFP4 dispatch code and
+scale) runs over every finite bf16 value under every block exponent it can
+take.  The sampled probe tests compare against the oracle; here the
 references are definitions that need no sampling:
 
 - bf16: round to nearest even on the bit pattern of a finite float (add
@@ -12,7 +14,9 @@ references are definitions that need no sampling:
 - E4M3: torch's CPU cast to float8_e4m3fn (round to nearest even; an oracle
   pin checks the oracle's encoder against the same cast), for every pattern
   whose magnitude is at most 448 * (1 + 2^-23) -- the largest quotient a
-  quantising dispatch can form (amax / (amax / 448)).
+  quantising dispatch can form (amax / (amax / 448));
+- MX FP4: the oracle's block quantiser (its E2M1 encoder is pinned against
+  the format's table and exact midpoints on the CPU).
 
 Source: "Choosing an EP API and backend" (OCP E4M3 on gfx950; the HIP
 backend's combine gathers in BF16 or FP32).
@@ -23,6 +27,7 @@ import pytest
 import torch
 
 import combine_mep_plan_amd as M
+from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
 
@@ -69,3 +74,33 @@ def test_e4m3_conversion_every_input_in_the_quotient_range():
                                       for i in bad[:8, 0].tolist()]
             del b, v, out, ref, got
     torch.cuda.synchronize()
+
+
+def test_mxfp4_block_encoder_every_value_under_every_exponent():
+    """Blocks [A, v1..v31]: A = the largest bf16 magnitude of binade B sets the
+    block exponent (B = 0..254: every exponent -127..125, subnormal amax
+    included); the v run over every finite bf16 value with |v| <= A, both signs,
+    so each value meets every exponent under which it can occur, saturation
+    range [6, 8) included."""
+    blocks = []
+    for B in range(255):
+        A = (B << 7) | 0x7F
+        mags = np.arange(A + 1, dtype=np.uint16)
+        vals = np.concatenate([mags, mags | np.uint16(0x8000)])
+        pad = (-vals.size) % 31
+        vals = np.concatenate([vals, np.zeros(pad, np.uint16)]).reshape(-1, 31)
+        head = np.full((vals.shape[0], 1), A, np.uint16)
+        blocks.append(np.concatenate([head, vals], axis=1))
+    x = np.ascontiguousarray(np.concatenate(blocks))  # [nblocks, 32] bf16 bits
+    nb = x.shape[0]
+    q_ref, e8_ref = O.mx4_quant_row(x.reshape(-1))
+    xd = torch.from_numpy(x.view(np.int16)).cuda()
+    q = torch.empty(nb * 16, dtype=torch.uint8, device="cuda")
+    e8 = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    M.mep_probe_mxfp4(xd, q, e8, nb)
+    torch.cuda.synchronize()
+    got_q, got_e8 = q.cpu().numpy(), e8.cpu().numpy()
+    bad = np.nonzero(got_e8 != np.asarray(e8_ref).reshape(-1))[0]
+    assert bad.size == 0, [(int(i), int(got_e8[i]), int(e8_ref[i])) for i in bad[:8]]
+    bad = np.nonzero(got_q != np.asarray(q_ref).reshape(-1))[0]
+    assert bad.size == 0, [(int(i) // 16, hex(int(got_q[i])), hex(int(q_ref[i]))) for i in bad[:8]]
