@@ -15,6 +15,6 @@ from ._binding import (  # noqa: F401
     LIB_PATH, MepConfig, MepError, Mep, lib, mep_cast_fp8_direct, mep_combine, mep_combine_fp8,
     mep_combine_fp8_direct, mep_convert_combine_input, mep_create, mep_destroy, mep_dispatch,
     mep_dispatch_standard_moe, mep_error_string, mep_get_route, mep_get_status, mep_plan,
-    mep_plan_dispatch, mep_plan_dispatch_noalloc, mep_probe_bf16, mep_probe_e4m3, mep_probe_mxfp4, mep_probe_stream, mep_reset, mep_to_expert_major,
+    mep_plan_dispatch, mep_plan_dispatch_noalloc, mep_probe_bf16, mep_probe_e4m3, mep_probe_fp8_block, mep_probe_mxfp4, mep_probe_stream, mep_reset, mep_to_expert_major,
     mep_workspace_bytes,
 )

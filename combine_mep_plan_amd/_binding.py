@@ -90,6 +90,7 @@ def lib() -> C.CDLL:
             "mep_probe_e4m3": ([p, p, i64, p], C.c_int),
             "mep_probe_bf16": ([p, p, i64, p], C.c_int),
             "mep_probe_mxfp4": ([p, p, p, i64, p], C.c_int),
+            "mep_probe_fp8_block": ([p, p, p, i64, p], C.c_int),
             "mep_probe_stream": ([p, p, i64, i64, i64, p], C.c_int),
         }
         for name, (args, res) in sig.items():
@@ -453,6 +454,11 @@ def mep_probe_e4m3(inp, out, n, stream=None) -> None:
 
 def mep_probe_bf16(inp, out, n, stream=None) -> None:
     _check("mep_probe_bf16", lib().mep_probe_bf16(_ptr(inp), _ptr(out), n, _stream(stream, out)))
+
+
+def mep_probe_fp8_block(inp, q, scales, nblocks, stream=None) -> None:
+    _check("mep_probe_fp8_block", lib().mep_probe_fp8_block(_ptr(inp), _ptr(q), _ptr(scales),
+                                                            nblocks, _stream(stream, q)))
 
 
 def mep_probe_mxfp4(inp, q, e8, nblocks, stream=None) -> None:

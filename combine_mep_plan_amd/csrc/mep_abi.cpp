@@ -55,6 +55,7 @@ WsLayout ws_layout(const mep_config& c) {
 using mep::WsLayout;
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+static bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 namespace mep {
 
@@ -665,6 +666,14 @@ int mep_probe_bf16(const float* in, uint16_t* out, int64_t n, void* stream) {
   if (n > 0 && (!in || !out)) return MEP_ERR_NULL;
   if (n > 0 && (!aligned16(in) || !aligned16(out))) return MEP_ERR_ALIGN;
   return hip_rc(mep::launch_probe_bf16(in, out, n, (hipStream_t)stream));
+}
+
+int mep_probe_fp8_block(const uint16_t* in, uint8_t* q, float* scales, int64_t nblocks,
+                        void* stream) {
+  if (nblocks < 0 || nblocks > ((int64_t)1 << 28)) return MEP_ERR_SHAPE;
+  if (nblocks > 0 && (!in || !q || !scales)) return MEP_ERR_NULL;
+  if (nblocks > 0 && (!aligned16(in) || !aligned16(q) || !aligned4(scales))) return MEP_ERR_ALIGN;
+  return hip_rc(mep::launch_probe_fp8_block(in, q, scales, nblocks, (hipStream_t)stream));
 }
 
 int mep_probe_mxfp4(const uint16_t* in, uint8_t* q, uint8_t* e8, int64_t nblocks,

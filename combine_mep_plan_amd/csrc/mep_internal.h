@@ -216,6 +216,8 @@ hipError_t launch_convert_combine_input(const ConvertArgs& a, hipStream_t s);
 hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int64_t n, hipStream_t s);
 hipError_t launch_probe_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t s);
 hipError_t launch_probe_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);
+hipError_t launch_probe_fp8_block(const uint16_t* in, uint8_t* q, float* scales, int64_t nblocks,
+                                  hipStream_t s);
 hipError_t launch_probe_mxfp4(const uint16_t* in, uint8_t* q, uint8_t* e8, int64_t nblocks,
                               hipStream_t s);
 hipError_t launch_stream_probe(const void* src, void* dst, int64_t waves, int64_t rd_units,

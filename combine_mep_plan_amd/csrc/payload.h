@@ -14,11 +14,27 @@
 
 namespace mep {
 
+// x / b rounded to nearest even in fp32, from y = 1/b rounded to nearest:
+// q1 = x*y is within a few ulps of x/b; one correction with the exact
+// remainder x - q*b (a fused multiply-add) makes it faithful and a second
+// one makes it the correctly rounded quotient (Markstein's theorem, which
+// holds while the remainders stay normal: the caller keeps b >= 2^-60, where
+// every quotient of magnitude >= 2^-11 has a normal remainder).  The sign of
+// a zero quotient is x's.  Three fused multiply-adds and two multiplies
+// instead of an IEEE division each.
+__device__ __forceinline__ float div_by_recip(float x, float b, float y) {
+  const float q1 = x * y;
+  const float r1 = __builtin_fmaf(-q1, b, x);
+  const float q2 = __builtin_fmaf(r1, y, q1);
+  const float r2 = __builtin_fmaf(-q2, b, x);
+  return __builtin_copysignf(__builtin_fmaf(r2, y, q2), x);
+}
+
 // FP8 block quantisation of one lane's 16 columns (in0: columns 0..7, in1:
 // 8..15, bf16) into 16 OCP E4M3 codes: the 8 lanes of a 128-column block share
-// scale = amax / 448 (fp32 division); codes are E4M3(x / scale) by correctly
-// rounded division and the packed convert (round to nearest even); an all-zero
-// block gives scale 0 and signed-zero codes.
+// scale = amax / 448 (fp32 division); codes are E4M3(x / scale) with the
+// quotient correctly rounded and the packed convert (round to nearest even);
+// an all-zero block gives scale 0 and signed-zero codes.
 __device__ __forceinline__ u32x4 quant16(u32x4 in0, u32x4 in1, float& scale) {
   float f[16];
 #pragma unroll
@@ -44,7 +60,13 @@ __device__ __forceinline__ u32x4 quant16(u32x4 in0, u32x4 in1, float& scale) {
              ((__float_as_uint(f[4 * i + 1]) >> 31) << 15) |
              ((__float_as_uint(f[4 * i + 2]) >> 31) << 23) |
              ((__float_as_uint(f[4 * i + 3]) >> 31) << 31);
-  } else {
+  } else if (s >= 0x1p-60f) {
+    const float y = 1.0f / s;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = pack_e4m3x4(div_by_recip(f[4 * i], s, y), div_by_recip(f[4 * i + 1], s, y),
+                         div_by_recip(f[4 * i + 2], s, y), div_by_recip(f[4 * i + 3], s, y));
+  } else {  // blocks with amax below 448 * 2^-60
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       w[i] = pack_e4m3x4(f[4 * i] / s, f[4 * i + 1] / s, f[4 * i + 2] / s, f[4 * i + 3] / s);

@@ -36,6 +36,20 @@ __global__ void probe_mxfp4_kernel(const u32x4* in, u32x4* q, uint8_t* e8, int64
   e8[b] = (uint8_t)e;
 }
 
+// FP8 blocks (128 bf16 columns) through the dispatch's own block encoder:
+// 8 lanes per block, 16 columns each, as in a dispatch wave; 128 code bytes
+// and one fp32 scale per block.
+__global__ void probe_fp8_block_kernel(const u32x4* in, u32x4* q, float* scales,
+                                       int64_t nblocks) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t b = g >> 3;
+  const int part = (int)(g & 7);
+  if (b >= nblocks) return;  // all 8 lanes of a block leave together
+  float scale = 0.0f;
+  q[b * 8 + part] = quant16(in[b * 16 + part * 2], in[b * 16 + part * 2 + 1], scale);
+  if (part == 0) scales[b] = scale;
+}
+
 __global__ void probe_bf16_kernel(const float* in, uint16_t* out, int64_t n) {
   const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 2;
   if (i + 1 < n) {
@@ -126,6 +140,15 @@ hipError_t launch_probe_mxfp4(const uint16_t* in, uint8_t* q, uint8_t* e8, int64
   if (nblocks == 0) return hipSuccess;
   probe_mxfp4_kernel<<<(unsigned)((nblocks + 255) / 256), 256, 0, s>>>(
       reinterpret_cast<const u32x4*>(in), reinterpret_cast<u32x4*>(q), e8, nblocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_fp8_block(const uint16_t* in, uint8_t* q, float* scales, int64_t nblocks,
+                                  hipStream_t s) {
+  if (nblocks == 0) return hipSuccess;
+  const int64_t threads = nblocks * 8;
+  probe_fp8_block_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(
+      reinterpret_cast<const u32x4*>(in), reinterpret_cast<u32x4*>(q), scales, nblocks);
   return hipGetLastError();
 }
 

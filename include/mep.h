@@ -368,6 +368,16 @@ int mep_probe_e4m3(const float *in, uint8_t *out, int64_t n, void *stream);
 int mep_probe_bf16(const float *in, uint16_t *out, int64_t n, void *stream);
 
 /*
+ * FP8 block probe: the dispatch's MEP_QUANT_FP8_E4M3_BLOCK128 block encoder
+ * over nblocks blocks of 128 bf16 values (in: uint16 bit patterns
+ * [nblocks,128], finite values only), writing each block's 128 E4M3 codes (q:
+ * uint8 [nblocks,128]) and its fp32 scale (scales [nblocks]).  in and q
+ * 16-byte aligned, scales 4-byte aligned; nblocks <= 2^28.
+ */
+int mep_probe_fp8_block(const uint16_t *in, uint8_t *q, float *scales, int64_t nblocks,
+                        void *stream);
+
+/*
  * MX FP4 block probe: the dispatch's MEP_QUANT_MXFP4 block encoder over
  * nblocks blocks of 32 bf16 values (in: uint16 bit patterns [nblocks,32],
  * finite values only), writing each block's 16 packed E2M1 code bytes (q:

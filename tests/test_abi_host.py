@@ -122,6 +122,11 @@ def test_call_order_and_argument_checks_before_any_launch():
     assert L.mep_probe_mxfp4(f, None, f, 1, None) == M.MEP_ERR_NULL
     assert L.mep_probe_mxfp4(f + 2, f, f, 1, None) == M.MEP_ERR_ALIGN
     assert L.mep_probe_mxfp4(None, None, None, 0, None) == M.MEP_OK
+    assert L.mep_probe_fp8_block(f, f, f, -1, None) == M.MEP_ERR_SHAPE
+    assert L.mep_probe_fp8_block(f, f, None, 1, None) == M.MEP_ERR_NULL
+    assert L.mep_probe_fp8_block(f, f + 8, f, 1, None) == M.MEP_ERR_ALIGN
+    assert L.mep_probe_fp8_block(f, f, f + 2, 1, None) == M.MEP_ERR_ALIGN
+    assert L.mep_probe_fp8_block(None, None, None, 0, None) == M.MEP_OK
     assert L.mep_get_status(None, None, None) == M.MEP_ERR_NULL
     ps = L.mep_probe_stream  # (src, dst, waves, rd_units, wr_units, stream)
     assert ps(f, f, 100, 1601, 0, None) == M.MEP_ERR_SHAPE      # 17 read units in a wave

@@ -3,9 +3,11 @@
 The kernels' fp32 -> bf16 round-to-nearest-even (every combine output) and
 fp32 -> OCP E4M3 (every quantised dispatch code) run through the library's
 codec probes over all fp32 bit patterns in their domain, chunk by chunk on the
-device; the MX FP4 block encoder (every MEP_QUANT_MXFP4 dispatch code and
-scale) runs over every finite bf16 value under every block exponent it can
-take.  The sampled probe tests compare against the oracle; here the
+device; the FP8 block encoder (every MEP_QUANT_FP8_E4M3_BLOCK128 dispatch
+code and scale) over every pair of a finite bf16 value and a bf16 block amax
+at least its magnitude, and the MX FP4 block encoder (every MEP_QUANT_MXFP4
+dispatch code and scale) over every finite bf16 value under every block
+exponent it can take.  The sampled probe tests compare against the oracle; here the
 references are definitions that need no sampling:
 
 - bf16: round to nearest even on the bit pattern of a finite float (add
@@ -15,6 +17,12 @@ references are definitions that need no sampling:
   pin checks the oracle's encoder against the same cast), for every pattern
   whose magnitude is at most 448 * (1 + 2^-23) -- the largest quotient a
   quantising dispatch can form (amax / (amax / 448));
+- FP8 blocks: scale = fp32(amax / 448) and quotient = fp32(x / scale), both
+  formed in fp64 and rounded once to fp32 -- which is the correctly rounded
+  fp32 result here, because an 8-bit bf16 numerator over an fp32 denominator
+  (or over 448) never comes within 2^-53 of an fp32 rounding midpoint
+  without being one, and never is one -- then the device E4M3 conversion
+  checked above;
 - MX FP4: the oracle's block quantiser (its E2M1 encoder is pinned against
   the format's table and exact midpoints on the CPU).
 
@@ -104,3 +112,53 @@ def test_mxfp4_block_encoder_every_value_under_every_exponent():
     assert bad.size == 0, [(int(i), int(got_e8[i]), int(e8_ref[i])) for i in bad[:8]]
     bad = np.nonzero(got_q != np.asarray(q_ref).reshape(-1))[0]
     assert bad.size == 0, [(int(i) // 16, hex(int(got_q[i])), hex(int(q_ref[i]))) for i in bad[:8]]
+
+
+def _fp8_blocks(A):
+    """Blocks [A, v1..v127] for amax patterns A (int64, positive finite bf16):
+    the v run over every bf16 value with |v| <= A, both signs, zero-padded."""
+    nb = (2 * (A + 1) + 126) // 127
+    total = int(nb.sum())
+    blk_a = torch.repeat_interleave(A, nb)
+    start = torch.repeat_interleave(torch.cumsum(nb, 0) - nb, nb)
+    within = torch.arange(total, device=A.device) - start
+    idx = within[:, None] * 127 + torch.arange(127, device=A.device)[None, :]
+    a = blk_a[:, None]
+    v = torch.where(idx <= a, idx, 0x8000 + idx - a - 1)
+    v = torch.where(idx < 2 * (a + 1), v, torch.zeros_like(v))
+    return torch.cat([a, v], dim=1)  # [blocks, 128] bf16 bit patterns as int64
+
+
+def test_fp8_block_encoder_every_value_under_every_amax():
+    """1.07e9 (value, amax) pairs: every positive finite bf16 amax (and zero),
+    with every bf16 value of magnitude up to it, through the dispatch's block
+    encoder (which divides by the scale through its reciprocal and two
+    remainder corrections for scales >= 2^-60, by IEEE division below)."""
+    amax_all = np.arange(0, 0x7F80, dtype=np.int64)
+    nb_all = (2 * (amax_all + 1) + 126) // 127
+    per_chunk = 1 << 20  # blocks per device pass
+    lo = 0
+    while lo < amax_all.size:
+        hi = lo + max(1, int(np.searchsorted(np.cumsum(nb_all[lo:]), per_chunk, side="right")))
+        bits = _fp8_blocks(torch.from_numpy(amax_all[lo:hi]).cuda())
+        nb = bits.shape[0]
+        x = _floats(bits << 16)  # [nb,128] fp32 values of the bf16 patterns
+        s_ref = (x[:, 0].double() / 448.0).float()
+        q_ref = (x.double() / s_ref.double()[:, None]).float()
+        q_ref = torch.where(s_ref[:, None] == 0, x, q_ref)  # all-zero block: signed zeros
+        codes_ref = torch.empty(q_ref.shape, dtype=torch.uint8, device="cuda")
+        M.mep_probe_e4m3(q_ref.contiguous(), codes_ref, q_ref.numel())
+        x16 = (bits - 65536 * (bits >= 32768).to(torch.int64)).to(torch.int16).contiguous()
+        codes = torch.empty((nb, 128), dtype=torch.uint8, device="cuda")
+        scales = torch.empty(nb, dtype=torch.float32, device="cuda")
+        M.mep_probe_fp8_block(x16, codes, scales, nb)
+        bad = (scales.view(torch.int32) != s_ref.view(torch.int32)).nonzero()
+        assert bad.numel() == 0, [(hex(int(bits[i, 0])), float(scales[i]), float(s_ref[i]))
+                                  for i in bad[:8, 0].tolist()]
+        bad = (codes != codes_ref).nonzero()
+        assert bad.numel() == 0, [(hex(int(bits[i, 0])), hex(int(bits[i, j])), hex(int(codes[i, j])),
+                                   hex(int(codes_ref[i, j])))
+                                  for i, j in bad[:8].tolist()]
+        del bits, x, s_ref, q_ref, codes_ref, x16, codes, scales
+        lo = hi
+    torch.cuda.synchronize()
