@@ -7,22 +7,26 @@
 // slot, each expert segment starting at a multiple of 128 rows; padding rows
 // are not written.
 //
-// Three launches:
-//   count:   one wave per (rank, 64-row chunk) builds each receive row's mask of
-//            the rank's local experts and the chunk's per-expert row counts (one
-//            ballot per local expert); it also clears the (token, top-k) ->
-//            expert-major row map;
-//   offsets: one workgroup; each thread sums a group of chunks for one expert
-//            (independent loads), and the padded experts are scanned through
-//            LDS into segment offsets;
-//   scatter: one wave per (receive row, slice of the row); the row's place
-//            inside an expert segment is the segment offset, plus the rows of
-//            the rank's earlier chunks naming that expert (one load per lane
-//            and a wave reduction), plus a ballot count of the earlier rows of
-//            its own chunk.  Each slice is copied with 16-byte-per-lane loads
-//            and non-temporal stores.
+// Two launches:
+//   count:   one workgroup per rank; its 16 waves take consecutive runs of the
+//            rank's 64-row receive chunks.  Per row: the mask of the rank's
+//            local experts it names; per chunk: one ballot per local expert
+//            gives the chunk's rows naming it.  Each wave keeps running sums
+//            (one lane per local expert), the waves' totals meet in LDS, and
+//            the launch writes every expert's row count and, per (chunk,
+//            expert), the rows of the rank's earlier chunks naming it -- an
+//            expert's rows all come from its own rank, so no other workgroup
+//            is involved.  It also clears the (token, top-k) -> expert-major
+//            row map;
+//   scatter: every workgroup first scans the experts' padded row counts in
+//            LDS into segment offsets (workgroup 0 also writes them out);
+//            then one wave per (receive row, slice of the row): the row's
+//            place inside an expert segment is the segment offset, plus the
+//            rows of the rank's earlier chunks naming that expert, plus a
+//            ballot count of the earlier rows of its own chunk.  Each slice
+//            is copied with 16-byte-per-lane loads and non-temporal stores.
 #include "dev.h"
-#include "mep_internal.h"
+#include "route.h"
 
 namespace mep {
 
@@ -32,139 +36,98 @@ __device__ __forceinline__ int clamp_count(const EmArgs& a, int r) {
   return min(max(a.recv_counts[r], 0), a.cap);
 }
 
-__global__ __launch_bounds__(256) void em_count_kernel(EmArgs a) {
+constexpr int kCountWaves = 16;
+
+template <int KMAX>
+__global__ __launch_bounds__(kCountWaves * 64) void em_count_kernel(EmArgs a) {
+  __shared__ int32_t wtot[kCountWaves][kMaxEpr];
   // clear the (t, j) -> expert-major row map
   const int64_t nmap = (int64_t)a.T * a.k;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nmap;
        i += (int64_t)gridDim.x * blockDim.x)
     a.em_row[i] = -1;
 
-  const int lane = threadIdx.x & 63;
-  const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int r = g / a.CR, c = g % a.CR;
-  if (r >= a.R) return;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = blockIdx.x;
   const int cnt = clamp_count(a, r);
-  if (c * kChunk >= cnt) return;  // whole wave
-  const int s = c * kChunk + lane;
+  const int nch = (cnt + kChunk - 1) / kChunk;
+  const int per = (nch + kCountWaves - 1) / kCountWaves;
+  const int c0 = min(w * per, nch), c1 = min(c0 + per, nch);
   const int E = a.R * a.epr;
-  uint64_t lm = 0;
-  if (s < cnt) {
-    const size_t row = (size_t)r * a.cap + s;
-    const int32_t* ids = a.recv_idx + row * a.k;
-    for (int j = 0; j < a.k; ++j) {
-      const int e = ids[j];
-      if (e >= 0 && e < E && e / a.epr == r) lm |= 1ull << (e - r * a.epr);
+  constexpr int B = KMAX <= 8 ? 4 : 1;  // chunks whose ids are loaded together
+  int run = 0;  // lane l: rows of this wave's earlier chunks naming local expert l
+  int pre0[B];  // the first batch's prefixes, stored once the base is known
+#pragma unroll
+  for (int q = 0; q < B; ++q) pre0[q] = 0;
+  for (int cb = c0; cb < c1; cb += B) {  // uniform
+    int ids[B][KMAX];
+#pragma unroll
+    for (int q = 0; q < B; ++q) {
+      const int s = (cb + q) * kChunk + lane;
+      if (cb + q < c1 && s < cnt) load_ids<KMAX>(a.recv_idx, r * a.cap + s, a.k, ids[q]);
     }
-    a.lmask[row] = lm;
+#pragma unroll
+    for (int q = 0; q < B; ++q) {
+      const int c = cb + q;
+      if (c >= c1) break;  // uniform
+      const int s = c * kChunk + lane;
+      uint64_t lm = 0;
+      if (s < cnt) {
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+          const int e = ids[q][j];
+          if (j < a.k && e >= 0 && e < E && e / a.epr == r) lm |= 1ull << (e - r * a.epr);
+        }
+        a.lmask[(size_t)r * a.cap + s] = lm;
+      }
+      int mine = 0;
+      for (int l = 0; l < a.epr; ++l) {
+        const uint64_t b = ballot((lm >> l) & 1ull);
+        if (lane == l) mine = __popcll(b);
+      }
+      if (cb == c0) pre0[q] = run;
+      else if (lane < a.epr) a.ccnt[((size_t)r * a.CR + c) * a.epr + lane] = run;
+      run += mine;
+    }
   }
-  int mine = 0;
-  for (int l = 0; l < a.epr; ++l) {
-    const uint64_t b = ballot((lm >> l) & 1ull);
-    if (lane == l) mine = __popcll(b);
+  if (lane < a.epr) wtot[w][lane] = run;
+  __syncthreads();
+  if (lane < a.epr) {
+    int base = 0, tot = 0;
+#pragma unroll
+    for (int ww = 0; ww < kCountWaves; ++ww) {
+      const int v = wtot[ww][lane];
+      tot += v;
+      base += ww < w ? v : 0;
+    }
+    if (w == 0) a.em_counts[r * a.epr + lane] = tot;
+#pragma unroll
+    for (int q = 0; q < B; ++q)
+      if (c0 + q < c1) a.ccnt[((size_t)r * a.CR + c0 + q) * a.epr + lane] = pre0[q] + base;
+    if (base)  // chunks past the first batch (more than B per wave)
+      for (int c = c0 + B; c < c1; ++c) a.ccnt[((size_t)r * a.CR + c) * a.epr + lane] += base;
   }
-  if (lane < a.epr) a.ccnt[((size_t)r * a.CR + c) * a.epr + lane] = mine;
 }
 
-constexpr int kOffThreads = 1024;
-constexpr int kMaxExperts = kMaxRanks * kMaxEpr;
 // 16-byte units per lane per scatter wave.  Each wave first finds its row's
 // rank, local experts and in-chunk position, so fewer, larger waves pay that
 // less often: at 4096 x 7168 FP8 on 32 ranks the conversion took 129, 95.5,
 // 91.6 and 94.8 us with 1, 2, 3 and 4 units per lane.
 constexpr int kEmUnitsPerLane = 3;
 
-// Chunks [c0, c1) of expert e's rank that thread group `grp` of G covers.
-__device__ __forceinline__ void group_chunks(const EmArgs& a, int e, int grp, int G, int& r,
-                                             int& l, int& c0, int& c1) {
-  r = e / a.epr;
-  l = e - r * a.epr;
-  const int nch = (clamp_count(a, r) + kChunk - 1) / kChunk;
-  const int per = (nch + G - 1) / G;
-  c0 = min(grp * per, nch);
-  c1 = min(c0 + per, nch);
-}
-
-__device__ __forceinline__ int group_rows(const EmArgs& a, int r, int l, int c0, int c1) {
-  int acc[4] = {0, 0, 0, 0};
-  int c = c0;
-  for (; c + 4 <= c1; c += 4) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] += a.ccnt[((size_t)r * a.CR + c + u) * a.epr + l];
-  }
-  for (; c < c1; ++c) acc[0] += a.ccnt[((size_t)r * a.CR + c) * a.epr + l];
-  return acc[0] + acc[1] + acc[2] + acc[3];
-}
-
-// Threads are (expert, chunk group) pairs, G groups per expert (G a power of
-// two, G * E <= 1024 where possible); experts beyond one pass take more passes.
-__global__ __launch_bounds__(kOffThreads) void em_offsets_kernel(EmArgs a, int G) {
-  __shared__ int32_t part[kOffThreads];
-  __shared__ int32_t seg[kMaxExperts];
-  const int E = a.R * a.epr;
-  const int tid = threadIdx.x;
-  const int slots = kOffThreads / G;  // experts per pass
-  const int passes = (E + slots - 1) / slots;
-  // 1: rows per expert
-  for (int p = 0; p < passes; ++p) {
-    const int e = p * slots + tid / G, grp = tid % G;
-    int r = 0, l = 0, c0 = 0, c1 = 0;
-    if (e < E) group_chunks(a, e, grp, G, r, l, c0, c1);
-    part[tid] = e < E ? group_rows(a, r, l, c0, c1) : 0;
-    __syncthreads();
-    if (e < E && grp == 0) {
-      int n = 0;
-      for (int q = 0; q < G; ++q) n += part[tid + q];
-      seg[e] = n;
-    }
-    __syncthreads();
-  }
-  // 2: counts, segment sizes padded to 128 rows, exclusive scan over experts
-  for (int e = tid; e < E; e += kOffThreads) a.em_counts[e] = seg[e];
-  const int perT = (E + kOffThreads - 1) / kOffThreads;
-  const int lo = min(tid * perT, E), hi = min(lo + perT, E);
-  int sum = 0;
-  for (int e = lo; e < hi; ++e) sum += (seg[e] + 127) / 128 * 128;
-  __syncthreads();
-  part[tid] = sum;
-  __syncthreads();
-  for (int d = 1; d < kOffThreads; d <<= 1) {
-    const int v = tid >= d ? part[tid - d] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  int run = part[tid] - sum;
-  for (int e = lo; e < hi; ++e) {
-    const int n = seg[e];
-    seg[e] = run;  // now the segment offset
-    a.em_offsets[e] = run;
-    run += (n + 127) / 128 * 128;
-  }
-  if (tid == kOffThreads - 1) {
-    a.em_offsets[E] = part[tid];
-  }
-  __syncthreads();
-}
-
-// Rows of the same rank's earlier chunks that name local expert l: lane c'
-// loads chunk c''s count, then a wave reduction (chunks beyond 64 in steps).
-__device__ __forceinline__ int rows_before_chunk(const EmArgs& a, int r, int c, int l,
-                                                 int lane) {
-  int n = 0;
-  for (int c0 = 0; c0 < c; c0 += kWave) {
-    const int cc = c0 + lane;
-    if (cc < c) n += a.ccnt[((size_t)r * a.CR + cc) * a.epr + l];
-  }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) n += __shfl_xor(n, d);
-  return n;
-}
-
 template <int UPL>
 __global__ __launch_bounds__(256) void em_scatter_kernel(EmArgs a) {
+  extern __shared__ int32_t seg[];  // [E]: padded row counts, then segment offsets
   __shared__ int32_t prefix[kMaxRanks + 1];
-  const int lane = threadIdx.x & 63;
-  if (threadIdx.x < kWave) {  // rank prefix of the receive counts, one lane per rank
+  __shared__ int32_t wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int E = a.R * a.epr;
+  // the experts' padded row counts (consecutive experts per thread), loaded
+  // together with the receive counts
+  const int per = (E + 255) / 256;
+  const int e0 = min(tid * per, E), e1 = min(e0 + per, E);
+  for (int e = e0; e < e1; ++e) seg[e] = (a.em_counts[e] + 127) / 128 * 128;
+  if (w == 0) {  // rank prefix of the receive counts, one lane per rank
     const int n = lane < a.R ? clamp_count(a, lane) : 0;
     int inc = n;
 #pragma unroll
@@ -176,45 +139,75 @@ __global__ __launch_bounds__(256) void em_scatter_kernel(EmArgs a) {
     if (lane == 0) prefix[0] = 0;
   }
   __syncthreads();
-  const int g = first_lane(blockIdx.x * 4 + (threadIdx.x >> 6));
+
+  // this wave's receive row and slice; every load that does not need the
+  // segment offsets goes out before they are scanned
+  const int g = first_lane(blockIdx.x * 4 + w);
   const int u = g / a.slices, sl = g - u * a.slices;
-  if (u >= prefix[a.R]) return;
-  int lo = 0, hi = a.R;  // largest r with prefix[r] <= u (uniform)
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (prefix[mid] <= u) lo = mid; else hi = mid;
+  const bool live = u < prefix[a.R];
+  int r = 0;
+  if (live) {
+    int lo = 0, hi = a.R;  // largest r with prefix[r] <= u (uniform)
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (prefix[mid] <= u) lo = mid; else hi = mid;
+    }
+    r = lo;
   }
-  const int r = lo;
-  const int s = u - prefix[r];
+  const int s = live ? u - prefix[r] : 0;
   const int cnt = prefix[r + 1] - prefix[r];
   const size_t row = (size_t)r * a.cap + s;
   const int nv = a.row_units;  // 16-byte units per row
-  // row slice first: its loads do not depend on the placement
   const u32x4* src = reinterpret_cast<const u32x4*>(a.recv_x) + row * nv;
   u32x4 val[UPL];
 #pragma unroll
   for (int q = 0; q < UPL; ++q) {
     const int v = (sl * UPL + q) * kWave + lane;
-    val[q] = v < nv ? src[v] : u32x4{0, 0, 0, 0};
+    val[q] = live && v < nv ? src[v] : u32x4{0, 0, 0, 0};
   }
   const int c = s / kChunk, sc = s % kChunk;
   const int peer = c * kChunk + lane;
-  const uint64_t lm_lane = peer < cnt ? a.lmask[(size_t)r * a.cap + peer] : 0ull;
-  const uint64_t lm_self =
-      ((uint64_t)(uint32_t)lane_value((int)(uint32_t)lm_lane, sc)) |
-      ((uint64_t)(uint32_t)lane_value((int)(uint32_t)(lm_lane >> 32), sc) << 32);
+  const uint64_t lm_lane = live && peer < cnt ? a.lmask[(size_t)r * a.cap + peer] : 0ull;
+  // lane l: rows of the rank's earlier chunks naming local expert l
+  const int pre = live && lane < a.epr ? a.ccnt[((size_t)r * a.CR + c) * a.epr + lane] : 0;
   int pos_code = 0, t = -1, myid = -1;
-  if (sl == 0) {
+  if (live && sl == 0) {
     pos_code = a.spos[row];
     t = pos_code - a.spos_base;
     if (lane < a.k) myid = a.recv_idx[row * a.k + lane];
   }
+
+  // segment offsets: scan of the padded counts within the wave, then across
+  int sum = 0;
+  for (int e = e0; e < e1; ++e) sum += seg[e];
+  int inc = sum;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int v = __shfl_up(inc, d);
+    if (lane >= d) inc += v;
+  }
+  if (lane == kWave - 1) wsum[w] = inc;
+  __syncthreads();
+  int off = inc - sum;
+  for (int ww = 0; ww < w; ++ww) off += wsum[ww];
+  for (int e = e0; e < e1; ++e) {
+    const int n = seg[e];
+    seg[e] = off;
+    if (blockIdx.x == 0) a.em_offsets[e] = off;
+    off += n;
+  }
+  if (blockIdx.x == 0 && tid == 255) a.em_offsets[E] = off;
+  __syncthreads();
+  if (!live) return;
+
+  const uint64_t lm_self =
+      ((uint64_t)(uint32_t)lane_value((int)(uint32_t)lm_lane, sc)) |
+      ((uint64_t)(uint32_t)lane_value((int)(uint32_t)(lm_lane >> 32), sc) << 32);
   u32x4* dst_x = reinterpret_cast<u32x4*>(a.em_x);
   for (uint64_t m = lm_self; m; m &= m - 1) {
     const int l = __builtin_ctzll(m);
     const uint64_t b = ballot(lane < sc && ((lm_lane >> l) & 1ull));
-    const int64_t pos = (int64_t)a.em_offsets[r * a.epr + l] +
-                        rows_before_chunk(a, r, c, l, lane) + __popcll(b);
+    const int64_t pos = (int64_t)seg[r * a.epr + l] + lane_value(pre, l) + __popcll(b);
     if (pos >= a.cap_em) {
       if (lane == 0) atomicOr(a.status, (uint32_t)MEP_DEV_EM_OVERFLOW);
       continue;
@@ -242,24 +235,19 @@ __global__ __launch_bounds__(256) void em_scatter_kernel(EmArgs a) {
 
 hipError_t launch_to_expert_major(const EmArgs& a0, hipStream_t s) {
   EmArgs a = a0;
-  const int waves = a.R * a.CR;
-  em_count_kernel<<<(waves + 3) / 4, 256, 0, s>>>(a);
+  if (a.k <= 8) em_count_kernel<8><<<a.R, kCountWaves * 64, 0, s>>>(a);
+  else em_count_kernel<kMaxTopk><<<a.R, kCountWaves * 64, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int E = a.R * a.epr;
-  int G = 1;
-  while (G * 2 * E <= kOffThreads && G < 64) G *= 2;
-  em_offsets_kernel<<<1, kOffThreads, 0, s>>>(a, G);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // one wave per (receive row, kEmUnits x 64 units); rows <= T * min(k, R)
+  // one wave per (receive row, kEmUnits x 64 units); rows <= T * min(k, R);
+  // at least one workgroup, which writes the segment offsets
   const int nv = a.row_units;
   const int per = kEmUnitsPerLane * kWave;
   a.slices = (nv + per - 1) / per;
   const int64_t rows = (int64_t)a.T * std::min(a.k, a.R);
-  const int64_t waves2 = rows * a.slices;
-  if (waves2 == 0) return hipSuccess;
-  em_scatter_kernel<kEmUnitsPerLane><<<(unsigned)((waves2 + 3) / 4), 256, 0, s>>>(a);
+  const int64_t waves = std::max<int64_t>(rows * a.slices, 1);
+  const size_t lds = (size_t)a.R * a.epr * sizeof(int32_t);
+  em_scatter_kernel<kEmUnitsPerLane><<<(unsigned)((waves + 3) / 4), 256, lds, s>>>(a);
   return hipGetLastError();
 }
 
