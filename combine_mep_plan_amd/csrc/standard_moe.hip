@@ -182,25 +182,33 @@ __host__ __device__ constexpr size_t route_lds_bytes(int E, bool fused) {
 template <int KMAX, bool FUSED>
 __global__ __launch_bounds__(kRouteThreads) void sm_route_kernel(SmArgs a) {
   extern __shared__ __align__(8) unsigned char smem[];
-  __shared__ int32_t part[kRouteThreads];
+  __shared__ int32_t wsum[kRouteThreads / kWave];
   const int E = a.E;
   uint64_t* mask = reinterpret_cast<uint64_t*>(smem);  // tokens of the chunk naming e
   int32_t* base = reinterpret_cast<int32_t*>(mask + E);  // first row of the chunk for e
   int32_t* pad = base + E;
-  const int tid = threadIdx.x, c = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = blockIdx.x;
   const int C = (a.T + kChunk - 1) / kChunk;
+  // the chunk's tokens, one per lane of the first wave; their ids go out first
+  const int t = c * kChunk + lane;
+  const bool mine = tid < kWave && t < a.T;
+  int ids[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) ids[j] = -1;
+  const bool valid = mine && load_ids<KMAX>(a, t, ids);
   const int32_t* hist = a.chunk_hist;
   if (FUSED) {
     // per expert: total over all chunks and prefix over the chunks before c
+    // (16 independent loads in flight per thread)
     for (int e = tid; e < E; e += kRouteThreads) {
       int tot = 0, pre = 0;
       int cc = 0;
-      for (; cc + 8 <= C; cc += 8) {
-        int v[8];
+      for (; cc + 16 <= C; cc += 16) {
+        int v[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = hist[(size_t)(cc + u) * E + e];
+        for (int u = 0; u < 16; ++u) v[u] = hist[(size_t)(cc + u) * E + e];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u) {
           tot += v[u];
           pre += cc + u < c ? v[u] : 0;
         }
@@ -216,26 +224,28 @@ __global__ __launch_bounds__(kRouteThreads) void sm_route_kernel(SmArgs a) {
       mask[e] = 0ull;
     }
     __syncthreads();
-    // padded totals scanned into segment offsets, consecutive experts per thread
+    // padded totals scanned into segment offsets, consecutive experts per
+    // thread: within the wave by shuffles, then across the waves
     const int per = (E + kRouteThreads - 1) / kRouteThreads;
     const int lo = min(tid * per, E), hi = min(lo + per, E);
     int sum = 0;
     for (int e = lo; e < hi; ++e) sum += pad[e];
-    part[tid] = sum;
-    __syncthreads();
-    for (int d = 1; d < kRouteThreads; d <<= 1) {
-      const int v = tid >= d ? part[tid - d] : 0;
-      __syncthreads();
-      part[tid] += v;
-      __syncthreads();
+    int inc = sum;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int v = __shfl_up(inc, d);
+      if (lane >= d) inc += v;
     }
-    int off = part[tid] - sum;
+    if (lane == kWave - 1) wsum[w] = inc;
+    __syncthreads();
+    int off = inc - sum;
+    for (int ww = 0; ww < w; ++ww) off += wsum[ww];
     for (int e = lo; e < hi; ++e) {
       if (c == 0) a.em_offsets[e] = off;
       base[e] += off;
       off += pad[e];
     }
-    if (c == 0 && tid == kRouteThreads - 1) a.em_offsets[E] = part[tid];
+    if (c == 0 && tid == kRouteThreads - 1) a.em_offsets[E] = off;
   } else {
     // prefixes and offsets from the offsets workgroup
     for (int e = tid; e < E; e += kRouteThreads) {
@@ -244,15 +254,8 @@ __global__ __launch_bounds__(kRouteThreads) void sm_route_kernel(SmArgs a) {
     }
   }
   __syncthreads();
-  // the chunk's tokens, one per lane of the first wave
-  const int lane = tid;
-  const int t = c * kChunk + lane;
-  const bool mine = tid < kWave && t < a.T;
-  int ids[KMAX];
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) ids[j] = -1;
   uint32_t firsts = 0;  // top-k positions that own a row
-  if (mine && load_ids<KMAX>(a, t, ids)) {
+  if (valid) {
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       if (j >= a.k) continue;
