@@ -9,12 +9,18 @@
 // multiply-add per top-k position in order j = 0..k-1, then bf16 round to
 // nearest even -- a fixed order, so the result does not depend on timing.
 //
-// A row is cut into slices of 2 x 16 bytes per lane (2 KiB per wave); one wave
-// handles one (token, slice), so a 4096-token batch runs ~29k short waves.
-// Up to top-8, each distinct expert-output row is loaded once (positions that
-// share a rank row reuse its registers) with non-temporal loads -- the rows
-// are read exactly once -- and all of a slice's loads are issued before the
-// FMAs.  Wider top-k takes the positions in groups of 8 (see below).
+// Up to top-8 a row is cut into slices of 16 bytes per lane (1 KiB per wave)
+// and one workgroup takes one token, a wave per slice (14 waves at 7168
+// columns; rows wider than 16 KiB split over as few workgroups as possible):
+// the pieces of each row the token gathers are then fetched together by one
+// CU.  At 4096 x 7168 on 8 ranks the combine took 60.7 us this way, against
+// 63.8 us with 2 KiB per wave and four waves per workgroup (tokens cut across
+// workgroups) and 164 us with 1 KiB per wave in four-wave workgroups.  Each
+// distinct expert-output row is loaded once (positions that share a rank row
+// reuse its registers) with non-temporal loads -- the rows are read exactly
+// once -- and all of a slice's loads are issued before the FMAs.  Wider
+// top-k takes the positions in groups of 8, 2 KiB per wave (see below), and
+// so does the E4M3 rounding in flight.
 //
 // Converted rank rows ("MORI-EP User Guide", section 4 convert_combine_input():
 // each row already holds its rank's weighted expert outputs): the same kernel
@@ -39,7 +45,12 @@ namespace mep {
 
 namespace {
 
-constexpr int kUnitsPerLane = 2;
+constexpr int kUnitsPerLane = 2;   // beyond top-8: 2 KiB of each row per wave
+constexpr int kMaxWavesPerWg = 16;  // 1024 threads
+// The E4M3 rounding in flight converts every loaded value, so its waves stay
+// busy longer after their loads: 2 KiB per wave keeps more bytes in flight
+// (prefill step with it 114.5 us against 118.8 us with 1 KiB).
+constexpr int kRoundUnitsPerLane = 2;
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
@@ -70,12 +81,13 @@ __device__ __forceinline__ void round_e4m3_unit(u32x4& x) {
 // SUM: the rows are converted rank rows that already carry the weights; each
 // token's distinct rank rows (the positions owning them) are added with unit
 // weight -- fmaf(1, y, acc) is acc + y with one rounding.
-template <int KMAX, bool DEDUPE, bool ROUND, bool SUM = false>
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+template <int KMAX, bool DEDUPE, bool ROUND, bool SUM = false, int UPL = 1>
+__global__ __launch_bounds__(kMaxWavesPerWg * 64) void combine_kernel(CombineArgs a) {
+  constexpr int kUnitsPerLane = UPL;
   const int lane = threadIdx.x & 63;
-  const int g = first_lane(blockIdx.x * 4 + (threadIdx.x >> 6));
-  const int t = g / a.slices, sl = g - t * a.slices;
-  if (t >= a.T) return;
+  const int t = blockIdx.x / a.wg_per_tok;
+  const int sl = (blockIdx.x - t * a.wg_per_tok) * a.waves_per_wg + first_lane(threadIdx.x >> 6);
+  if (t >= a.T || sl >= a.slices) return;
   const int nv = a.H / 8;
   const uint32_t own = SUM ? a.ufirst[t] : 0xFFFFFFFFu;
   int row[KMAX];
@@ -425,28 +437,41 @@ __global__ __launch_bounds__(256) void cast_fp8_kernel(CastArgs a) {
 hipError_t launch_combine(const CombineArgs& a0, hipStream_t s) {
   if (a0.T == 0) return hipSuccess;
   CombineArgs a = a0;
-  const int per = kWave * kUnitsPerLane;
-  a.slice_units = per;
-  a.slices = (a.H / 8 + per - 1) / per;
-  const int blocks = (int)(((int64_t)a.T * a.slices + 3) / 4);
-  const bool dedupe = !a.distinct_rows;
-  if (a.sum_rows) {  // converted rank rows: the owning positions' rows are distinct
-    if (a.k > 8) combine_wide_kernel<false, false, true><<<blocks, 256, 0, s>>>(a);
-    else combine_kernel<8, false, false, true><<<blocks, 256, 0, s>>>(a);
-  } else if (a.k > 8) {
-    if (a.round_e4m3) {
+  if (a.k > 8) {  // groups of 8 positions, 2 KiB per wave, four waves per workgroup
+    const int per = kWave * kUnitsPerLane;
+    a.slice_units = per;
+    a.slices = (a.H / 8 + per - 1) / per;
+    const int blocks = (int)(((int64_t)a.T * a.slices + 3) / 4);
+    const bool dedupe = !a.distinct_rows && !a.sum_rows;
+    if (a.sum_rows) combine_wide_kernel<false, false, true><<<blocks, 256, 0, s>>>(a);
+    else if (a.round_e4m3) {
       if (dedupe) combine_wide_kernel<true, true><<<blocks, 256, 0, s>>>(a);
       else combine_wide_kernel<false, true><<<blocks, 256, 0, s>>>(a);
     } else {
       if (dedupe) combine_wide_kernel<true, false><<<blocks, 256, 0, s>>>(a);
       else combine_wide_kernel<false, false><<<blocks, 256, 0, s>>>(a);
     }
-  } else if (a.round_e4m3) {
-    if (dedupe) combine_kernel<8, true, true><<<blocks, 256, 0, s>>>(a);
-    else combine_kernel<8, false, true><<<blocks, 256, 0, s>>>(a);
+    return hipGetLastError();
+  }
+  // 1 KiB per wave (2 KiB with the E4M3 rounding); a token's waves in as few
+  // workgroups as possible
+  const int upl = a.round_e4m3 ? kRoundUnitsPerLane : 1;
+  a.slice_units = kWave * upl;
+  a.slices = (a.H / 8 + a.slice_units - 1) / a.slice_units;
+  a.wg_per_tok = (a.slices + kMaxWavesPerWg - 1) / kMaxWavesPerWg;
+  a.waves_per_wg = (a.slices + a.wg_per_tok - 1) / a.wg_per_tok;
+  const int64_t blocks = (int64_t)a.T * a.wg_per_tok;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks), block((unsigned)(kWave * a.waves_per_wg));
+  const bool dedupe = !a.distinct_rows;
+  if (a.sum_rows)  // converted rank rows: the owning positions' rows are distinct
+    combine_kernel<8, false, false, true><<<grid, block, 0, s>>>(a);
+  else if (a.round_e4m3) {
+    if (dedupe) combine_kernel<8, true, true, false, kRoundUnitsPerLane><<<grid, block, 0, s>>>(a);
+    else combine_kernel<8, false, true, false, kRoundUnitsPerLane><<<grid, block, 0, s>>>(a);
   } else {
-    if (dedupe) combine_kernel<8, true, false><<<blocks, 256, 0, s>>>(a);
-    else combine_kernel<8, false, false><<<blocks, 256, 0, s>>>(a);
+    if (dedupe) combine_kernel<8, true, false><<<grid, block, 0, s>>>(a);
+    else combine_kernel<8, false, false><<<grid, block, 0, s>>>(a);
   }
   return hipGetLastError();
 }
