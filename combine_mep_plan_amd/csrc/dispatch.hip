@@ -57,21 +57,25 @@ __device__ __forceinline__ WaveRoute wave_route(const DispatchArgs& a, int t, in
   const int tok = c * kChunk + lane;
   w.base = 0;
   if (MODE == kCounts) {
-    // the chunk's in-block prefix and the first four earlier blocks' totals go
+    // the chunk's in-block prefix and the first 16 earlier blocks' totals go
     // out together with the mask load (a rolled loop would wait on each);
-    // blocks past the fourth (batches over 4096 tokens) are summed after
-    const int nb = c / 16;
-    int acc = 0, v[4] = {0, 0, 0, 0};
+    // blocks past the 16th (batches over 16384 tokens) are summed after
+    const int nb = c / a.blk_chunks;
+    int acc = 0, v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q] = 0;
     if (lane < a.R) {
       acc = a.chunk_cnt[(size_t)c * a.R + lane];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < 16; ++q)
         if (q < nb) v[q] = a.block_cnt[(size_t)q * a.R + lane];
     }
     w.mask_l = tok < a.T ? a.mask[tok] : 0ull;
     if (lane < a.R) {
-      for (int b = 4; b < nb; ++b) acc += a.block_cnt[(size_t)b * a.R + lane];
-      w.base = acc + v[0] + v[1] + v[2] + v[3];
+      for (int b = 16; b < nb; ++b) acc += a.block_cnt[(size_t)b * a.R + lane];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc += v[q];
+      w.base = acc;
     }
   } else if (KMAX <= 8) {
     // the token's chunk and the (at most three) earlier chunks: every id load
@@ -270,9 +274,13 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
 hipError_t launch_plan_dispatch(const PlanArgs& p, const DispatchArgs& a, hipStream_t s) {
   if (a.T == 0) return launch_plan(p, s);
   if (a.T <= kInlinePlanTokens) return launch_dtype<kInline>(a, s);
-  hipError_t e = launch_plan_counts(p, s);
+  const int C = (a.T + kChunk - 1) / kChunk;
+  PlanArgs pc = p;
+  DispatchArgs ac = a;
+  pc.blk_chunks = ac.blk_chunks = count_block_chunks(C);
+  hipError_t e = launch_plan_counts(pc, s);
   if (e != hipSuccess) return e;
-  return launch_dtype<kCounts>(a, s);
+  return launch_dtype<kCounts>(ac, s);
 }
 
 }  // namespace mep

@@ -38,7 +38,7 @@ WsLayout ws_layout(const mep_config& c) {
   L.status = take(3 * sizeof(uint32_t));
   L.tok_status = take(cap);
   L.chunk_cnt = take(C * R * sizeof(int32_t));
-  L.block_cnt = take((C + 15) / 16 * R * sizeof(int32_t));
+  L.block_cnt = take((C + mep::kMinBlockChunks - 1) / mep::kMinBlockChunks * R * sizeof(int32_t));
   L.mask = take(cap * sizeof(uint64_t));
   L.rrow = take(cap * k * sizeof(int32_t));
   L.ufirst = take(cap * sizeof(uint32_t));

@@ -16,6 +16,15 @@ constexpr int kMaxTopk = 32;     // first-occurrence bits of a token fit 32 bits
 constexpr int kMaxEpr = 64;      // a row's local experts fit one 64-bit mask
 constexpr int kChunk = 64;       // tokens (or receive rows) per scan chunk = one wave
 
+// Chunks per block of the plan's count launch for a batch of C chunks: small
+// blocks (4 chunks, 256 threads) start and finish sooner, but every later
+// chunk sums the totals of all earlier blocks, so batches over 64 chunks
+// (4096 tokens) take blocks of 16 chunks; either way a batch of up to 16384
+// tokens has at most 16 earlier blocks.  The workspace holds blocks of the
+// smaller size.
+__host__ __device__ constexpr int count_block_chunks(int C) { return C <= 64 ? 4 : 16; }
+constexpr int kMinBlockChunks = 4;
+
 // 16-byte units per received row of a payload mode: 8 bf16 values, 16 E4M3
 // codes or 32 packed E2M1 codes per unit.
 __host__ __device__ constexpr int payload_units(int quant, int H) {
@@ -70,6 +79,7 @@ struct PlanArgs {
   uint32_t* ufirst;
   int32_t T, k, R, E, cap, spos_base;  // spos_base = rank * R * cap
   RankDiv rdiv;
+  int32_t blk_chunks;  // chunks per count block (count_block_chunks), set at launch
 };
 
 struct DispatchArgs {
@@ -95,6 +105,7 @@ struct DispatchArgs {
   int32_t T, H, k, R, E, cap, spos_base;
   int32_t quant, scale_dim;
   RankDiv rdiv;
+  int32_t blk_chunks;      // fused: chunks per count block (count_block_chunks)
   int32_t slices, slice_units;  // waves per token and 16-byte lane units per wave
 };
 

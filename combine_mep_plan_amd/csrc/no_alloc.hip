@@ -58,7 +58,7 @@ ScratchLayout scratch_layout(int64_t T, int64_t k, int64_t R) {
   };
   L.status = take(2 * sizeof(uint32_t));
   L.chunk_cnt = take((size_t)(C * R) * sizeof(int32_t));
-  L.block_cnt = take((size_t)((C + 15) / 16 * R) * sizeof(int32_t));
+  L.block_cnt = take((size_t)((C + mep::kMinBlockChunks - 1) / mep::kMinBlockChunks * R) * sizeof(int32_t));
   L.mask = take((size_t)T * sizeof(uint64_t));
   L.rrow = take((size_t)(T * k) * sizeof(int32_t));
   L.ufirst = take((size_t)T * sizeof(uint32_t));

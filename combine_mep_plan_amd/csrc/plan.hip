@@ -17,17 +17,18 @@
 // top-k entries with one LDS read and a popcount -- no per-rank loop per lane.
 //
 // The per-rank base of a chunk is the exclusive prefix over earlier chunks,
-// built in two levels: inside a 16-chunk block through LDS, across blocks by
-// summing block totals.  Up to 1024 tokens one workgroup does everything in a
-// single launch; beyond that, a count launch writes the block-level prefixes
-// and a slot launch (one wave per chunk) finishes.
+// built in two levels: inside a block of chunks (4 up to 4096 tokens, 16
+// beyond) through LDS, across blocks by summing block totals.  Up to 1024
+// tokens one workgroup does everything in a single launch; beyond that, a
+// count launch writes the block-level prefixes and a slot launch (one wave per
+// chunk) finishes.
 #include "route.h"
 
 namespace mep {
 
 namespace {
 
-constexpr int kBlockChunks = 16;  // chunks (waves) per count block
+constexpr int kBlockChunks = 16;  // chunks (waves) of the single-workgroup plan; most per count block
 
 // Slot phase for one chunk.  `base` in lane r is the number of rows rank r got
 // from all earlier tokens.  bal/bas are this wave's LDS scratch (64 entries).
@@ -100,14 +101,15 @@ __global__ __launch_bounds__(1024) void plan_single_kernel(PlanArgs a) {
   if (w * kChunk < a.T) chunk_slots<KMAX>(a, w, lane, base, ids, mask, bal[w], bas[w]);
 }
 
-// Count launch: per 16-chunk block, the exclusive prefix of every chunk inside
-// the block (chunk_cnt[c][r]) and the block totals (block_cnt[b][r]).
+// Count launch: per block of a.blk_chunks chunks (one wave each), the exclusive
+// prefix of every chunk inside the block (chunk_cnt[c][r]) and the block
+// totals (block_cnt[b][r]).
 template <int KMAX>
 __global__ __launch_bounds__(1024) void plan_count_kernel(PlanArgs a) {
   __shared__ int cnt[kBlockChunks][kMaxRanks];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int b = blockIdx.x;
-  const int c = b * kBlockChunks + w;
+  const int c = b * a.blk_chunks + w;
   const int C = (a.T + kChunk - 1) / kChunk;
   if (b == 0 && threadIdx.x == 0) *a.status_next = 0u;
   const int t = c * kChunk + lane;
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(1024) void plan_count_kernel(PlanArgs a) {
     int pre = 0;
     for (int ww = 0; ww < w; ++ww) pre += cnt[ww][lane];
     if (c < C) a.chunk_cnt[(size_t)c * a.R + lane] = pre;
-    if (w == kBlockChunks - 1) a.block_cnt[(size_t)b * a.R + lane] = pre + mine;
+    if (w == a.blk_chunks - 1) a.block_cnt[(size_t)b * a.R + lane] = pre + mine;
   }
 }
 
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(256) void plan_slot_kernel(PlanArgs a) {
   const int c = blockIdx.x * 4 + w;
   const int C = (a.T + kChunk - 1) / kChunk;
   if (c >= C) return;  // whole wave; no block barrier below
-  const int b = c / kBlockChunks;
+  const int b = c / a.blk_chunks;
   int base = 0;
   if (lane < a.R) {
     base = a.chunk_cnt[(size_t)c * a.R + lane];
@@ -182,9 +184,11 @@ hipError_t launch_plan_k(const PlanArgs& a, hipStream_t s) {
     plan_single_kernel<KMAX><<<1, 1024, 0, s>>>(a);
     return hipGetLastError();
   }
-  hipError_t e = launch_plan_counts(a, s);
+  PlanArgs b = a;
+  b.blk_chunks = count_block_chunks(C);
+  hipError_t e = launch_plan_counts(b, s);
   if (e != hipSuccess) return e;
-  plan_slot_kernel<KMAX><<<(C + 3) / 4, 256, 0, s>>>(a);
+  plan_slot_kernel<KMAX><<<(C + 3) / 4, 256, 0, s>>>(b);
   return hipGetLastError();
 }
 
@@ -192,9 +196,11 @@ hipError_t launch_plan_k(const PlanArgs& a, hipStream_t s) {
 
 hipError_t launch_plan_counts(const PlanArgs& a, hipStream_t s) {
   const int C = (a.T + kChunk - 1) / kChunk;
-  const int B = (C + kBlockChunks - 1) / kBlockChunks;
-  if (a.k <= 8) plan_count_kernel<8><<<B, 1024, 0, s>>>(a);
-  else plan_count_kernel<kMaxTopk><<<B, 1024, 0, s>>>(a);
+  const int n = a.blk_chunks;
+  if (n != count_block_chunks(C)) return hipErrorInvalidValue;
+  const int B = (C + n - 1) / n;
+  if (a.k <= 8) plan_count_kernel<8><<<B, 64 * n, 0, s>>>(a);
+  else plan_count_kernel<kMaxTopk><<<B, 64 * n, 0, s>>>(a);
   return hipGetLastError();
 }
 
