@@ -326,10 +326,12 @@ def test_fused_plan_dispatch_64_ranks(T):
     assert M.mep_get_status(g.m.h) == 0
 
 
-@pytest.mark.parametrize("T,R", [(5200, 8), (9000, 8), (8193, 33)])
+@pytest.mark.parametrize("T,R", [(4097, 8), (5200, 8), (9000, 8), (8193, 33), (20000, 8)])
 def test_fused_plan_dispatch_long_batches(T, R):
-    # more than four 16-chunk count blocks before a token's chunk (the per-wave
-    # base sums the later blocks after the first four)
+    # past 4096 tokens the count blocks hold 16 chunks instead of 4 (4097: the
+    # first such batch); past 16384 tokens a token's chunk has more than the
+    # 16 earlier block totals a dispatch wave loads with its mask, and sums
+    # the rest after (20000 tokens: up to 19 earlier blocks)
     wl = Workload("long", T, 256, R, 4, 8, T, "fp8", "uniform", "dequant_half", "rank_major")
     inp = make_inputs(wl, 2)
     for fused in (True, False):
