@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kCountWaves * 64) void em_count_kernel(EmArgs a) {
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {
           const int e = ids[q][j];
-          if (j < a.k && e >= 0 && e < E && e / a.epr == r) lm |= 1ull << (e - r * a.epr);
+          if (j < a.k && e >= 0 && e < E && (int)a.rdiv((uint32_t)e) == r) lm |= 1ull << (e - r * a.epr);
         }
         a.lmask[(size_t)r * a.cap + s] = lm;
       }

@@ -442,6 +442,7 @@ int mep_to_expert_major(mep_handle* h, const void* recv_x, const float* recv_sca
   a.H = c.hidden_dim;
   a.k = c.num_experts_per_token;
   a.R = c.world_size;
+  a.rdiv = h->rdiv;
   a.epr = c.num_experts_per_rank;
   a.cap = c.max_num_inp_token_per_rank;
   a.CR = (c.max_num_inp_token_per_rank + mep::kChunk - 1) / mep::kChunk;

@@ -51,8 +51,8 @@ struct WsLayout {
   size_t status;     // uint32 [3]: sticky MEP_DEV_* bits, one word per reset epoch [0, 1];
                      // the expert-major overflow word of captured iterations [2]
   size_t tok_status; // uint8 [cap]: bad/repeated-id bits of each token of a captured plan
-  size_t chunk_cnt;  // int32 [C][R]: rows earlier chunks of the same 16-chunk block send to each rank
-  size_t block_cnt;  // int32 [ceil(C/16)][R]: rows each 16-chunk block sends to each rank
+  size_t chunk_cnt;  // int32 [C][R]: rows earlier chunks of the same count block send to each rank
+  size_t block_cnt;  // int32 [ceil(C/4)][R]: rows each count block (4 or 16 chunks) sends to each rank
   size_t mask;       // uint64 [cap]: destination-rank mask of each token (0 = dropped)
   size_t rrow;       // int32 [cap][k]: flat receive row r*cap+slot of (t, j), -1 if dropped
   size_t ufirst;     // uint32 [cap]: bit j set when top-k position j owns its rank's row
@@ -160,6 +160,7 @@ struct EmArgs {
   uint64_t* lmask;              // [R*cap]
   int32_t* ccnt;                // [R][CR][epr]
   uint32_t* status;
+  RankDiv rdiv;                 // expert id -> rank
   int64_t cap_em;
   int32_t T, H, k, R, epr, cap, CR, nb, row_units, spos_base;  // row_units: 16-byte units per row
   int32_t slices;  // scatter: waves per receive row
