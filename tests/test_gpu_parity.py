@@ -285,8 +285,8 @@ def test_expert_major_overflow_sets_status():
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025, 2049, 3000])
 def test_plan_block_boundaries(T, fused):
     # mep_plan: one workgroup up to 1024 tokens, else count + slot launches split
-    # at 16-chunk blocks; fused: one launch up to 256 tokens, else count +
-    # dispatch launches
+    # into count blocks of 4 chunks (256 tokens; 16 chunks above 4096 tokens);
+    # fused: one launch up to 256 tokens, else count + dispatch launches
     wl = _variant("skew", tokens=T, cap=3072, hidden=256)
     inp = make_inputs(wl, T)
     g = gpu_plan_dispatch(wl, inp, src_rank=3, fused=fused)
