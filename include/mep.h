@@ -200,9 +200,10 @@ int mep_plan_dispatch(mep_handle *h, const int32_t *indices, int32_t T, int32_t 
  * host-side checks) with no handle and no workspace.  The plan's scratch is a
  * 2 MiB device array inside the library, one per GPU, held until the process
  * ends; its address on the stream's GPU is looked up on the first call there
- * (hipGetSymbolAddress, no allocation).  The batch must fit it: about
- * 183 KiB for 4096 tokens at top-8 on 8 ranks, roughly
- * T*(12 + 4k) + (T/64)*R*4 bytes in general; MEP_ERR_SHAPE beyond 2 MiB
+ * (hipGetSymbolAddress, no allocation).  The batch must fit it: 179 KiB
+ * for 4096 tokens at top-8 on 8 ranks, roughly T*(12 + 4k) + (T/64)*R*5
+ * bytes in general (each section rounded up to 256 bytes); MEP_ERR_SHAPE
+ * beyond 2 MiB
  * (no launch).  Every call on one GPU shares that scratch, so calls that
  * overlap on one GPU (concurrent streams, or threads) race; calls ordered on
  * one stream do not.  Tokens with bad expert ids are not dispatched, as in
