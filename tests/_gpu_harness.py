@@ -53,7 +53,7 @@ def alloc_recv(wl: Workload):
 
 
 @dataclasses.dataclass
-class GpuRun:
+class GpuResult:
     m: M.Mep
     x: torch.Tensor
     w: torch.Tensor
@@ -67,7 +67,7 @@ class GpuRun:
     route: torch.Tensor
 
 
-def gpu_plan_dispatch(wl: Workload, inp: dict, src_rank: int = 0, fused: bool = False) -> GpuRun:
+def gpu_plan_dispatch(wl: Workload, inp: dict, src_rank: int = 0, fused: bool = False) -> GpuResult:
     """Plan + dispatch through the C ABI: mep_plan then mep_dispatch, or the
     fused mep_plan_dispatch."""
     T = inp["indices"].shape[0]
@@ -85,7 +85,7 @@ def gpu_plan_dispatch(wl: Workload, inp: dict, src_rank: int = 0, fused: bool = 
     route = torch.full((max(T, 1), wl.topk), SENT32, dtype=torch.int32, device="cuda")
     M.mep_get_route(m.h, route)
     torch.cuda.synchronize()
-    return GpuRun(m, x, w, idx, counts, spos, recv_x, recv_s, recv_w, recv_i, route[:T])
+    return GpuResult(m, x, w, idx, counts, spos, recv_x, recv_s, recv_w, recv_i, route[:T])
 
 
 def oracle_plan_dispatch(wl: Workload, inp: dict, src_rank: int = 0):
@@ -100,7 +100,7 @@ def expected_route(wl: Workload, inp: dict, pl: dict) -> np.ndarray:
     return np.where(pl["slot"] >= 0, r * wl.cap + pl["slot"], -1).astype(np.int32)
 
 
-def check_plan_dispatch(wl: Workload, inp: dict, g: GpuRun, pl: dict, d: dict) -> None:
+def check_plan_dispatch(wl: Workload, inp: dict, g: GpuResult, pl: dict, d: dict) -> None:
     """Bit-exact comparison of counts, src_token_pos, route, and every written
     receive row; unwritten rows must still hold the sentinel."""
     R, cap = wl.ranks, wl.cap

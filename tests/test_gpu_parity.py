@@ -21,7 +21,7 @@ import combine_mep_plan_amd as M
 from oracle import oracle as O
 from synthetic import WORKLOADS, Workload, make_inputs
 
-from _gpu_harness import (SENT8, SENT32, GpuRun, alloc_recv, bf16_ulp_diff, check_combine,
+from _gpu_harness import (SENT8, SENT32, GpuResult, alloc_recv, bf16_ulp_diff, check_combine,
                           check_expert_major, check_plan_dispatch, dev, gpu_plan_dispatch, host,
                           oracle_plan_dispatch, run_full, stand_in_oracle)
 
@@ -362,7 +362,7 @@ def test_fused_plan_dispatch_repeated(R):
         route = torch.full((T, wl.topk), SENT32, dtype=torch.int32, device="cuda")
         M.mep_get_route(m.h, route)
         torch.cuda.synchronize()
-        g = GpuRun(m, x, w, idx, counts, spos, *recv, route)
+        g = GpuResult(m, x, w, idx, counts, spos, *recv, route)
         pl, d = oracle_plan_dispatch(wl, inp, src_rank=src)
         _say(f"R={R} call {i} T={T}")
         check_plan_dispatch(wl, inp, g, pl, d)

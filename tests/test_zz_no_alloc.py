@@ -12,7 +12,7 @@ import torch
 import combine_mep_plan_amd as M
 from synthetic import Workload, make_inputs
 
-from _gpu_harness import (GpuRun, alloc_recv, check_plan_dispatch, dev, gpu_plan_dispatch, host,
+from _gpu_harness import (GpuResult, alloc_recv, check_plan_dispatch, dev, gpu_plan_dispatch, host,
                           oracle_plan_dispatch)
 
 pytestmark = pytest.mark.gpu
