@@ -303,7 +303,7 @@ __global__ __launch_bounds__(256) void sm_scatter_kernel(SmArgs a) {
   const int v = sl * kWave + lane;
   const bool on = v < nu;
   Unit<QUANT> unit;
-  unit.load(a.x, t, a.H, v, on);
+  unit.template load<true>(a.x, t, a.H, v, on);
   // the token's rows, placed by the route launch (-1: no row)
   int rows[KMAX];
   const int32_t* rr = a.em_row + (size_t)t * a.k;
