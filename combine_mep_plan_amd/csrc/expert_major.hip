@@ -171,10 +171,12 @@ __global__ __launch_bounds__(256) void em_scatter_kernel(EmArgs a) {
   // lane l: rows of the rank's earlier chunks naming local expert l
   const int pre = live && lane < a.epr ? a.ccnt[((size_t)r * a.CR + c) * a.epr + lane] : 0;
   int pos_code = 0, t = -1, myid = -1;
+  float scw = 0.0f;  // the row's first 64 scale words, one per lane
   if (live && sl == 0) {
     pos_code = a.spos[row];
     t = pos_code - a.spos_base;
     if (lane < a.k) myid = a.recv_idx[row * a.k + lane];
+    if (lane < a.nb) scw = a.recv_scales[row * a.nb + lane];
   }
 
   // segment offsets: scan of the padded counts within the wave, then across
@@ -217,9 +219,11 @@ __global__ __launch_bounds__(256) void em_scatter_kernel(EmArgs a) {
       const int v = (sl * UPL + q) * kWave + lane;
       if (v < nv) store_nt(dst_x + (size_t)pos * nv + v, val[q]);
     }
-    if (sl == 0)  // the row's scale columns, one per lane
-      for (int i = lane; i < a.nb; i += kWave)
+    if (sl == 0) {  // the row's scale columns, one per lane
+      if (lane < a.nb) a.em_scales[(size_t)pos * a.nb + lane] = scw;
+      for (int i = lane + kWave; i < a.nb; i += kWave)  // rows over 64 words
         a.em_scales[(size_t)pos * a.nb + i] = a.recv_scales[row * a.nb + i];
+    }
     if (sl == 0) {
       const int e = r * a.epr + l;
       const uint64_t hit = ballot(myid == e);  // top-k position naming e
