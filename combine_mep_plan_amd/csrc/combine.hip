@@ -389,21 +389,27 @@ __global__ __launch_bounds__(256) void combine_fp8_wide_kernel(CombineArgs a) {
   store_nt(out + 1, o1);
 }
 
-// One wave per (token, slice); the token's distinct rows in groups of 8, all
-// loads of a group issued before its converts.
+// One wave per (token, 1 KiB of E4M3 output per row); the token's distinct
+// rows in groups of 8, all loads of a group issued before its converts.  The
+// cast has no blocks, so any column may go to any lane: lane l takes 8-column
+// units l and l + 64 of the wave's 128, which makes every load (1 KiB) and
+// every store (512 bytes) contiguous across the wave.  With each lane's 16
+// columns adjacent instead (32-byte strided loads and stores) the cast took
+// 89.7 us at 4096 x 7168 on 8 ranks against 84.8 us.
 template <bool RANK_MAJOR>
 __global__ __launch_bounds__(256) void cast_fp8_kernel(CastArgs a) {
   constexpr int G = 8;
+  typedef uint32_t u32x2c __attribute__((ext_vector_type(2)));
   const int lane = threadIdx.x & 63;
   const int g = first_lane(blockIdx.x * 4 + (threadIdx.x >> 6));
   const int t = g / a.slices, sl = g - t * a.slices;
   if (t >= a.T) return;
-  const int nv8 = a.H / 16, nv = a.H / 8;
-  const int v = sl * kWave + lane;
-  const bool on = v < nv8;
+  const int nv = a.H / 8;  // 16-byte bf16 units per row (8 columns each)
+  const int u0 = sl * 128 + lane, u1 = u0 + 64;  // this lane's two units
+  const bool on0 = u0 < nv, on1 = u1 < nv;
   const uint32_t own = RANK_MAJOR ? a.ufirst[t] : 0xFFFFFFFFu;  // uniform
   const u32x4* y = reinterpret_cast<const u32x4*>(a.y);
-  u32x4* y8 = reinterpret_cast<u32x4*>(a.y8);
+  u32x2c* y8 = reinterpret_cast<u32x2c*>(a.y8);  // 8-byte units: 8 E4M3 columns
   for (int j0 = 0; j0 < a.k; j0 += G) {
     int row[G];
     u32x4 in[G][2];
@@ -412,22 +418,25 @@ __global__ __launch_bounds__(256) void cast_fp8_kernel(CastArgs a) {
       const int j = j0 + u;
       row[u] = (j < a.k && (own >> j & 1u)) ? a.rows[(size_t)t * a.k + j] : -1;
       in[u][0] = in[u][1] = u32x4{0, 0, 0, 0};
-      if (row[u] >= 0 && on) {
-        in[u][0] = __builtin_nontemporal_load(y + (size_t)row[u] * nv + 2 * v);
-        in[u][1] = __builtin_nontemporal_load(y + (size_t)row[u] * nv + 2 * v + 1);
+      if (row[u] >= 0) {
+        if (on0) in[u][0] = __builtin_nontemporal_load(y + (size_t)row[u] * nv + u0);
+        if (on1) in[u][1] = __builtin_nontemporal_load(y + (size_t)row[u] * nv + u1);
       }
     }
 #pragma unroll
     for (int u = 0; u < G; ++u) {
-      if (row[u] < 0 || !on) continue;
-      u32x4 o;
+      if (row[u] < 0) continue;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {  // output word i: columns 4i..4i+3
-        const uint32_t p0 = in[u][i / 2][(2 * i) % 4], p1 = in[u][i / 2][(2 * i) % 4 + 1];
-        o[i] = pack_e4m3x4(clamp448(bf16_lo(p0)), clamp448(bf16_hi(p0)), clamp448(bf16_lo(p1)),
-                           clamp448(bf16_hi(p1)));
+      for (int h = 0; h < 2; ++h) {
+        if (!(h ? on1 : on0)) continue;
+        const u32x4 x = in[u][h];
+        u32x2c o;
+        o[0] = pack_e4m3x4(clamp448(bf16_lo(x[0])), clamp448(bf16_hi(x[0])), clamp448(bf16_lo(x[1])),
+                           clamp448(bf16_hi(x[1])));
+        o[1] = pack_e4m3x4(clamp448(bf16_lo(x[2])), clamp448(bf16_hi(x[2])), clamp448(bf16_lo(x[3])),
+                           clamp448(bf16_hi(x[3])));
+        __builtin_nontemporal_store(o, y8 + (size_t)row[u] * nv + (h ? u1 : u0));
       }
-      store_nt(y8 + (size_t)row[u] * nv8 + v, o);
     }
   }
 }
