@@ -9,11 +9,12 @@
 // multiply-add per top-k position in order j = 0..k-1, then bf16 round to
 // nearest even -- a fixed order, so the result does not depend on timing.
 //
-// Up to top-8 a row is cut into slices of 16 bytes per lane (1 KiB per wave)
-// and one workgroup takes one token, a wave per slice (14 waves at 7168
-// columns; rows wider than 16 KiB split over as few workgroups as possible):
-// the pieces of each row the token gathers are then fetched together by one
-// CU.  At 4096 x 7168 on 8 ranks the combine took 60.7 us this way, against
+// Up to top-8 a row is cut into slices of 16 bytes per lane (1 KiB per wave;
+// 8 bytes when a token's rows are all distinct, see kDistinctLaneBytes) and
+// one workgroup takes one token, a wave per slice (14 waves at 7168 columns;
+// rows wider than 16 KiB, 8 KiB at 8 bytes per lane, split over as few
+// workgroups as possible): the pieces of each row the token gathers are then
+// fetched together by one CU.  At 4096 x 7168 on 8 ranks the combine took 60.7 us this way, against
 // 63.8 us with 2 KiB per wave and four waves per workgroup (tokens cut across
 // workgroups) and 164 us with 1 KiB per wave in four-wave workgroups.  Each
 // distinct expert-output row is loaded once (positions that share a rank row
@@ -38,6 +39,8 @@
 // combine with ROUND takes every value of each loaded row through the same
 // E4M3 encode and decode before the multiply-adds -- bit for bit the
 // two-launch result, with the bf16 rows read once and no E4M3 rows written.
+#include <type_traits>
+
 #include "dev.h"
 #include "mep_internal.h"
 
@@ -47,6 +50,13 @@ namespace {
 
 constexpr int kUnitsPerLane = 2;   // beyond top-8: 2 KiB of each row per wave
 constexpr int kMaxWavesPerWg = 16;  // 1024 threads
+// Top-8 combine of distinct rows (expert-major rows, converted rank rows):
+// 8 bytes of each row per lane, so a wave keeps 8 x 512 bytes in flight.  At
+// 4096 x 7168, eight expert-major rows per token, the combine took 88.1 us
+// this way against 91.7 us with 16 bytes per lane (8 KiB per wave); the rank
+// rows of a deduplicated combine (5.3 distinct per token at top-8 on 8
+// ranks) keep 16 bytes per lane: 61.5 us against 72.5 us with 8.
+constexpr int kDistinctLaneBytes = 8;
 // The E4M3 rounding in flight converts every loaded value, so its waves stay
 // busy longer after their loads: 2 KiB per wave keeps more bytes in flight
 // (prefill step with it 114.5 us against 118.8 us with 1 KiB).
@@ -81,14 +91,18 @@ __device__ __forceinline__ void round_e4m3_unit(u32x4& x) {
 // SUM: the rows are converted rank rows that already carry the weights; each
 // token's distinct rank rows (the positions owning them) are added with unit
 // weight -- fmaf(1, y, acc) is acc + y with one rounding.
-template <int KMAX, bool DEDUPE, bool ROUND, bool SUM = false, int UPL = 1>
+template <int KMAX, bool DEDUPE, bool ROUND, bool SUM = false, int UPL = 1, int LB = 16>
 __global__ __launch_bounds__(kMaxWavesPerWg * 64) void combine_kernel(CombineArgs a) {
+  static_assert(LB == 16 || (LB == 8 && !ROUND && !DEDUPE), "8-byte lanes: distinct rows only");
+  using V = typename std::conditional<LB == 16, u32x4, u32x2>::type;
+  constexpr int NW = LB / 4;  // bf16 pairs per lane unit
   constexpr int kUnitsPerLane = UPL;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x / a.wg_per_tok;
-  const int sl = (blockIdx.x - t * a.wg_per_tok) * a.waves_per_wg + first_lane(threadIdx.x >> 6);
+  const int part = blockIdx.x - t * a.wg_per_tok;  // which of the token's workgroups
+  const int sl = part * a.waves_per_wg + first_lane(threadIdx.x >> 6);
   if (t >= a.T || sl >= a.slices) return;
-  const int nv = a.H / 8;
+  const int nv = a.H * 2 / LB;
   const uint32_t own = SUM ? a.ufirst[t] : 0xFFFFFFFFu;
   int row[KMAX];
   float w[KMAX];
@@ -108,21 +122,21 @@ __global__ __launch_bounds__(kMaxWavesPerWg * 64) void combine_kernel(CombineArg
         if (jj < j && row[jj] == row[j]) src[j] = jj;
     }
   }
-  const u32x4* y = reinterpret_cast<const u32x4*>(a.y);
-  u32x4* out = reinterpret_cast<u32x4*>(a.out) + (size_t)t * nv;
+  const V* y = reinterpret_cast<const V*>(a.y);
+  V* out = reinterpret_cast<V*>(a.out) + (size_t)t * nv;
   const int v0 = sl * (kWave * kUnitsPerLane) + lane;
-  u32x4 in[kUnitsPerLane][KMAX];
+  V in[kUnitsPerLane][KMAX];
 #pragma unroll
   for (int u = 0; u < kUnitsPerLane; ++u) {
     const int v = v0 + u * kWave;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
-      in[u][j] = u32x4{0, 0, 0, 0};
+      in[u][j] = V{};
       if (row[j] >= 0 && src[j] == j && v < nv)
         in[u][j] = __builtin_nontemporal_load(y + (size_t)row[j] * nv + v);
     }
   }
-  if (ROUND) {
+  if constexpr (ROUND) {
 #pragma unroll
     for (int u = 0; u < kUnitsPerLane; ++u)
 #pragma unroll
@@ -133,28 +147,28 @@ __global__ __launch_bounds__(kMaxWavesPerWg * 64) void combine_kernel(CombineArg
   for (int u = 0; u < kUnitsPerLane; ++u) {
     const int v = v0 + u * kWave;
     if (v >= nv) continue;
-    float acc[8];
+    float acc[2 * NW];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    for (int i = 0; i < 2 * NW; ++i) acc[i] = 0.0f;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       if (row[j] < 0) continue;  // uniform: position skipped (token not dispatched)
-      u32x4 x = in[u][j];
+      V x = in[u][j];
       if (DEDUPE) {
 #pragma unroll
         for (int jj = 0; jj < j; ++jj)
           if (src[j] == jj) x = in[u][jj];
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < NW; ++i) {
         const float lo = bf16_lo(x[i]), hi = bf16_hi(x[i]);
         acc[2 * i] = __builtin_fmaf(w[j], lo, acc[2 * i]);
         acc[2 * i + 1] = __builtin_fmaf(w[j], hi, acc[2 * i + 1]);
       }
     }
-    u32x4 o;
+    V o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = pack_bf16_rne(acc[2 * i], acc[2 * i + 1]);
+    for (int i = 0; i < NW; ++i) o[i] = pack_bf16_rne(acc[2 * i], acc[2 * i + 1]);
     store_nt(out + v, o);
   }
 }
@@ -462,25 +476,28 @@ hipError_t launch_combine(const CombineArgs& a0, hipStream_t s) {
     }
     return hipGetLastError();
   }
-  // 1 KiB per wave (2 KiB with the E4M3 rounding); a token's waves in as few
-  // workgroups as possible
+  // 1 KiB of each row per wave when rows are shared (dedupe), 512 bytes when
+  // a token's rows are all distinct, 2 KiB with the E4M3 rounding; a token's
+  // waves in as few workgroups as possible
+  const bool dedupe = !a.distinct_rows && !a.sum_rows;
+  const bool narrow = a.sum_rows || (!a.round_e4m3 && !dedupe);  // the 8-byte-lane kernels
+  const int lane_bytes = narrow ? kDistinctLaneBytes : 16;
   const int upl = a.round_e4m3 ? kRoundUnitsPerLane : 1;
   a.slice_units = kWave * upl;
-  a.slices = (a.H / 8 + a.slice_units - 1) / a.slice_units;
+  a.slices = (a.H * 2 / lane_bytes + a.slice_units - 1) / a.slice_units;
   a.wg_per_tok = (a.slices + kMaxWavesPerWg - 1) / kMaxWavesPerWg;
   a.waves_per_wg = (a.slices + a.wg_per_tok - 1) / a.wg_per_tok;
   const int64_t blocks = (int64_t)a.T * a.wg_per_tok;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks), block((unsigned)(kWave * a.waves_per_wg));
-  const bool dedupe = !a.distinct_rows;
   if (a.sum_rows)  // converted rank rows: the owning positions' rows are distinct
-    combine_kernel<8, false, false, true><<<grid, block, 0, s>>>(a);
+    combine_kernel<8, false, false, true, 1, kDistinctLaneBytes><<<grid, block, 0, s>>>(a);
   else if (a.round_e4m3) {
     if (dedupe) combine_kernel<8, true, true, false, kRoundUnitsPerLane><<<grid, block, 0, s>>>(a);
     else combine_kernel<8, false, true, false, kRoundUnitsPerLane><<<grid, block, 0, s>>>(a);
   } else {
     if (dedupe) combine_kernel<8, true, false><<<grid, block, 0, s>>>(a);
-    else combine_kernel<8, false, false><<<grid, block, 0, s>>>(a);
+    else combine_kernel<8, false, false, false, 1, kDistinctLaneBytes><<<grid, block, 0, s>>>(a);
   }
   return hipGetLastError();
 }

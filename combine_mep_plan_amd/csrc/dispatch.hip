@@ -10,12 +10,14 @@
 // columns, code = E4M3(x / scale), round to nearest even) is this library's
 // reading; the pages do not print the format.
 //
-// Layout of the work: a row is cut into 1 KiB-per-wave slices -- each lane owns
-// one 16-byte unit of the received row (bf16: 8 columns; FP8: 16 columns, 8
-// lanes per 128-column scale block; FP4: 32 columns, one MX block) -- and one
-// wave handles one (token, slice).  Many small waves keep enough writes in flight to approach the HBM
-// write rate; every receive-row store is a non-temporal 16-byte-per-lane
-// store (1 KiB per wave instruction).
+// Layout of the work: a row is cut into slices of 64 lane items -- each lane
+// owns one item of the received row (bf16: 8 columns, 16 bytes; FP8: 16
+// columns, 16 bytes, 8 lanes per 128-column scale block; MX FP4: 16 columns,
+// 8 bytes, 2 lanes per MX block; carried FP4: 32 columns, 16 bytes) -- and
+// one wave handles one (token, slice).  Many small waves keep enough writes in
+// flight to approach the HBM write rate; every receive-row store is a
+// non-temporal 16- or 8-byte-per-lane store (1 KiB or 512 bytes per wave
+// instruction).
 //
 // Where the destination slots come from:
 //   kRoute  : a prior plan's receive row of each (token, top-k position);
@@ -169,7 +171,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
   if (MODE == kInline && g == 0 && lane == 0) *a.status_next = 0u;
 
   // this wave's unit of the row: loads go out before the routing work
-  const int nu = payload_units(QUANT, a.H);
+  const int nu = lane_items(QUANT, a.H);
   const int v = sl * kWave + lane;
   const bool on = v < nu;
   Unit<QUANT> unit;
@@ -202,14 +204,14 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
 
   float scale = 0.0f;
   uint32_t e8 = 0;
-  const u32x4 q = unit.convert(scale, e8);
+  const typename Unit<QUANT>::Out q = unit.convert(scale, e8);
   // after a prior plan, loading the metadata and the rows only once the
   // token is known to be dispatched measured faster at large batches than
   // issuing them with the payload unit
   if (MODE == kRoute) meta = load_meta<QUANT>(a, t, sl, lane);
   auto emit = [&](int row) {
     if (on) {
-      store_nt(reinterpret_cast<u32x4*>(a.recv_x) + (size_t)row * nu + v, q);
+      store_nt(reinterpret_cast<typename Unit<QUANT>::Out*>(a.recv_x) + (size_t)row * nu + v, q);
       store_unit_scale<QUANT>(a.recv_scales, (size_t)row, a.H, v, scale, e8);
     }
     if (sl == 0) {
@@ -244,7 +246,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
 template <int QUANT, int MODE>
 hipError_t launch_mode(const DispatchArgs& a0, hipStream_t s) {
   DispatchArgs a = a0;
-  a.slices = (payload_units(QUANT, a.H) + kWave - 1) / kWave;
+  a.slices = (lane_items(QUANT, a.H) + kWave - 1) / kWave;
   a.slice_units = kWave;
   const int64_t waves = (int64_t)a.T * a.slices;
   const int blocks = (int)((waves + 3) / 4);

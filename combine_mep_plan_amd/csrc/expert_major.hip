@@ -41,53 +41,73 @@ constexpr int kCountWaves = 16;
 template <int KMAX>
 __global__ __launch_bounds__(kCountWaves * 64) void em_count_kernel(EmArgs a) {
   __shared__ int32_t wtot[kCountWaves][kMaxEpr];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = blockIdx.x;
+  // Loads go out before any store (a wait for a load issued after stores
+  // also waits for those stores): the rank's receive count and, on the guess
+  // that the rank received at most 16 chunks (one per wave), the ids of chunk
+  // w's rows -- all inside the receive buffer; rows at or past the count are
+  // ignored below.
+  int spec[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) spec[j] = -1;
+  const int spec_s = w * kChunk + lane;
+  if (spec_s < a.cap) load_ids<KMAX>(a.recv_idx, r * a.cap + spec_s, a.k, spec);
+  const int cnt = clamp_count(a, r);
   // clear the (t, j) -> expert-major row map
   const int64_t nmap = (int64_t)a.T * a.k;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nmap;
        i += (int64_t)gridDim.x * blockDim.x)
     a.em_row[i] = -1;
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int r = blockIdx.x;
-  const int cnt = clamp_count(a, r);
   const int nch = (cnt + kChunk - 1) / kChunk;
   const int per = (nch + kCountWaves - 1) / kCountWaves;
   const int c0 = min(w * per, nch), c1 = min(c0 + per, nch);
   const int E = a.R * a.epr;
+  // chunk c's local-expert masks (stored per row) and, in lane l, its rows
+  // naming local expert l
+  auto count_chunk = [&](int c, const int (&ids)[KMAX]) {
+    const int s = c * kChunk + lane;
+    uint64_t lm = 0;
+    if (s < cnt) {
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        const int e = ids[j];
+        if (j < a.k && e >= 0 && e < E && (int)a.rdiv((uint32_t)e) == r) lm |= 1ull << (e - r * a.epr);
+      }
+      a.lmask[(size_t)r * a.cap + s] = lm;
+    }
+    int mine = 0;
+    for (int l = 0; l < a.epr; ++l) {
+      const uint64_t b = ballot((lm >> l) & 1ull);
+      if (lane == l) mine = __popcll(b);
+    }
+    return mine;
+  };
   constexpr int B = KMAX <= 8 ? 4 : 1;  // chunks whose ids are loaded together
   int run = 0;  // lane l: rows of this wave's earlier chunks naming local expert l
   int pre0[B];  // the first batch's prefixes, stored once the base is known
 #pragma unroll
   for (int q = 0; q < B; ++q) pre0[q] = 0;
-  for (int cb = c0; cb < c1; cb += B) {  // uniform
-    int ids[B][KMAX];
+  if (per == 1) {  // chunk c0 == w, whose ids are already here
+    if (c0 < c1) run = count_chunk(c0, spec);
+  } else {
+    for (int cb = c0; cb < c1; cb += B) {  // uniform
+      int ids[B][KMAX];
 #pragma unroll
-    for (int q = 0; q < B; ++q) {
-      const int s = (cb + q) * kChunk + lane;
-      if (cb + q < c1 && s < cnt) load_ids<KMAX>(a.recv_idx, r * a.cap + s, a.k, ids[q]);
-    }
-#pragma unroll
-    for (int q = 0; q < B; ++q) {
-      const int c = cb + q;
-      if (c >= c1) break;  // uniform
-      const int s = c * kChunk + lane;
-      uint64_t lm = 0;
-      if (s < cnt) {
-#pragma unroll
-        for (int j = 0; j < KMAX; ++j) {
-          const int e = ids[q][j];
-          if (j < a.k && e >= 0 && e < E && (int)a.rdiv((uint32_t)e) == r) lm |= 1ull << (e - r * a.epr);
-        }
-        a.lmask[(size_t)r * a.cap + s] = lm;
+      for (int q = 0; q < B; ++q) {
+        const int s = (cb + q) * kChunk + lane;
+        if (cb + q < c1 && s < cnt) load_ids<KMAX>(a.recv_idx, r * a.cap + s, a.k, ids[q]);
       }
-      int mine = 0;
-      for (int l = 0; l < a.epr; ++l) {
-        const uint64_t b = ballot((lm >> l) & 1ull);
-        if (lane == l) mine = __popcll(b);
+#pragma unroll
+      for (int q = 0; q < B; ++q) {
+        const int c = cb + q;
+        if (c >= c1) break;  // uniform
+        const int mine = count_chunk(c, ids[q]);
+        if (cb == c0) pre0[q] = run;
+        else if (lane < a.epr) a.ccnt[((size_t)r * a.CR + c) * a.epr + lane] = run;
+        run += mine;
       }
-      if (cb == c0) pre0[q] = run;
-      else if (lane < a.epr) a.ccnt[((size_t)r * a.CR + c) * a.epr + lane] = run;
-      run += mine;
     }
   }
   if (lane < a.epr) wtot[w][lane] = run;

@@ -33,6 +33,13 @@ __host__ __device__ constexpr int payload_units(int quant, int H) {
                                                                        : H / 16;
 }
 
+// Items of a received row that the dispatch waves take one per lane: the
+// 16-byte units above, except MXFP4, whose lanes take 16 columns (8 code
+// bytes, half an MX block) so that a row's waves stay full.
+__host__ __device__ constexpr int lane_items(int quant, int H) {
+  return quant == MEP_QUANT_MXFP4 ? H / 16 : payload_units(quant, H);
+}
+
 // Modes whose rows arrive already quantised, with the caller's scale words.
 __host__ __device__ constexpr bool is_carry(int quant) {
   return quant == MEP_QUANT_FP8_CARRY || quant == MEP_QUANT_FP4_CARRY;

@@ -172,6 +172,7 @@ __global__ __launch_bounds__(kOffThreads) void sm_offsets_kernel(SmArgs a) {
 constexpr int kRouteThreads = 256;
 constexpr int64_t kRouteFusedMax = 32768;  // chunks x experts summed per route workgroup
 constexpr int kRouteFusedMaxExperts = 2048;
+constexpr int kHistBatch = 64;  // histogram loads per round: 4096 tokens in one round
 
 // LDS of a route workgroup: token masks [E] u64, row bases [E] i32 and, when
 // the offsets are computed here, padded totals [E] i32.
@@ -199,16 +200,16 @@ __global__ __launch_bounds__(kRouteThreads) void sm_route_kernel(SmArgs a) {
   const int32_t* hist = a.chunk_hist;
   if (FUSED) {
     // per expert: total over all chunks and prefix over the chunks before c
-    // (16 independent loads in flight per thread)
+    // (kHistBatch independent loads in flight per thread)
     for (int e = tid; e < E; e += kRouteThreads) {
       int tot = 0, pre = 0;
       int cc = 0;
-      for (; cc + 16 <= C; cc += 16) {
-        int v[16];
+      for (; cc + kHistBatch <= C; cc += kHistBatch) {
+        int v[kHistBatch];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) v[u] = hist[(size_t)(cc + u) * E + e];
+        for (int u = 0; u < kHistBatch; ++u) v[u] = hist[(size_t)(cc + u) * E + e];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
+        for (int u = 0; u < kHistBatch; ++u) {
           tot += v[u];
           pre += cc + u < c ? v[u] : 0;
         }
@@ -299,7 +300,7 @@ __global__ __launch_bounds__(256) void sm_scatter_kernel(SmArgs a) {
   const int t = g / a.slices, sl = g - t * a.slices;
   if (t >= a.T) return;
   // this wave's slice of the row: loads go out first
-  const int nu = payload_units(QUANT, a.H);
+  const int nu = lane_items(QUANT, a.H);
   const int v = sl * kWave + lane;
   const bool on = v < nu;
   Unit<QUANT> unit;
@@ -311,13 +312,13 @@ __global__ __launch_bounds__(256) void sm_scatter_kernel(SmArgs a) {
   for (int j = 0; j < KMAX; ++j) rows[j] = j < a.k ? rr[j] : -1;
   float scale = 0.0f;
   uint32_t e8 = 0;
-  const u32x4 q = unit.convert(scale, e8);
+  const typename Unit<QUANT>::Out q = unit.convert(scale, e8);
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
     const int pos = rows[j];
     if (pos < 0) continue;
     if (on) {
-      store_nt(reinterpret_cast<u32x4*>(a.em_x) + (size_t)pos * nu + v, q);
+      store_nt(reinterpret_cast<typename Unit<QUANT>::Out*>(a.em_x) + (size_t)pos * nu + v, q);
       store_unit_scale<QUANT>(a.em_scales, (size_t)pos, a.H, v, scale, e8);
     }
     if (is_carry(QUANT) && sl == 0)
@@ -328,7 +329,7 @@ __global__ __launch_bounds__(256) void sm_scatter_kernel(SmArgs a) {
 template <int QUANT>
 hipError_t launch_scatter(const SmArgs& a0, hipStream_t s) {
   SmArgs a = a0;
-  a.slices = (payload_units(QUANT, a.H) + kWave - 1) / kWave;
+  a.slices = (lane_items(QUANT, a.H) + kWave - 1) / kWave;
   const int blocks = (int)(((int64_t)a.T * a.slices + 3) / 4);
   if (a.k <= 8) sm_scatter_kernel<QUANT, 8><<<blocks, 256, 0, s>>>(a);
   else sm_scatter_kernel<QUANT, kMaxTopk><<<blocks, 256, 0, s>>>(a);

@@ -25,15 +25,17 @@ __global__ void probe_e4m3_kernel(const float* in, uint8_t* out, int64_t n) {
   }
 }
 
-// One MX FP4 block (32 bf16 columns) per thread, through the dispatch's own
-// block encoder: 16 code bytes and one scale byte per block.
-__global__ void probe_mxfp4_kernel(const u32x4* in, u32x4* q, uint8_t* e8, int64_t nblocks) {
-  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= nblocks) return;
-  const u32x4 x[4] = {in[4 * b], in[4 * b + 1], in[4 * b + 2], in[4 * b + 3]};
+// MX FP4 blocks (32 bf16 columns) through the dispatch's own block encoder:
+// 2 lanes per block, 16 columns each, as in a dispatch wave; 16 code bytes
+// and one scale byte per block.
+__global__ void probe_mxfp4_kernel(const u32x4* in, u32x2* q, uint8_t* e8, int64_t nblocks) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t b = g >> 1;
+  const int part = (int)(g & 1);
+  if (b >= nblocks) return;  // both lanes of a block leave together
   uint32_t e = 0;
-  q[b] = quant_mx4(x, e);
-  e8[b] = (uint8_t)e;
+  q[g] = quant_mx4_half(in[2 * g], in[2 * g + 1], e);
+  if (part == 0) e8[b] = (uint8_t)e;
 }
 
 // FP8 blocks (128 bf16 columns) through the dispatch's own block encoder:
@@ -138,8 +140,9 @@ hipError_t launch_probe_e4m3(const float* in, uint8_t* out, int64_t n, hipStream
 hipError_t launch_probe_mxfp4(const uint16_t* in, uint8_t* q, uint8_t* e8, int64_t nblocks,
                               hipStream_t s) {
   if (nblocks == 0) return hipSuccess;
-  probe_mxfp4_kernel<<<(unsigned)((nblocks + 255) / 256), 256, 0, s>>>(
-      reinterpret_cast<const u32x4*>(in), reinterpret_cast<u32x4*>(q), e8, nblocks);
+  const int64_t threads = nblocks * 2;
+  probe_mxfp4_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(
+      reinterpret_cast<const u32x4*>(in), reinterpret_cast<u32x2*>(q), e8, nblocks);
   return hipGetLastError();
 }
 
