@@ -16,13 +16,16 @@
 //            the launch writes every expert's row count and, per (chunk,
 //            expert), the rows of the rank's earlier chunks naming it -- an
 //            expert's rows all come from its own rank, so no other workgroup
-//            is involved.  It also clears the (token, top-k) -> expert-major
-//            row map;
-//   scatter: every workgroup first scans the experts' padded row counts in
-//            LDS into segment offsets (workgroup 0 also writes them out);
-//            then one wave per (receive row, slice of the row): the row's
-//            place inside an expert segment is the segment offset, plus the
-//            rows of the rank's earlier chunks naming that expert, plus a
+//            is involved -- and, with every segment padded to 128 rows, each
+//            expert's offset among its rank's segments and the rank's total.
+//            It also clears the (token, top-k) -> expert-major row map;
+//   scatter: one wave per (receive row, slice of the row).  Each wave scans
+//            the R receive counts and the R padded rank totals across its
+//            lanes, which gives its row's rank and the start of that rank's
+//            segments (no LDS, no barrier; workgroup 0 also writes the
+//            segment offsets out).  The row's place inside an expert segment
+//            is that start, plus the expert's offset inside the rank, plus
+//            the rows of the rank's earlier chunks naming that expert, plus a
 //            ballot count of the earlier rows of its own chunk.  Each slice
 //            is copied with 16-byte-per-lane loads and non-temporal stores.
 #include "dev.h"
@@ -112,8 +115,9 @@ __global__ __launch_bounds__(kCountWaves * 64) void em_count_kernel(EmArgs a) {
   }
   if (lane < a.epr) wtot[w][lane] = run;
   __syncthreads();
+  int tot = 0;
   if (lane < a.epr) {
-    int base = 0, tot = 0;
+    int base = 0;
 #pragma unroll
     for (int ww = 0; ww < kCountWaves; ++ww) {
       const int v = wtot[ww][lane];
@@ -127,55 +131,72 @@ __global__ __launch_bounds__(kCountWaves * 64) void em_count_kernel(EmArgs a) {
     if (base)  // chunks past the first batch (more than B per wave)
       for (int c = c0 + B; c < c1; ++c) a.ccnt[((size_t)r * a.CR + c) * a.epr + lane] += base;
   }
-}
-
-// 16-byte units per lane per scatter wave.  Each wave first finds its row's
-// rank, local experts and in-chunk position, so fewer, larger waves pay that
-// less often: at 4096 x 7168 FP8 on 32 ranks the conversion took 129, 95.5,
-// 91.6 and 94.8 us with 1, 2, 3 and 4 units per lane.
-constexpr int kEmUnitsPerLane = 3;
-
-template <int UPL>
-__global__ __launch_bounds__(256) void em_scatter_kernel(EmArgs a) {
-  extern __shared__ int32_t seg[];  // [E]: padded row counts, then segment offsets
-  __shared__ int32_t prefix[kMaxRanks + 1];
-  __shared__ int32_t wsum[4];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int E = a.R * a.epr;
-  // the experts' padded row counts (consecutive experts per thread), loaded
-  // together with the receive counts
-  const int per = (E + 255) / 256;
-  const int e0 = min(tid * per, E), e1 = min(e0 + per, E);
-  for (int e = e0; e < e1; ++e) seg[e] = (a.em_counts[e] + 127) / 128 * 128;
-  if (w == 0) {  // rank prefix of the receive counts, one lane per rank
-    const int n = lane < a.R ? clamp_count(a, lane) : 0;
-    int inc = n;
+  if (w == 0) {
+    // the rank's experts' segments, each padded to a multiple of 128 rows:
+    // their in-rank offsets and the rank's total
+    const int pad = (tot + 127) / 128 * 128;
+    int inc = pad;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
       const int v = __shfl_up(inc, d);
       if (lane >= d) inc += v;
     }
-    if (lane < a.R) prefix[lane + 1] = inc;
-    if (lane == 0) prefix[0] = 0;
+    if (lane < a.epr) a.seg_inrank[r * a.epr + lane] = inc - pad;
+    if (lane == kWave - 1) a.seg_rank[r] = inc;
   }
-  __syncthreads();
+}
 
-  // this wave's receive row and slice; every load that does not need the
-  // segment offsets goes out before they are scanned
+// 16-byte units per lane per scatter wave.  Each wave first finds its row's
+// rank, local experts and in-chunk position, so larger waves pay that less
+// often, while smaller ones keep more rows in flight: at 4096 x 7168 FP8 on
+// 32 ranks the conversion took 99.5, 84.5, 86.0 and 87.9 us with 1, 2, 3 and
+// 4 units per lane (with the segment offsets still scanned in LDS by every
+// workgroup: 129, 95.5, 91.6 and 94.8 us).
+constexpr int kEmUnitsPerLane = 2;
+
+template <int UPL>
+__global__ __launch_bounds__(256) void em_scatter_kernel(EmArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = first_lane(blockIdx.x * 4 + w);
   const int u = g / a.slices, sl = g - u * a.slices;
-  const bool live = u < prefix[a.R];
-  int r = 0;
-  if (live) {
-    int lo = 0, hi = a.R;  // largest r with prefix[r] <= u (uniform)
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (prefix[mid] <= u) lo = mid; else hi = mid;
-    }
-    r = lo;
+  // lane q < R: rank q's receive rows and its experts' padded segment rows,
+  // both scanned across the lanes
+  int n = 0, p = 0;
+  if (lane < a.R) {
+    n = clamp_count(a, lane);
+    p = a.seg_rank[lane];
   }
-  const int s = live ? u - prefix[r] : 0;
-  const int cnt = prefix[r + 1] - prefix[r];
+  int n_inc = n, p_inc = p;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int vn = __shfl_up(n_inc, d), vp = __shfl_up(p_inc, d);
+    if (lane >= d) {
+      n_inc += vn;
+      p_inc += vp;
+    }
+  }
+  if (blockIdx.x == 0) {
+    // segment offsets: expert e of rank q starts after the padded segments of
+    // the ranks before q and of q's earlier experts
+    const int E = a.R * a.epr;
+    const int p_exc = p_inc - p;
+    for (int e0 = w * kWave; e0 < E; e0 += 4 * kWave) {  // uniform
+      const int e = e0 + lane;
+      const int q = e < E ? (int)a.rdiv((uint32_t)e) : 0;
+      const int base = __shfl(p_exc, q);
+      if (e < E) a.em_offsets[e] = base + a.seg_inrank[e];
+    }
+    if (tid == 0) a.em_offsets[E] = lane_value(p_inc, a.R - 1);
+  }
+
+  // this wave's receive row u (in rank-major order over the received rows):
+  // its rank is the number of ranks whose rows all come before u
+  const bool live = u < lane_value(n_inc, a.R - 1);
+  if (!live) return;
+  const int r = __popcll(ballot(lane < a.R && n_inc <= u));
+  const int seg_base = r > 0 ? lane_value(p_inc, r - 1) : 0;
+  const int s = u - (r > 0 ? lane_value(n_inc, r - 1) : 0);
+  const int cnt = lane_value(n, r);
   const size_t row = (size_t)r * a.cap + s;
   const int nv = a.row_units;  // 16-byte units per row
   const u32x4* src = reinterpret_cast<const u32x4*>(a.recv_x) + row * nv;
@@ -183,44 +204,26 @@ __global__ __launch_bounds__(256) void em_scatter_kernel(EmArgs a) {
 #pragma unroll
   for (int q = 0; q < UPL; ++q) {
     const int v = (sl * UPL + q) * kWave + lane;
-    val[q] = live && v < nv ? src[v] : u32x4{0, 0, 0, 0};
+    val[q] = v < nv ? src[v] : u32x4{0, 0, 0, 0};
   }
   const int c = s / kChunk, sc = s % kChunk;
   const int peer = c * kChunk + lane;
-  const uint64_t lm_lane = live && peer < cnt ? a.lmask[(size_t)r * a.cap + peer] : 0ull;
-  // lane l: rows of the rank's earlier chunks naming local expert l
-  const int pre = live && lane < a.epr ? a.ccnt[((size_t)r * a.CR + c) * a.epr + lane] : 0;
+  const uint64_t lm_lane = peer < cnt ? a.lmask[(size_t)r * a.cap + peer] : 0ull;
+  // lane l: rows of the rank's earlier chunks naming local expert l, and the
+  // start of local expert l's segment inside the rank's segments
+  int pre = 0, inr = 0;
+  if (lane < a.epr) {
+    pre = a.ccnt[((size_t)r * a.CR + c) * a.epr + lane];
+    inr = a.seg_inrank[r * a.epr + lane];
+  }
   int pos_code = 0, t = -1, myid = -1;
   float scw = 0.0f;  // the row's first 64 scale words, one per lane
-  if (live && sl == 0) {
+  if (sl == 0) {
     pos_code = a.spos[row];
     t = pos_code - a.spos_base;
     if (lane < a.k) myid = a.recv_idx[row * a.k + lane];
     if (lane < a.nb) scw = a.recv_scales[row * a.nb + lane];
   }
-
-  // segment offsets: scan of the padded counts within the wave, then across
-  int sum = 0;
-  for (int e = e0; e < e1; ++e) sum += seg[e];
-  int inc = sum;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int v = __shfl_up(inc, d);
-    if (lane >= d) inc += v;
-  }
-  if (lane == kWave - 1) wsum[w] = inc;
-  __syncthreads();
-  int off = inc - sum;
-  for (int ww = 0; ww < w; ++ww) off += wsum[ww];
-  for (int e = e0; e < e1; ++e) {
-    const int n = seg[e];
-    seg[e] = off;
-    if (blockIdx.x == 0) a.em_offsets[e] = off;
-    off += n;
-  }
-  if (blockIdx.x == 0 && tid == 255) a.em_offsets[E] = off;
-  __syncthreads();
-  if (!live) return;
 
   const uint64_t lm_self =
       ((uint64_t)(uint32_t)lane_value((int)(uint32_t)lm_lane, sc)) |
@@ -229,7 +232,8 @@ __global__ __launch_bounds__(256) void em_scatter_kernel(EmArgs a) {
   for (uint64_t m = lm_self; m; m &= m - 1) {
     const int l = __builtin_ctzll(m);
     const uint64_t b = ballot(lane < sc && ((lm_lane >> l) & 1ull));
-    const int64_t pos = (int64_t)seg[r * a.epr + l] + lane_value(pre, l) + __popcll(b);
+    const int64_t pos =
+        (int64_t)seg_base + lane_value(inr, l) + lane_value(pre, l) + __popcll(b);
     if (pos >= a.cap_em) {
       if (lane == 0) atomicOr(a.status, (uint32_t)MEP_DEV_EM_OVERFLOW);
       continue;
@@ -270,8 +274,7 @@ hipError_t launch_to_expert_major(const EmArgs& a0, hipStream_t s) {
   a.slices = (nv + per - 1) / per;
   const int64_t rows = (int64_t)a.T * std::min(a.k, a.R);
   const int64_t waves = std::max<int64_t>(rows * a.slices, 1);
-  const size_t lds = (size_t)a.R * a.epr * sizeof(int32_t);
-  em_scatter_kernel<kEmUnitsPerLane><<<(unsigned)((waves + 3) / 4), 256, lds, s>>>(a);
+  em_scatter_kernel<kEmUnitsPerLane><<<(unsigned)((waves + 3) / 4), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

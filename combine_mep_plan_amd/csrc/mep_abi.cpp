@@ -45,6 +45,7 @@ WsLayout ws_layout(const mep_config& c) {
   L.em_row = take(cap * k * sizeof(int32_t));
   L.em_lmask = take(R * cap * sizeof(uint64_t));
   L.em_ccnt = take(R * C * epr * sizeof(int32_t));
+  L.em_seg = take((R + R * epr) * sizeof(int32_t));
   L.sm_hist = take(C * R * epr * sizeof(int32_t));
   L.total = off;
   return L;
@@ -436,6 +437,8 @@ int mep_to_expert_major(mep_handle* h, const void* recv_x, const float* recv_sca
   a.em_row = ws_ptr<int32_t>(h, h->lay.em_row);
   a.lmask = ws_ptr<uint64_t>(h, h->lay.em_lmask);
   a.ccnt = ws_ptr<int32_t>(h, h->lay.em_ccnt);
+  a.seg_rank = ws_ptr<int32_t>(h, h->lay.em_seg);
+  a.seg_inrank = a.seg_rank + c.world_size;
   a.status = status_word(h);
   a.cap_em = cap_em;
   a.T = h->plan_T;

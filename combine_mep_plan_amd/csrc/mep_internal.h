@@ -66,6 +66,8 @@ struct WsLayout {
   size_t em_row;     // int32 [cap][k]: expert-major row of (t, j), -1 if none
   size_t em_lmask;   // uint64 [R*cap]: local experts named by each receive row
   size_t em_ccnt;    // int32 [R][CR][epr]: per 64-row chunk, rows per local expert
+  size_t em_seg;     // int32 [R + R*epr]: padded segment rows of each rank's experts, then
+                     // each expert's padded in-rank offset
   size_t sm_hist;    // int32 [C][E]: standard-MoE dispatch, per-chunk expert counts / prefixes
   size_t total;
 };
@@ -149,6 +151,7 @@ struct ConvertArgs {         // expert-major expert outputs back to rank-major r
   const uint32_t* ufirst;    // [T] positions owning a rank row
   void* y;                   // [R*cap,H] bf16
   int32_t T, H, k, slices;
+  int32_t wg_per_tok, waves_per_wg;  // top-8: workgroups per token, waves per workgroup
 };
 
 struct EmArgs {
@@ -166,6 +169,8 @@ struct EmArgs {
   int32_t* em_row;              // [T,k]
   uint64_t* lmask;              // [R*cap]
   int32_t* ccnt;                // [R][CR][epr]
+  int32_t* seg_rank;            // [R]: padded segment rows of rank r's experts
+  int32_t* seg_inrank;          // [E]: padded rows of the same rank's earlier experts
   uint32_t* status;
   RankDiv rdiv;                 // expert id -> rank
   int64_t cap_em;
