@@ -578,6 +578,43 @@ def sets_sweep(M, torch, wl, counts, steps):
     return out
 
 
+PROBE_WAVES = (28672, 57344, 86016, 114688, 172032)
+
+
+def _probe_buffers(torch, units):
+    """One source and one destination buffer for the streaming probe; each launch
+    takes the next region of them, the regions of a cycle spanning at least
+    1 GiB each way (so no launch finds its data in the 256 MB Infinity Cache)."""
+    span = max(1 << 30, 3 * 1024 * max(max(r, w) for r, w in units.values()))
+    return (span, torch.empty(span, dtype=torch.uint8, device="cuda"),
+            torch.empty(span, dtype=torch.uint8, device="cuda"))
+
+
+def _probe_ms(M, torch, bufs, ru, wu, nw, reps):
+    span, src_all, dst_all = bufs
+    stream = torch.cuda.current_stream()
+    nreg = span // (1024 * max(ru, wu))
+
+    def fn(i):
+        j = i % nreg
+        src = src_all[j * ru * 1024:(j + 1) * ru * 1024] if ru else src_all[:16]
+        dst = dst_all[j * wu * 1024:(j + 1) * wu * 1024] if wu else dst_all[:16]
+        M.mep_probe_stream(src, dst, nw, ru, wu, stream)
+    for i in range(nreg):
+        fn(i)
+    return _loop_ms(torch, stream, fn, max(reps, nreg))
+
+
+def _probe_entry(ru, wu, by_waves):
+    best = min(by_waves, key=by_waves.get)
+    ms = by_waves[best]
+    out = {"GBps": round((ru + wu) * 1024 / (ms * 1e-3) / 1e9, 1), "us": round(ms * 1e3, 2),
+           "read_bytes": ru * 1024, "write_bytes": wu * 1024, "waves": best}
+    if len(by_waves) > 1:
+        out["us_by_waves"] = {str(w): round(v * 1e3, 2) for w, v in by_waves.items()}
+    return out
+
+
 def stream_ceilings(M, torch, wl, U, reps=20):
     """What HBM gives plain streams with the prefill kernels' own byte mixes:
     the library's streaming probe with the same bytes read and written,
@@ -585,9 +622,7 @@ def stream_ceilings(M, torch, wl, U, reps=20):
     stores.  The mixes are timed at several wave counts (4096 tokens x 7
     slices = 28672 is the kernels' old shape; plain streams do better with
     more, smaller waves) and the fastest is the ceiling.  Also the combine's
-    reads alone and writes alone.  Successive launches use successive regions
-    of buffers of at least 1 GiB, so no launch finds its data in the 256 MB
-    Infinity Cache."""
+    reads alone and writes alone."""
     T, H, k = wl.tokens, wl.hidden, wl.topk
     waves = T * ((H // 8 + 127) // 128)
     mixes = {
@@ -607,34 +642,48 @@ def stream_ceilings(M, torch, wl, U, reps=20):
                           if -(-max(units[n]) // w) <= 16]
     wave_counts["combine_reads_2k_waves"] = [-(-units["combine_reads_2k_waves"][0] // 2)]
     wave_counts["dispatch_writes_1k_waves"] = [units["dispatch_writes_1k_waves"][1]]
-    # one source and one destination buffer, each launch on the next region of
-    # them, the regions of a cycle spanning at least 1 GiB each way (so no
-    # launch finds its data in the 256 MB Infinity Cache)
-    span = max(1 << 30, 3 * 1024 * max(max(r, w) for r, w in units.values()))
-    src_all = torch.empty(span, dtype=torch.uint8, device="cuda")
-    dst_all = torch.empty(span, dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
+    bufs = _probe_buffers(torch, units)
     out = {}
     for name, (ru, wu) in units.items():
-        nreg = span // (1024 * max(ru, wu))
-        by_waves = {}
-        for nw in wave_counts[name]:
-            def fn(i, ru=ru, wu=wu, nreg=nreg, nw=nw):
-                j = i % nreg
-                src = src_all[j * ru * 1024:(j + 1) * ru * 1024] if ru else src_all[:16]
-                dst = dst_all[j * wu * 1024:(j + 1) * wu * 1024] if wu else dst_all[:16]
-                M.mep_probe_stream(src, dst, nw, ru, wu, stream)
-            for i in range(nreg):
-                fn(i)
-            by_waves[nw] = _loop_ms(torch, stream, fn, max(reps, nreg))
-        best = min(by_waves, key=by_waves.get)
-        ms = by_waves[best]
-        out[name] = {"GBps": round((ru + wu) * 1024 / (ms * 1e-3) / 1e9, 1),
-                     "us": round(ms * 1e3, 2), "read_bytes": ru * 1024, "write_bytes": wu * 1024,
-                     "waves": best}
-        if len(by_waves) > 1:
-            out[name]["us_by_waves"] = {str(w): round(v * 1e3, 2) for w, v in by_waves.items()}
-    del src_all, dst_all
+        out[name] = _probe_entry(ru, wu, {nw: _probe_ms(M, torch, bufs, ru, wu, nw, reps)
+                                          for nw in wave_counts[name]})
+    del bufs
+    return out
+
+
+def op_mixes(wl, U, Uem, quant, em, fp8c):
+    """Bytes read and written by each main operation of a workload (the same
+    algorithmic bytes as Runner.bytes, split by direction)."""
+    T, H, k, E = wl.tokens, wl.hidden, wl.topk, wl.experts
+    rb = row_bytes(H, quant)
+    mixes = {"dispatch": (T * H * 2 + T * k * 8, U * (rb + k * 8))}
+    if em:
+        mixes["combine"] = (T * k * H * 2 + T * k * 8, T * H * 2)
+        mixes["to_expert_major"] = (U * (rb + k * 4), T * k * (rb + 4))
+        mixes["dispatch_standard_moe"] = (T * H * 2 + T * k * 4, Uem * (rb + 4) + E * 8)
+        mixes["convert_combine_input"] = (Uem * (H * 2 + 4) + T * k * 8, U * H * 2)
+        mixes["combine_rank_sum"] = (U * H * 2 + T * k * 4, T * H * 2)
+    elif fp8c:
+        mixes["cast_fp8_direct"] = (U * H * 2, U * H)
+        mixes["combine"] = (U * H + T * k * 8, T * H * 2)
+        mixes["combine_in_flight"] = (U * H * 2 + T * k * 8, T * H * 2)
+    else:
+        mixes["combine"] = (U * H * 2 + T * k * 8, T * H * 2)
+    return mixes
+
+
+def workload_ceilings(M, torch, mixes, reps=20):
+    """The streaming probe at each operation's own mix of reads and writes,
+    timed at several wave counts (at most 16 KiB read per wave); the fastest
+    is that operation's ceiling."""
+    units = {n: (-(-r // 1024), -(-w // 1024)) for n, (r, w) in mixes.items()}
+    bufs = _probe_buffers(torch, units)
+    out = {}
+    for name, (ru, wu) in units.items():
+        counts = [w for w in PROBE_WAVES if -(-ru // w) <= 16]
+        out[name] = _probe_entry(ru, wu, {nw: _probe_ms(M, torch, bufs, ru, wu, nw, reps)
+                                          for nw in counts})
+    del bufs
     return out
 
 
@@ -751,8 +800,16 @@ def main():
             xwl = WORKLOADS[name]
             say(f"{name}: T={xwl.tokens} R={xwl.ranks} epr={xwl.experts_per_rank}")
             r = Runner(M, torch, xwl, (0,), nsets)
-            extra[name] = {"U": r.U, "seed": 0, "ops": r.measure(max(args.steps // 2, 10), 3)}
+            xops = r.measure(max(args.steps // 2, 10), 3)
+            xU = r.U
+            mixes = op_mixes(xwl, r.U, r.Uem, r.quant, r.em, r.fp8c)
             del r
+            torch.cuda.empty_cache()
+            # each operation against the probe at its own read/write mix
+            xceil = workload_ceilings(M, torch, mixes)
+            for op, c in xceil.items():
+                xops[op]["frac_of_mix_ceiling"] = round(xops[op]["GBps"] / c["GBps"], 4)
+            extra[name] = {"U": xU, "seed": 0, "ops": xops, "mix_ceilings": xceil}
             torch.cuda.empty_cache()
 
     ssweep = {}

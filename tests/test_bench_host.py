@@ -50,3 +50,32 @@ def test_byte_counts_match_the_buffers_they_move():
     assert bench.convert_combine_input_bytes(T, H, k, U, Uem) == \
         Uem * (H * 2 + f32) + T * k * 2 * i32 + U * H * 2
     assert bench.combine_rank_sum_bytes(T, H, k, U) == U * H * 2 + T * k * i32 + T * H * 2
+
+
+def test_probe_mixes_split_each_operation_bytes_into_reads_and_writes():
+    # the streaming-probe ceiling of an operation is taken at that operation's
+    # own bytes: its read and write parts add up to the bytes it is priced with
+    from synthetic import WORKLOADS
+    U, Uem = 21706, 32768
+    for name in ("skew", "stdmoe", "prefill_mxfp4", "prefill_fp8direct"):
+        wl = WORKLOADS[name]
+        T, H, k = wl.tokens, wl.hidden, wl.topk
+        em, fp8c = wl.layout == "expert_major", wl.combine == "fp8_direct"
+        want = {"dispatch": bench.dispatch_bytes(T, H, k, U, wl.quant)}
+        if em:
+            want.update(combine=bench.combine_em_bytes(T, H, k),
+                        to_expert_major=bench.to_expert_major_bytes(T, H, k, U, wl.quant),
+                        dispatch_standard_moe=bench.standard_moe_bytes(T, H, k, wl.experts, Uem,
+                                                                       wl.quant),
+                        convert_combine_input=bench.convert_combine_input_bytes(T, H, k, U, Uem),
+                        combine_rank_sum=bench.combine_rank_sum_bytes(T, H, k, U))
+        elif fp8c:
+            want.update(cast_fp8_direct=bench.cast_fp8_bytes(H, U),
+                        combine=bench.combine_fp8_bytes(T, H, k, U),
+                        combine_in_flight=bench.combine_bytes(T, H, k, U))
+        else:
+            want.update(combine=bench.combine_bytes(T, H, k, U))
+        mixes = bench.op_mixes(wl, U, Uem, wl.quant, em, fp8c)
+        assert set(mixes) == set(want), name
+        for op, (rd, wr) in mixes.items():
+            assert rd > 0 and wr > 0 and rd + wr == want[op], (name, op)
