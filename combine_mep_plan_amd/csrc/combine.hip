@@ -14,10 +14,10 @@
 // one workgroup takes one token, a wave per slice (14 waves at 7168 columns;
 // rows wider than 16 KiB, 8 KiB at 8 bytes per lane, split over as few
 // workgroups as possible): the pieces of each row the token gathers are then
-// fetched together by one CU.  At 4096 x 7168 on 8 ranks the combine took 60.7 us this way, against
-// 63.8 us with 2 KiB per wave and four waves per workgroup (tokens cut across
-// workgroups) and 164 us with 1 KiB per wave in four-wave workgroups.  Each
-// distinct expert-output row is loaded once (positions that share a rank row
+// fetched together by one CU.  At 4096 x 7168 on 8 ranks the combine took
+// 60.7 us this way, against 63.8 us with 2 KiB per wave and four waves per
+// workgroup (tokens cut across workgroups) and 164 us with 1 KiB per wave in
+// four-wave workgroups.  Each distinct expert-output row is loaded once (positions that share a rank row
 // reuse its registers) with non-temporal loads -- the rows are read exactly
 // once -- and all of a slice's loads are issued before the FMAs.  Wider
 // top-k takes the positions in groups of 8, 2 KiB per wave (see below), and

@@ -131,7 +131,7 @@ struct CombineArgs {
   int32_t distinct_rows;   // 1: the k rows of a token are distinct (no dedupe needed)
   int32_t sum_rows;        // 1: add the token's distinct rank rows, no weights
   int32_t round_e4m3;      // 1: each value rounded through E4M3 (direct cast) before use
-  int32_t slices, slice_units;  // waves per token and 16-byte lane units per wave
+  int32_t slices, slice_units;  // waves per token and lane units (16 or 8 bytes) per wave
   int32_t wg_per_tok, waves_per_wg;  // top-8 kernel: workgroups per token, waves in each
 };
 
