@@ -403,13 +403,13 @@ __global__ __launch_bounds__(256) void combine_fp8_wide_kernel(CombineArgs a) {
   store_nt(out + 1, o1);
 }
 
-// One wave per (token, 1 KiB of E4M3 output per row); the token's distinct
-// rows in groups of 8, all loads of a group issued before its converts.  The
-// cast has no blocks, so any column may go to any lane: lane l takes 8-column
-// units l and l + 64 of the wave's 128, which makes every load (1 KiB) and
-// every store (512 bytes) contiguous across the wave.  With each lane's 16
-// columns adjacent instead (32-byte strided loads and stores) the cast took
-// 89.7 us at 4096 x 7168 on 8 ranks against 84.8 us.
+// One wave per (token, 512 bytes of E4M3 output per row); the token's
+// distinct rows in groups of 8, all loads of a group issued before its
+// converts.  Lane l takes 8-column unit l of the wave's 64, so every load
+// (1 KiB) and every store (512 bytes) is contiguous across the wave.  At 4096
+// x 7168 on 8 ranks: 84.4 us, against 84.9 us with two units per lane (l and
+// l + 64), 89.7 us with each lane's 16 columns adjacent (32-byte strided
+// loads and stores) and 88.5 us with a token's waves in one workgroup.
 template <bool RANK_MAJOR>
 __global__ __launch_bounds__(256) void cast_fp8_kernel(CastArgs a) {
   constexpr int G = 8;
@@ -419,38 +419,32 @@ __global__ __launch_bounds__(256) void cast_fp8_kernel(CastArgs a) {
   const int t = g / a.slices, sl = g - t * a.slices;
   if (t >= a.T) return;
   const int nv = a.H / 8;  // 16-byte bf16 units per row (8 columns each)
-  const int u0 = sl * 128 + lane, u1 = u0 + 64;  // this lane's two units
-  const bool on0 = u0 < nv, on1 = u1 < nv;
+  const int u = sl * kWave + lane;  // this lane's unit
+  const bool on = u < nv;
   const uint32_t own = RANK_MAJOR ? a.ufirst[t] : 0xFFFFFFFFu;  // uniform
   const u32x4* y = reinterpret_cast<const u32x4*>(a.y);
   u32x2c* y8 = reinterpret_cast<u32x2c*>(a.y8);  // 8-byte units: 8 E4M3 columns
+  if (!on) return;
   for (int j0 = 0; j0 < a.k; j0 += G) {
     int row[G];
-    u32x4 in[G][2];
+    u32x4 in[G];
 #pragma unroll
-    for (int u = 0; u < G; ++u) {
-      const int j = j0 + u;
-      row[u] = (j < a.k && (own >> j & 1u)) ? a.rows[(size_t)t * a.k + j] : -1;
-      in[u][0] = in[u][1] = u32x4{0, 0, 0, 0};
-      if (row[u] >= 0) {
-        if (on0) in[u][0] = __builtin_nontemporal_load(y + (size_t)row[u] * nv + u0);
-        if (on1) in[u][1] = __builtin_nontemporal_load(y + (size_t)row[u] * nv + u1);
-      }
+    for (int q = 0; q < G; ++q) {
+      const int j = j0 + q;
+      row[q] = (j < a.k && (own >> j & 1u)) ? a.rows[(size_t)t * a.k + j] : -1;
+      in[q] = u32x4{0, 0, 0, 0};
+      if (row[q] >= 0) in[q] = __builtin_nontemporal_load(y + (size_t)row[q] * nv + u);
     }
 #pragma unroll
-    for (int u = 0; u < G; ++u) {
-      if (row[u] < 0) continue;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (!(h ? on1 : on0)) continue;
-        const u32x4 x = in[u][h];
-        u32x2c o;
-        o[0] = pack_e4m3x4(clamp448(bf16_lo(x[0])), clamp448(bf16_hi(x[0])), clamp448(bf16_lo(x[1])),
-                           clamp448(bf16_hi(x[1])));
-        o[1] = pack_e4m3x4(clamp448(bf16_lo(x[2])), clamp448(bf16_hi(x[2])), clamp448(bf16_lo(x[3])),
-                           clamp448(bf16_hi(x[3])));
-        __builtin_nontemporal_store(o, y8 + (size_t)row[u] * nv + (h ? u1 : u0));
-      }
+    for (int q = 0; q < G; ++q) {
+      if (row[q] < 0) continue;
+      const u32x4 x = in[q];
+      u32x2c o;
+      o[0] = pack_e4m3x4(clamp448(bf16_lo(x[0])), clamp448(bf16_hi(x[0])), clamp448(bf16_lo(x[1])),
+                         clamp448(bf16_hi(x[1])));
+      o[1] = pack_e4m3x4(clamp448(bf16_lo(x[2])), clamp448(bf16_hi(x[2])), clamp448(bf16_lo(x[3])),
+                         clamp448(bf16_hi(x[3])));
+      __builtin_nontemporal_store(o, y8 + (size_t)row[q] * nv + u);
     }
   }
 }
@@ -519,7 +513,7 @@ hipError_t launch_combine_fp8(const CombineArgs& a0, hipStream_t s) {
 hipError_t launch_cast_fp8(const CastArgs& a0, hipStream_t s) {
   if (a0.T == 0) return hipSuccess;
   CastArgs a = a0;
-  a.slices = (a.H / 16 + kWave - 1) / kWave;
+  a.slices = (a.H / 8 + kWave - 1) / kWave;
   const int blocks = (int)(((int64_t)a.T * a.slices + 3) / 4);
   if (a.ufirst) cast_fp8_kernel<true><<<blocks, 256, 0, s>>>(a);
   else cast_fp8_kernel<false><<<blocks, 256, 0, s>>>(a);
