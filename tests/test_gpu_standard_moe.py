@@ -331,3 +331,38 @@ def test_carry_rank_major_dispatch(T, sd, fused):
     for e in range(wl.experts):
         used[offs[e]:offs[e] + cnt[e]] = True
     assert np.array_equal(host(ems)[used].view(np.uint32), em["em_scales"][used].view(np.uint32))
+
+
+def test_hip_graph_standard_moe_replay():
+    # the standard-MoE dispatch and the expert-major combine captured once in a
+    # HIP graph, replayed with new routing and token rows written in place
+    # (eager refills and synchronisation in between): every replay must match
+    # the oracle -- layout, rows, scales, sources, route, status and combine
+    wl = _wl("stdmoe", 700, hidden=1024)
+    T, H = wl.tokens, wl.hidden
+    g = StdRun(wl, _inputs(wl, 600, "fp8", 0), "fp8")  # eager warm-up, allocates everything
+    y = torch.zeros((g.cap_em, H), dtype=torch.int16, device="cuda")
+    out = torch.zeros((T, H), dtype=torch.int16, device="cuda")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g.call()
+        M.mep_combine(g.m.h, M.MEP_EXPERT_MAJOR, y, g.w, out)
+    for rep in range(4):
+        new = _inputs(wl, 700 + rep, "fp8", 0)
+        g.x.copy_(dev(new["x"]))
+        g.idx.copy_(dev(new["indices"]))
+        g.w.copy_(dev(new["weights"]))
+        g.em_x.fill_(SENT8)
+        g.em_s.fill_(float("nan"))
+        g.em_src.fill_(SENT32)
+        em = _oracle(wl, new, "fp8", g.cap_em)
+        y_np = O.expert_dequant(em["em_x"], em["em_scales"], 1.0)
+        y.copy_(dev(y_np))  # the expert stand-in for this replay, written before it
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _say(f"[std] graph replay {rep}")
+        _check(g, em)
+        check_combine(host(out, np.uint16), O.combine_em(y_np, new["weights"], em["tok_em_row"]))
+    assert M.mep_get_status(g.m.h) == 0
